@@ -1,0 +1,137 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled GEMM library.
+ *
+ * The operation (Colfax Research, "Optimizing an NVFP4 Blockscaled GEMM on RTX
+ * PRO 6000 Blackwell GPU (SM120)", introduction and "Version 2"; TileLang PR
+ * #3290, "Summary"):
+ *
+ *   W4A4:  D[m][n] = alpha * sum_k (A[m][k] * SFA[m][k/16]) * (B[n][k] * SFB[n][k/16])
+ *   W4A16: y[m][n] = alpha * sum_k  x[m][k] * (W[n][k] * SFW[n][k/16])
+ *
+ * A, B, W hold 4-bit E2M1 codes packed two per byte along K (element 2j in the
+ * low nibble of byte j); SFA, SFB, SFW hold one E4M3 (or UE4M3) scale byte per
+ * 16 consecutive K-elements of a row; x and y are BF16; alpha is FP32 and is
+ * applied to the FP32 accumulator before the output conversion (Colfax
+ * article, "Version 3").
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_dev or described as device memory are device pointers
+ *    owned by the caller. The library never allocates, frees or retains a
+ *    pointer beyond the call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued asynchronously; the call returns after the enqueue.
+ *  - Argument checks run on the host before anything is enqueued; a non-OK
+ *    status means nothing was launched.
+ *  - Results are deterministic: the same inputs give bit-identical outputs on
+ *    every call, in or out of hipGraph capture.
+ *  - Sizes are int64_t; all device offsets are 64-bit.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,       /* a size is negative/zero where not allowed, or K % 64, N % 32, ld checks fail */
+  NVFP4_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks the stated alignment */
+  NVFP4_ERR_DTYPE = 4,       /* an enum argument (scale kind, output dtype, op) is out of range */
+  NVFP4_ERR_VALUE = 5,       /* a host scalar is not finite */
+  NVFP4_ERR_WORKSPACE = 6,   /* workspace missing or smaller than nvfp4_workspace_bytes() */
+  NVFP4_ERR_UNSUPPORTED = 7, /* the current device is not gfx950 */
+  NVFP4_ERR_HIP = 8          /* a HIP runtime call or launch failed */
+} nvfp4_status;
+
+typedef enum { NVFP4_SCALE_UE4M3 = 0, NVFP4_SCALE_E4M3 = 1 } nvfp4_scale_kind;
+typedef enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 } nvfp4_out_dtype;
+typedef enum { NVFP4_OP_W4A4 = 0, NVFP4_OP_W4A16 = 1, NVFP4_OP_QUANTIZE = 2 } nvfp4_op;
+
+/* Checks that the current HIP device is gfx950 and records its CU count.
+ * Call once per device before the first GEMM (and before any graph capture). */
+nvfp4_status nvfp4_init(void);
+
+/* Human-readable name of a status code (static string). */
+const char *nvfp4_status_string(int status);
+
+/* Size in bytes of a prepared weight: N*K/2 + N*K/16, the same as the packed
+ * codes plus the scales (TileLang PR #3290, "Design: Weight layout").
+ * Returns 0 for N % 32 != 0, K % 64 != 0 or non-positive sizes. */
+size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes an op needs for (M, N, K); 0 means no workspace is used.
+ * The workspace holds split-K partial sums and arrival tickets (W4A16) or
+ * per-workgroup maxima (quantize). */
+size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/* Zeroes a workspace on `stream` with a fill kernel (no hipMemset, so it may be
+ * captured). Required once after allocation; the library leaves the ticket
+ * area zeroed again after every call. */
+nvfp4_status nvfp4_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Prepare a weight once (TileLang PR #3290, "Design: Weight layout").
+ *  w_codes  [N][K/2] bytes, device, packed E2M1, 16-byte aligned.
+ *  w_scales [N][K/16] bytes, device, E4M3 (kind = NVFP4_SCALE_E4M3) or UE4M3.
+ *  N % 32 == 0, K % 64 == 0.
+ *  w_prep   nvfp4_prepared_weight_bytes(N, K) bytes, device, 16-byte aligned.
+ * The prepared layout: 32 (n) x 64 (k) tiles in n-major, k-minor order; the
+ * first N*K/2 bytes hold 1024-byte code tiles (row r of the tile at bytes
+ * 32r..32r+31, standard packing), the rest 128-byte scale tiles (row r, block b
+ * at byte 4r+b). Blocks with a zero scale get zero codes and scale 0; blocks
+ * with a negative scale get their code signs flipped and the scale magnitude;
+ * NaN scale bytes (and, for UE4M3, bytes with bit 7 set) keep their codes, get
+ * scale byte 0x7F (NaN) and are counted.
+ *  bad_count_dev  device int32 or NULL; when given it is overwritten with the
+ *  number of invalid scale bytes (read it after the stream completes). */
+nvfp4_status nvfp4_prepare_weight(const uint8_t *w_codes, const uint8_t *w_scales, int scale_kind,
+                                  int64_t N, int64_t K, uint8_t *w_prep, int32_t *bad_count_dev,
+                                  void *stream);
+
+/* W4A4 GEMM: D = alpha_eff * (A.SFA)(W.SFW)^T with FP32 accumulation, where
+ * alpha_eff = alpha * (*alpha_dev) in FP32 (alpha alone when alpha_dev is NULL).
+ *  a_codes  [M][K/2] bytes, device, 16-byte aligned (rows are K/2 bytes apart).
+ *  a_scales [M][K/16] bytes, device, E4M3 or UE4M3 bytes read as E4M3, 4-byte
+ *           aligned. A NaN scale (0x7F/0xFF) propagates NaN into its output row.
+ *  w_prep   prepared weight of shape (N, K).
+ *  d        [M][ldd] elements of out_dtype (FP32 or BF16 with round-to-nearest-
+ *           even), device, element-aligned; ldd >= N.
+ *  M >= 0 (M == 0 is a no-op), N % 32 == 0, K % 64 == 0.
+ *  ws/ws_bytes  unused by this op (may be NULL/0). */
+nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
+                             int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
+                             void *d, int out_dtype, int64_t ldd, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* W4A16 GEMM: y = alpha_eff * x (W.SFW)^T, x and y BF16, FP32 accumulation.
+ *  x  [M][ldx] BF16 (uint16 bit patterns), device, 16-byte aligned, ldx % 8 == 0, ldx >= K.
+ *  y  [M][ldy] BF16, device, 2-byte aligned, ldy >= N.
+ *  M >= 0, N % 32 == 0, K % 64 == 0.
+ *  ws  workspace of nvfp4_workspace_bytes(NVFP4_OP_W4A16, M, N, K) bytes,
+ *      zeroed once with nvfp4_workspace_init. Calls that share a workspace must
+ *      not run concurrently (use one workspace per stream). */
+nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_prep, int64_t M,
+                              int64_t N, int64_t K, float alpha, const float *alpha_dev, uint16_t *y,
+                              int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
+/* BF16 -> NVFP4 quantizer (the recipe: per-tensor g = 2688 / max|x| (1 if the
+ * tensor is zero); per 16-block scale = E4M3_RNE_sat((amax_b / 6) * g); codes =
+ * E2M1_RNE_sat(x * (g / scale)) with x's sign, all in IEEE FP32; zero-scale
+ * blocks get zero codes).
+ *  x       [rows][K] BF16, device, 16-byte aligned, K % 16 == 0 and K % 8 == 0.
+ *  codes   [rows][K/2] bytes out, 8-byte aligned.  scales [rows][K/16] UE4M3 bytes out.
+ *  g_dev   device float out: g.  inv_g_dev  device float out (may be NULL): 1/g in FP32.
+ *  ws      nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, 0, K) bytes (no init needed).
+ * Inputs must be finite. rows == 0 writes g = 1. */
+nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales,
+                            float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,219 @@
+"""Python binding of libnvfp4.so, the gfx950 NVFP4 block-scaled GEMM library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/nvfp4.h. torch supplies device
+memory and the current stream. There is no CPU fallback: without the built
+library every call raises.
+
+Entry points (same names as the C ABI):
+  nvfp4_prepare_weight(w_codes, w_scales, scale_kind="e4m3", out=None, bad_count=None)
+  nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None)
+  nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=None)
+  nvfp4_quantize(x, codes=None, scales=None, g=None, inv_g=None, ws=None)
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_VALUE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(9)
+SCALE_UE4M3, SCALE_E4M3 = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+OP_W4A4, OP_W4A16, OP_QUANTIZE = 0, 1, 2
+
+# C signatures: (name, restype, argtypes)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGS = [
+    ("nvfp4_init", ctypes.c_int, []),
+    ("nvfp4_status_string", ctypes.c_char_p, [ctypes.c_int]),
+    ("nvfp4_prepared_weight_bytes", ctypes.c_size_t, [_I64, _I64]),
+    ("nvfp4_workspace_bytes", ctypes.c_size_t, [ctypes.c_int, _I64, _I64, _I64]),
+    ("nvfp4_workspace_init", ctypes.c_int, [_P, ctypes.c_size_t, _P]),
+    ("nvfp4_prepare_weight", ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P]),
+    ("nvfp4_gemm_w4a4", ctypes.c_int,
+     [_P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P]),
+    ("nvfp4_gemm_w4a16", ctypes.c_int,
+     [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _I64, _P, ctypes.c_size_t, _P]),
+    ("nvfp4_quantize", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+]
+EXPORTED = [s[0] for s in _SIGS]
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m nvfp4_block_scaled_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in _SIGS:
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class NVFP4Error(RuntimeError):
+    pass
+
+
+def _check(status):
+    if status == OK:
+        return
+    msg = lib().nvfp4_status_string(status).decode()
+    if status == ERR_DTYPE:
+        raise TypeError(msg)
+    if status in (ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_WORKSPACE, ERR_NULL):
+        raise ValueError(msg)
+    raise NVFP4Error(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def init():
+    _check(lib().nvfp4_init())
+
+
+def prepared_weight_bytes(N, K):
+    return int(lib().nvfp4_prepared_weight_bytes(N, K))
+
+
+def workspace_bytes(op, M, N, K):
+    return int(lib().nvfp4_workspace_bytes(op, M, N, K))
+
+
+def workspace(op, M, N, K, device="cuda"):
+    """Allocate and zero a workspace for (op, M, N, K); None when the op needs none."""
+    n = workspace_bytes(op, M, N, K)
+    if n == 0:
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(lib().nvfp4_workspace_init(_ptr(ws), n, _stream()))
+    return ws
+
+
+def _u8(t, name):
+    t = _dev(t, name)
+    if t.dtype in (torch.uint8, torch.int8):
+        return t.view(torch.uint8)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    raise TypeError(f"{name} must hold bytes (uint8/int8/float8_e4m3fn), got {t.dtype}")
+
+
+def nvfp4_prepare_weight(w_codes, w_scales, scale_kind="e4m3", out=None, bad_count=None):
+    """Prepared copy of a weight ([N][K/2] packed codes, [N][K/16] scale bytes).
+
+    Returns (w_prep uint8 tensor, bad_count int32 device tensor)."""
+    w_codes = _u8(w_codes, "w_codes")
+    w_scales = _u8(w_scales, "w_scales")
+    if w_codes.dim() != 2 or w_scales.dim() != 2:
+        raise ValueError("w_codes and w_scales must be 2-D")
+    N, K2 = w_codes.shape
+    K = 2 * K2
+    if tuple(w_scales.shape) != (N, K // 16):
+        raise ValueError("w_scales must be [N][K/16]")
+    kind = {"e4m3": SCALE_E4M3, "ue4m3": SCALE_UE4M3}.get(scale_kind)
+    if kind is None:
+        raise TypeError("scale_kind must be 'e4m3' or 'ue4m3'")
+    nbytes = prepared_weight_bytes(N, K)
+    if nbytes == 0:
+        raise ValueError("N % 32 == 0 and K % 64 == 0 are required")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w_codes.device)
+    if bad_count is None:
+        bad_count = torch.empty(1, dtype=torch.int32, device=w_codes.device)
+    _check(lib().nvfp4_prepare_weight(_ptr(w_codes), _ptr(w_scales), kind, N, K, _ptr(out), _ptr(bad_count),
+                                      _stream()))
+    return out, bad_count
+
+
+def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None):
+    a_codes = _u8(a_codes, "a_codes")
+    a_scales = _u8(a_scales, "a_scales")
+    w_prep = _u8(w_prep, "w_prep")
+    M = a_codes.shape[0] if a_codes.dim() == 2 else 0
+    if a_codes.dim() != 2 or a_codes.shape[1] * 2 != K or tuple(a_scales.shape) != (M, K // 16):
+        raise ValueError("a_codes must be [M][K/2] and a_scales [M][K/16]")
+    if w_prep.numel() != prepared_weight_bytes(N, K):
+        raise ValueError("w_prep does not match (N, K)")
+    od = {"bf16": (OUT_BF16, torch.bfloat16), "f32": (OUT_F32, torch.float32)}.get(out_dtype)
+    if od is None:
+        raise TypeError("out_dtype must be 'bf16' or 'f32'")
+    if out is None:
+        out = torch.empty((M, N), dtype=od[1], device=a_codes.device)
+    elif out.dtype != od[1] or out.dim() != 2 or out.shape[0] != M or out.stride(1) != 1:
+        raise ValueError("out must be [M][>=N] rows of out_dtype")
+    if alpha_dev is not None and (alpha_dev.dtype != torch.float32 or not alpha_dev.is_cuda):
+        raise TypeError("alpha_dev must be a float32 device tensor")
+    _check(lib().nvfp4_gemm_w4a4(_ptr(a_codes), _ptr(a_scales), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
+                                 _ptr(out), od[0], out.stride(0), None, 0, _stream()))
+    return out
+
+
+def nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=None):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError("x must be a CUDA tensor")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if x.dim() != 2 or x.shape[1] != K or x.stride(1) != 1:
+        raise ValueError("x must be [M][K] with unit column stride")
+    if x.data_ptr() % 16 != 0 or x.stride(0) % 8 != 0:
+        x = x.contiguous().clone()          # misaligned activations are copied
+    M = x.shape[0]
+    w_prep = _u8(w_prep, "w_prep")
+    if w_prep.numel() != prepared_weight_bytes(N, K):
+        raise ValueError("w_prep does not match (N, K)")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[0] != M or out.stride(1) != 1:
+        raise ValueError("out must be [M][>=N] bfloat16")
+    if ws is None:
+        ws = workspace(OP_W4A16, M, N, K, x.device)
+    nws = 0 if ws is None else ws.numel()
+    _check(lib().nvfp4_gemm_w4a16(_ptr(x), x.stride(0), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
+                                  _ptr(out), out.stride(0), _ptr(ws), nws, _stream()))
+    return out
+
+
+def nvfp4_quantize(x, codes=None, scales=None, g=None, inv_g=None, ws=None):
+    """BF16 [rows][K] -> (codes [rows][K/2] uint8, scales [rows][K/16] uint8, g, inv_g) on the device."""
+    x = _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    rows, K = x.shape
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
+    if g is None:
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    if inv_g is None:
+        inv_g = torch.empty(1, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(OP_QUANTIZE, rows, 0, K), dtype=torch.uint8, device=dev)
+    _check(lib().nvfp4_quantize(_ptr(x), rows, K, _ptr(codes), _ptr(scales), _ptr(g), _ptr(inv_g), _ptr(ws),
+                                ws.numel(), _stream()))
+    return codes, scales, g, inv_g

@@ -1,0 +1,115 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments with the documented status before any
+launch (no GPU needed: every case here fails in the host-side checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = nv.lib()
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(nv.EXPORTED) == names
+
+
+def test_status_strings():
+    L = nv.lib()
+    assert L.nvfp4_status_string(0) == b"ok"
+    assert L.nvfp4_status_string(2) == b"bad shape"
+    assert L.nvfp4_status_string(99) == b"unknown status"
+
+
+def test_prepared_size():
+    L = nv.lib()
+    assert L.nvfp4_prepared_weight_bytes(34816, 5120) == 34816 * 5120 // 2 + 34816 * 5120 // 16
+    assert L.nvfp4_prepared_weight_bytes(33, 64) == 0
+    assert L.nvfp4_prepared_weight_bytes(32, 65) == 0
+    assert L.nvfp4_prepared_weight_bytes(0, 64) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)       # a non-null, 64 KiB-aligned value; never dereferenced
+ODD = ctypes.c_void_p(0x10001)
+
+
+def test_gemm_w4a4_argument_checks():
+    f = nv.lib().nvfp4_gemm_w4a4
+    ok = dict(a=FAKE, s=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ad=None, d=FAKE, dt=nv.OUT_BF16, ldd=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["a"], a["s"], a["w"], a["M"], a["N"], a["K"], a["alpha"], a["ad"], a["d"], a["dt"], a["ldd"],
+                 None, 0, None)
+    assert call(dt=7) == nv.ERR_DTYPE
+    assert call(K=96) == nv.ERR_SHAPE
+    assert call(N=48) == nv.ERR_SHAPE
+    assert call(M=-1) == nv.ERR_SHAPE
+    assert call(ldd=32) == nv.ERR_SHAPE
+    assert call(M=0) == nv.OK                     # empty: nothing to do, nothing launched
+    assert call(a=None) == nv.ERR_NULL
+    assert call(d=None) == nv.ERR_NULL
+    assert call(alpha=float("nan")) == nv.ERR_VALUE
+    assert call(alpha=float("inf")) == nv.ERR_VALUE
+    assert call(a=ODD) == nv.ERR_ALIGN
+    assert call(w=ODD) == nv.ERR_ALIGN
+
+
+def test_gemm_w4a16_argument_checks():
+    f = nv.lib().nvfp4_gemm_w4a16
+
+    def call(x=FAKE, ldx=128, w=FAKE, M=1, N=64, K=128, alpha=1.0, y=FAKE, ldy=64, ws=None, nws=0):
+        return f(x, ldx, w, M, N, K, alpha, None, y, ldy, ws, nws, None)
+    assert call(K=100) == nv.ERR_SHAPE
+    assert call(ldx=64) == nv.ERR_SHAPE
+    assert call(ldy=32) == nv.ERR_SHAPE
+    assert call(M=0) == nv.OK
+    assert call(x=None) == nv.ERR_NULL
+    assert call(alpha=float("-inf")) == nv.ERR_VALUE
+    assert call(ldx=132) == nv.ERR_ALIGN
+    assert call(x=ODD) == nv.ERR_ALIGN
+
+
+def test_prepare_and_quantize_argument_checks():
+    L = nv.lib()
+    p = L.nvfp4_prepare_weight
+    assert p(None, FAKE, nv.SCALE_E4M3, 32, 64, FAKE, None, None) == nv.ERR_NULL
+    assert p(FAKE, FAKE, 5, 32, 64, FAKE, None, None) == nv.ERR_DTYPE
+    assert p(FAKE, FAKE, nv.SCALE_E4M3, 33, 64, FAKE, None, None) == nv.ERR_SHAPE
+    assert p(FAKE, FAKE, nv.SCALE_E4M3, 32, 96, FAKE, None, None) == nv.ERR_SHAPE
+    assert p(ODD, FAKE, nv.SCALE_E4M3, 32, 64, FAKE, None, None) == nv.ERR_ALIGN
+    q = L.nvfp4_quantize
+    assert q(FAKE, 4, 32, FAKE, FAKE, None, None, FAKE, 4096, None) == nv.ERR_NULL
+    assert q(FAKE, 4, 24, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_SHAPE
+    assert q(FAKE, 4, 32, FAKE, FAKE, FAKE, None, None, 0, None) == nv.ERR_WORKSPACE
+    assert q(FAKE, 4, 32, FAKE, FAKE, FAKE, None, FAKE, 16, None) == nv.ERR_WORKSPACE
+    assert q(ODD, 4, 32, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_ALIGN
+
+
+def test_workspace_sizes():
+    L = nv.lib()
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 8192, 8192, 8192) == 0
+    assert L.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 0, 5120) >= 4
+    assert L.nvfp4_workspace_bytes(7, 1, 1, 1) == 0
+    assert L.nvfp4_workspace_init(None, 0, None) == nv.OK
+    assert L.nvfp4_workspace_init(None, 64, None) == nv.ERR_NULL
+    assert L.nvfp4_workspace_init(ODD, 64, None) == nv.ERR_ALIGN
+
+
+def test_python_wrapper_type_errors():
+    import torch
+    with pytest.raises(TypeError):
+        nv.nvfp4_gemm_w4a16(torch.zeros(2, 64), None, 32, 64)

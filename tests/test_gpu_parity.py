@@ -1,0 +1,325 @@
+"""GPU parity of the HIP library against the CPU oracle, through the C ABI.
+
+Byte outputs (prepared weights, quantized codes and scales, g) must match
+bit for bit; GEMM outputs must lie inside the stated FP32 / BF16 error bound
+of the exact result (tests/gpu_helpers.py). All inputs are seeded (synth.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_amd as nv
+import synth
+from oracle import formats, gemm, prepared, quantize
+from gpu_helpers import alpha_ab, assert_close, dev, gpu_quantize_checked, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _init():
+    nv.init()
+
+
+def _random_nvfp4(seed, rows, K, lo=-4, hi=4):
+    codes = formats.pack_nibbles(synth.random_codes(seed, rows, K))
+    scales = formats.round_e4m3_byte(synth.loguniform_scale_targets(seed + 1000, rows, K // 16, lo, hi))
+    return codes, scales
+
+
+def _prep(codes, scales, kind="e4m3"):
+    wp, bad = nv.nvfp4_prepare_weight(dev(codes), dev(scales), kind)
+    torch.cuda.synchronize()
+    return wp, int(bad.item())
+
+
+# ------------------------------------------------------------------ prepare
+
+@pytest.mark.parametrize("kind", ["e4m3", "ue4m3"])
+def test_prepare_bit_exact(kind):
+    N, K = 96, 320
+    codes, _ = _random_nvfp4(1, N, K)
+    r = np.random.default_rng(2)
+    scales = r.integers(0, 256, (N, K // 16), dtype=np.uint8)   # every byte: negatives, zeros, NaNs
+    wp, bad = _prep(codes, scales, kind)
+    ref, bad_ref = prepared.prepare_weight(codes, scales, kind)
+    np.testing.assert_array_equal(wp.cpu().numpy(), ref)
+    assert bad == bad_ref and bad > 0
+
+
+def test_prepare_decode_shape_bit_exact():
+    N, K = synth.DECODE_SHAPES[0]
+    codes, scales = _random_nvfp4(3, N, K)
+    wp, bad = _prep(codes, scales)
+    ref, _ = prepared.prepare_weight(codes, scales)
+    assert bad == 0
+    np.testing.assert_array_equal(wp.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ quantize
+
+@pytest.mark.parametrize("rows,K", [(1, 16), (3, 32), (77, 640), (256, 5120)])
+def test_quantize_bit_exact(rows, K):
+    x = synth.normal_bf16(rows * 7 + K, rows, K)
+    codes, scales, g, inv_g = nv.nvfp4_quantize(dev(x).view(torch.bfloat16))
+    c_ref, s_ref, g_ref, ig_ref = quantize.quantize(x)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    assert np.float32(g.item()) == g_ref and np.float32(inv_g.item()) == ig_ref
+
+
+def test_quantize_edge_values():
+    # zeros, a zero block, ties on the E2M1 grid, tiny values, both signs, sign of zero
+    vals = np.zeros((4, 64), np.float32)
+    vals[0, :16] = [6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, -.25, -.75, -2.5, -5, .1, 5.9, 0, -0.0]
+    vals[1, 16:32] = [1, .5, .400390625, -1] + [0] * 12
+    vals[2, :] = np.linspace(-1e-3, 1e-3, 64)
+    vals[3, 5] = -1e-30
+    x = formats.f32_to_bf16_bits(vals)
+    codes, scales, g, _ = nv.nvfp4_quantize(dev(x).view(torch.bfloat16))
+    c_ref, s_ref, g_ref, _ = quantize.quantize(x)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    z = np.zeros((2, 32), np.uint16)
+    codes, scales, g, inv_g = nv.nvfp4_quantize(dev(z).view(torch.bfloat16))
+    assert g.item() == 1.0 and not codes.any() and not scales.any()
+
+
+def test_quantize_prefill_activation_full():
+    x, _ = synth.prefill_activation()
+    codes, scales, g, inv_g = nv.nvfp4_quantize(dev(x).view(torch.bfloat16))
+    c_ref, s_ref, g_ref, ig_ref = quantize.quantize(x)
+    assert np.float32(g.item()) == g_ref and np.float32(inv_g.item()) == ig_ref
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+
+
+# ------------------------------------------------------------------ W4A4
+
+def _w4a4(a, sa, b, sb, alpha, out_dtype, alpha_dev=None):
+    N, K = b.shape[0], b.shape[1] * 2
+    wp, bad = _prep(b, sb)
+    assert bad == 0
+    ad = None if alpha_dev is None else torch.tensor([alpha_dev], dtype=torch.float32, device="cuda")
+    out = nv.nvfp4_gemm_w4a4(dev(a), dev(sa), wp, N, K, alpha, ad, out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_w4a4_random_codes_256_f32_and_repeat():
+    """Random codes (all 16) with log-uniform scales, 256^3, alpha = 1, FP32 out."""
+    c = synth.small_random_case(256, 256, 256, seed=0)
+    a, b = formats.pack_nibbles(c["a_codes"]), formats.pack_nibbles(c["b_codes"])
+    sa, sb = formats.round_e4m3_byte(c["a_scale_targets"]), formats.round_e4m3_byte(c["b_scale_targets"])
+    out = _w4a4(a, sa, b, sb, 1.0, "f32")
+    D, S = gemm.w4a4_exact(a, sa, b, sb, 1.0)
+    assert_close(host(out), D, S, bf16=False, what="256^3 f32")
+    out2 = _w4a4(a, sa, b, sb, 1.0, "f32")
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 32, 64), (300, 320, 192), (513, 256, 128), (77, 544, 320), (256, 512, 1024)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_w4a4_ragged_shapes(M, N, K, out_dtype):
+    a, sa = _random_nvfp4(M + 11, M, K)
+    b, sb = _random_nvfp4(N + 13, N, K)
+    alpha = 0.37
+    out = _w4a4(a, sa, b, sb, alpha, out_dtype)
+    D, S = gemm.w4a4_exact(a, sa, b, sb, alpha)
+    assert_close(host(out), D, S, bf16=out_dtype == "bf16", what=f"{M}x{N}x{K}")
+
+
+def test_w4a4_closed_forms():
+    M = N = 64
+    K = 256
+    ones = np.full((M, K // 2), 0x22, np.uint8)
+    s1 = np.full((M, K // 16), 0x38, np.uint8)
+    out = _w4a4(ones, s1, ones, s1, 1.0, "f32")
+    assert (host(out) == K).all()
+    # largest magnitude, exactly representable: K * 2688^2
+    six = np.full((M, K // 2), 0x77, np.uint8)
+    smax = np.full((M, K // 16), 0x7E, np.uint8)
+    out = _w4a4(six, smax, six, smax, 1.0, "f32")
+    assert (host(out) == K * 2688.0 ** 2).all()
+    # identity A picks rows of B~
+    eye = np.zeros((K, K), np.uint8)
+    eye[np.arange(K), np.arange(K)] = 0x2
+    b, sb = _random_nvfp4(5, N, K)
+    out = _w4a4(formats.pack_nibbles(eye), np.full((K, K // 16), 0x38, np.uint8), b, sb, 1.0, "f32")
+    np.testing.assert_array_equal(host(out), gemm.decode_nvfp4(b, sb).T)
+    # alpha from a device scalar multiplies in FP32
+    out = _w4a4(ones, s1, ones, s1, 0.5, "f32", alpha_dev=0.25)
+    assert (host(out) == K * 0.125).all()
+
+
+def test_w4a4_nan_scale_propagates_to_its_row():
+    M, N, K = 64, 64, 128
+    a, sa = _random_nvfp4(21, M, K)
+    b, sb = _random_nvfp4(22, N, K)
+    sa[7, 3] = 0x7F
+    out = host(_w4a4(a, sa, b, sb, 1.0, "f32"))
+    assert np.isnan(out[7]).all() and not np.isnan(np.delete(out, 7, axis=0)).any()
+
+
+def test_w4a4_normal_2048_bf16_full():
+    S = 2048
+    xa, xb = synth.square_normal(S, "A"), synth.square_normal(S, "B")
+    a, sa, gA, _ = quantize.quantize(xa)
+    b, sb, gB, _ = quantize.quantize(xb)
+    alpha = alpha_ab(gA, gB)
+    out = _w4a4(a, sa, b, sb, float(alpha), "bf16")
+    D, Sabs = gemm.w4a4_exact(a, sa, b, sb, alpha)
+    assert_close(host(out), D, Sabs, bf16=True, what="2048^3 bf16")
+
+
+def _square_sampled(S, gen, n_rows=96, n_cols=96, extra_rows=()):
+    """The product path at full size (GPU quantize of A and B, prepare, GEMM in
+    the benchmark's launch configuration) checked on sampled outputs."""
+    xa, xb = gen(S, "A"), gen(S, "B")
+    if isinstance(xa, tuple):
+        xa, xb = xa[0], xb[0]
+    r = np.random.default_rng(S)
+    rows = np.unique(np.concatenate([r.choice(S, n_rows, replace=False), np.asarray(extra_rows, int), [0, S - 1]]))
+    cols = np.unique(np.concatenate([r.choice(S, n_cols, replace=False), [0, S - 1]]))
+    ca, sa, _, _, gA = gpu_quantize_checked(nv, xa, rows)
+    cb, sb, _, _, gB = gpu_quantize_checked(nv, xb, cols)
+    wp, bad = nv.nvfp4_prepare_weight(cb, sb, "ue4m3")
+    alpha = alpha_ab(gA, gB)
+    out = nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, float(alpha), None, "bf16")
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    got = host(out[torch.as_tensor(rows).cuda()][:, torch.as_tensor(cols).cuda()])
+    a_ref, sa_ref = quantize.quantize_rows_with_g(xa[rows], gA)
+    b_ref, sb_ref = quantize.quantize_rows_with_g(xb[cols], gB)
+    D, Sabs = gemm.w4a4_exact(a_ref, sa_ref, b_ref, sb_ref, alpha)
+    assert_close(got, D, Sabs, bf16=True, what=f"{S}^3 sampled")
+    return out
+
+
+def test_w4a4_normal_8192_sampled():
+    _square_sampled(8192, synth.square_normal)
+
+
+@pytest.mark.slow
+def test_w4a4_large_16384_sampled():
+    S = 16384
+    _, outl, _ = synth.square_large(S, "A")
+    _square_sampled(S, synth.square_large, extra_rows=outl[:32])
+
+
+# ------------------------------------------------------------------ W4A16
+
+_DECODE_W = {}
+
+
+def _decode_weight(j):
+    if j not in _DECODE_W:
+        _DECODE_W[j] = synth.decode_weight(j)
+    return _DECODE_W[j]
+
+
+def _w4a16_case(M, N, K, seed, alpha=0.75):
+    b, sb = _random_nvfp4(seed, N, K, -3, 3)
+    x = synth.normal_bf16(seed + 1, M, K)
+    wp, bad = _prep(b, sb)
+    return x, b, sb, wp, alpha
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 17, 32, 64, 128, 300])
+@pytest.mark.parametrize("N,K", [(96, 192), (320, 640)])
+def test_w4a16_small_shapes(M, N, K):
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 31 + N)
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
+    torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"w4a16 M={M} {N}x{K}")
+
+
+@pytest.mark.parametrize("j", range(4))
+@pytest.mark.parametrize("mi", range(5))
+def test_w4a16_decode_shapes(j, mi):
+    """27B-class layer shapes with W ~ N(0, 0.02) quantized on the GPU (sampled rows
+    checked bit-exact), x ~ N(0, 1); outputs checked on sampled weight rows."""
+    M = synth.DECODE_MS[mi]
+    N, K = synth.DECODE_SHAPES[j]
+    w = _decode_weight(j)
+    x = synth.decode_activation(M, j, mi)
+    r = np.random.default_rng(j * 10 + mi)
+    cols = np.unique(np.concatenate([r.choice(N, 128, replace=False), [0, N - 1]]))
+    cw, sw, _, _, gW = gpu_quantize_checked(nv, w, cols)
+    wp, bad = nv.nvfp4_prepare_weight(cw, sw, "ue4m3")
+    alpha = np.float32(np.float32(1.0) / gW)
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, float(alpha))
+    out2 = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, float(alpha))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "repeat calls must be bit-identical"
+    rows = np.arange(M) if M <= 32 else np.unique(np.concatenate([r.choice(M, 16, replace=False), [M - 1]]))
+    got = host(out[torch.as_tensor(rows).cuda()][:, torch.as_tensor(cols).cuda()])
+    c_ref, s_ref = quantize.quantize_rows_with_g(w[cols], gW)
+    y, S = gemm.w4a16(x[rows], c_ref, s_ref, alpha)
+    assert_close(got, y, S, bf16=True, what=f"decode {N}x{K} M={M}")
+
+
+def test_w4a16_zero_negative_scales_and_strided_out():
+    M, N, K = 3, 64, 256
+    b, sb = _random_nvfp4(41, N, K)
+    sb[0, :] = 0x00
+    sb[1, :] |= 0x80            # negative scales
+    sb[2, 1] = 0x80             # -0
+    x = synth.normal_bf16(42, M, K)
+    wp, bad = _prep(b, sb)
+    assert bad == 0
+    big = torch.zeros((M, N + 64), dtype=torch.bfloat16, device="cuda")
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, 1.0, out=big[:, :N])
+    torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, 1.0)
+    assert_close(host(big[:, :N]), y, S, bf16=True, what="signed scales")
+    assert (host(big[:, N:]) == 0).all()
+
+
+def test_w4a16_graph_capture_replay_matches_eager():
+    M, N, K = 1, 5120, 5120
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, 77)
+    xd = dev(x).view(torch.bfloat16).clone()
+    ws = nv.workspace(nv.OP_W4A16, M, N, K)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    nv.nvfp4_gemm_w4a16(xd, wp, N, K, alpha, out=out, ws=ws)   # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            nv.nvfp4_gemm_w4a16(xd, wp, N, K, alpha, out=out, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xn = synth.normal_bf16(900 + rep, M, K)
+        xd.copy_(dev(xn).view(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        eager = nv.nvfp4_gemm_w4a16(dev(xn).view(torch.bfloat16), wp, N, K, alpha)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+
+
+# ------------------------------------------------------------------ prefill W4A4 with on-device quantize
+
+def test_prefill_quantize_then_w4a4_sampled():
+    x, _ = synth.prefill_activation()
+    w = synth.prefill_weight()
+    M, K = x.shape
+    N = w.shape[0]
+    r = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([r.choice(M, 64, replace=False), [M - 1]]))
+    cols = np.unique(np.concatenate([r.choice(N, 64, replace=False), [N - 1]]))
+    cw, sw, _, _, gW = gpu_quantize_checked(nv, w, cols)
+    wp, _ = nv.nvfp4_prepare_weight(cw, sw, "ue4m3")
+    ca, sa, gA_dev, inv_gA, gA = gpu_quantize_checked(nv, x, rows)
+    alpha_w = np.float32(np.float32(1.0) / gW)
+    out = nv.nvfp4_gemm_w4a4(ca, sa, wp, N, K, float(alpha_w), inv_gA, "bf16")
+    torch.cuda.synchronize()
+    alpha_eff = gemm.alpha_product(alpha_w, np.float32(np.float32(1.0) / gA))
+    a_ref, sa_ref = quantize.quantize_rows_with_g(x[rows], gA)
+    b_ref, sb_ref = quantize.quantize_rows_with_g(w[cols], gW)
+    D, S = gemm.w4a4_exact(a_ref, sa_ref, b_ref, sb_ref, alpha_eff)
+    got = host(out[torch.as_tensor(rows).cuda()][:, torch.as_tensor(cols).cuda()])
+    assert_close(got, D, S, bf16=True, what="prefill")
