@@ -195,12 +195,22 @@ def main():
     ap.add_argument("--size", type=int, default=8192)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
+    if args.copy_ref:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_ref_bytes_read": 1 << 30, "copy_ref_bytes_written": 1 << 30}), flush=True)
+        return
     import nvfp4_block_scaled_amd as nv
     nv.init()
     S = args.size

@@ -80,10 +80,11 @@ nvfp4_status nvfp4_workspace_init(void *ws, size_t ws_bytes, void *stream);
  *  N % 32 == 0, K % 64 == 0.
  *  w_prep   nvfp4_prepared_weight_bytes(N, K) bytes, device, 16-byte aligned.
  * The prepared layout: 32 (n) x 64 (k) tiles in n-major, k-minor order; the
- * first N*K/2 bytes hold 1024-byte code tiles (row r of the tile at bytes
- * 32r..32r+31, standard packing), the rest 128-byte scale tiles (row r, block b
- * at byte 4r+b). Blocks with a zero scale get zero codes and scale 0; blocks
- * with a negative scale get their code signs flipped and the scale magnitude;
+ * first N*K/2 bytes hold 1024-byte code tiles of 64 16-byte units, unit
+ * 32h + r holding the standard-packed codes of row r for k in [32h, 32h+32)
+ * of the tile; the rest are 128-byte scale tiles in the same order (row r,
+ * block b at byte 4r+b). Blocks with a zero scale get zero codes and scale 0;
+ * blocks with a negative scale get their code signs flipped and the scale magnitude;
  * NaN scale bytes (and, for UE4M3, bytes with bit 7 set) keep their codes, get
  * scale byte 0x7F (NaN) and are counted.
  *  bad_count_dev  device int32 or NULL; when given it is overwritten with the

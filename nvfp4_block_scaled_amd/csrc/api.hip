@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint8_t *__restrict_
   const int64_t tile = (n / 32) * (K / 64) + b / 4;
   const int64_t r = n % 32;
   const int64_t bb = b % 4;
-  *reinterpret_cast<u32x2_t *>(prep + tile * 1024 + r * 32 + bb * 8) = c;
+  // chunk byte 8 bb of row r: 16-byte unit 32 (bb / 2) + r, byte 8 (bb % 2)
+  *reinterpret_cast<u32x2_t *>(prep + tile * 1024 + 16 * (32 * (bb >> 1) + r) + 8 * (bb & 1)) = c;
   prep[N * K / 2 + tile * 128 + r * 4 + bb] = (uint8_t)out_s;
 }
 

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const uint16_t *
   const int r = lane & 15, q = lane >> 4, th = q >> 1, kh = q & 1;
   const int64_t ng = blockIdx.x >> 1;
   const int row = (blockIdx.x & 1) * 16 + r;                 // row inside the 32-row tile
-  const uint8_t *codes = wp + ((ng * T) << 10) + row * 32 + kh * 16;
+  const uint8_t *codes = wp + ((ng * T) << 10) + 16 * (32 * kh + row);
   const uint8_t *scl = wp + N * K / 2 + ((ng * T) << 7) + row * 4;
   float acc[M];
 #pragma unroll
@@ -250,7 +250,7 @@ __device__ __forceinline__ void tile_compute(const uint8_t *lds, int wm, int wn,
 #pragma unroll
   for (int j = 0; j < 2; j++) {
     const int g = wn * 2 + j;
-    wf[j] = *reinterpret_cast<const u32x4_t *>(lds + WC_OFF + g * 1024 + r * 32 + h * 16);
+    wf[j] = *reinterpret_cast<const u32x4_t *>(lds + WC_OFF + g * 1024 + 16 * (32 * h + r));
     const uint32_t sw = *reinterpret_cast<const uint32_t *>(lds + WS_OFF + g * 128 + r * 4);
     sc[j] = e4m3x2_to_f32(sw >> (16 * h));
   }

@@ -10,10 +10,12 @@ same size as the checkpoint tensors, N*K/2 + N*K/16 bytes.
 Layout (this library's own design, written here as a plain index map). The
 weight W [N][K] is cut into tiles of 32 rows (n) x 64 columns (k); tiles are
 numbered t = (n // 32) * (K // 64) + (k // 64). The first N*K/2 bytes are the
-code tiles, 1024 bytes each: byte 32*r + j of tile t is byte j of the k-chunk's
-32 packed bytes of row r (element 2j in the low nibble, 2j+1 in the high). The
-next N*K/16 bytes are the scale tiles, 128 bytes each: byte 4*r + b of tile t is
-the (folded) scale of row r, block b (k in [16b, 16b+16) of the chunk).
+code tiles, 1024 bytes each, as 64 units of 16 bytes: unit 32*h + r holds bytes
+16h .. 16h+15 of row r's 32 packed bytes of the k-chunk (element 2j in the low
+nibble of byte j, 2j+1 in the high), i.e. codes of k in [32h, 32h+32). So byte
+j of row r sits at 16 * (32 * (j // 16) + r) + j % 16. The next N*K/16 bytes
+are the scale tiles, 128 bytes each: byte 4*r + b of tile t is the (folded)
+scale of row r, block b (k in [16b, 16b+16) of the chunk).
 
 Scale-byte validity: for E4M3 input 0x7F and 0xFF are NaN; for UE4M3 input a
 byte with bit 7 set is invalid, as is 0x7F. Invalid bytes are counted; their
@@ -60,8 +62,8 @@ def prepare_weight(codes_packed, scale_bytes, scale_kind="e4m3"):
     assert N % TILE_N == 0 and K % TILE_K == 0
     nt, kt = N // TILE_N, K // TILE_K
     out = np.empty(N * K2 + N * (K // 16), dtype=np.uint8)
-    # code byte (n, j) -> tile (n//32, j//32), in-tile offset 32*(n%32) + j%32
-    c = codes.reshape(nt, TILE_N, kt, 32).transpose(0, 2, 1, 3)
+    # code byte (n, j) -> tile (n//32, j//32), unit 32*((j%32)//16) + n%32, byte j%16
+    c = codes.reshape(nt, TILE_N, kt, 2, 16).transpose(0, 2, 3, 1, 4)
     out[:N * K2] = c.reshape(-1)
     # scale byte (n, b) -> tile (n//32, b//4), in-tile offset 4*(n%32) + b%4
     s = scales.reshape(nt, TILE_N, kt, 4).transpose(0, 2, 1, 3)
@@ -74,7 +76,8 @@ def prepared_offsets(n, k, N, K):
     tile = (n // TILE_N) * (K // TILE_K) + (k // TILE_K)
     r = n % TILE_N
     kk = k % TILE_K
-    code_off = tile * 1024 + 32 * r + kk // 2
+    j = kk // 2
+    code_off = tile * 1024 + 16 * (32 * (j // 16) + r) + j % 16
     scale_off = N * K // 2 + tile * 128 + 4 * r + kk // 16
     return code_off, kk % 2, scale_off
 
@@ -83,7 +86,7 @@ def unprepare(prep, N, K):
     """Inverse map: prepared bytes -> ([N][K/2] codes, [N][K/16] scales)."""
     prep = np.asarray(prep, dtype=np.uint8)
     nt, kt = N // TILE_N, K // TILE_K
-    c = prep[:N * K // 2].reshape(nt, kt, TILE_N, 32).transpose(0, 2, 1, 3).reshape(N, K // 2)
+    c = prep[:N * K // 2].reshape(nt, kt, 2, TILE_N, 16).transpose(0, 3, 1, 2, 4).reshape(N, K // 2)
     s = prep[N * K // 2:].reshape(nt, kt, TILE_N, 4).transpose(0, 2, 1, 3).reshape(N, K // 16)
     return c.copy(), s.copy()
 

@@ -352,15 +352,18 @@ def test_prepared_hand_checked_tile():
     scales[3, 5] = 0x40
     prep, bad = prepared.prepare_weight(codes, scales)
     assert bad == 0 and prep.size == N * K // 2 + N * K // 16
-    assert prep[0] == 0x10            # row 0, k 0,1 -> codes 0,1
-    assert prep[32] == 0x21           # row 1, k 0,1 -> codes 1,2
-    assert prep[32 * 15] == 0x0F      # row 15, k 0,1 -> codes 15,0
+    assert prep[0] == 0x10            # unit 0 = row 0, k 0,1 -> codes 0,1
+    assert prep[16] == 0x21           # unit 1 = row 1, k 0,1 -> codes 1,2
+    assert prep[16 * 15] == 0x0F      # unit 15 = row 15, k 0,1 -> codes 15,0
+    assert prep[16 * 37 + 4] == 0xED  # unit 32 + 5 = row 5, k 32+8, 32+9 -> codes 13, 14
     assert prep[1024] == 0x10         # tile 1 (k 64..127), row 0, k 64,65 -> codes 0,1
-    assert prep[1024 + 32 * 2 + 3] == ((2 + 64 + 6) % 16) | (((2 + 64 + 7) % 16) << 4)
+    assert prep[1024 + 16 * 2 + 3] == ((2 + 64 + 6) % 16) | (((2 + 64 + 7) % 16) << 4)
     # scale (3, 5): tile 1 (blocks 4..7), row 3, block 1 -> 2048 + 128 + 4*3 + 1
     assert prep[2048 + 128 + 13] == 0x40
     off, nib, soff = prepared.prepared_offsets(3, 64 + 16 + 5, N, K)
-    assert (off, nib, soff) == (1024 + 96 + 10, 1, 2048 + 128 + 13)
+    assert (off, nib, soff) == (1024 + 16 * 3 + 10, 1, 2048 + 128 + 13)
+    off, nib, _ = prepared.prepared_offsets(5, 40, N, K)
+    assert (off, nib) == (16 * 37 + 4, 0)
 
 
 def test_prepared_bijection_and_folding():
