@@ -65,13 +65,13 @@ const char *nvfp4_status_string(int status);
 size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
 
 /* Workspace bytes an op needs for (M, N, K); 0 means no workspace is used.
- * The workspace holds split-K partial sums and arrival tickets (W4A16) or
- * per-workgroup maxima (quantize). */
+ * The workspace holds split-K partial sums (W4A16) or per-workgroup maxima
+ * (quantize); every call overwrites what it reads. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* Zeroes a workspace on `stream` with a fill kernel (no hipMemset, so it may be
- * captured). Required once after allocation; the library leaves the ticket
- * area zeroed again after every call. */
+ * captured). The current kernels do not need a zeroed workspace; the call is
+ * kept so that a caller can clear one without hipMemset. */
 nvfp4_status nvfp4_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Prepare a weight once (TileLang PR #3290, "Design: Weight layout").
@@ -112,9 +112,9 @@ nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, co
  *  x  [M][ldx] BF16 (uint16 bit patterns), device, 16-byte aligned, ldx % 8 == 0, ldx >= K.
  *  y  [M][ldy] BF16, device, 2-byte aligned, ldy >= N.
  *  M >= 0, N % 32 == 0, K % 64 == 0.
- *  ws  workspace of nvfp4_workspace_bytes(NVFP4_OP_W4A16, M, N, K) bytes,
- *      zeroed once with nvfp4_workspace_init. Calls that share a workspace must
- *      not run concurrently (use one workspace per stream). */
+ *  ws  workspace of nvfp4_workspace_bytes(NVFP4_OP_W4A16, M, N, K) bytes (may be
+ *      NULL when that is 0). Calls that share a workspace must not run
+ *      concurrently (use one workspace per stream). */
 nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_prep, int64_t M,
                               int64_t N, int64_t K, float alpha, const float *alpha_dev, uint16_t *y,
                               int64_t ldy, void *ws, size_t ws_bytes, void *stream);
