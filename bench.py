@@ -4,7 +4,11 @@
 Step = one W4A4 NVFP4 GEMM D = alpha (A.SFA)(B.SFB)^T at M = N = K = 8192 with
 BF16 output: A and B are BF16 N(0,1) tensors quantized on the device by the
 library's quantizer, B prepared once (untimed), all inputs resident in HBM
-when the timed region starts. `value` is TFLOP/s (2 M N K per step).
+when the timed region starts. `value` is TFLOP/s (2 M N K per step). One
+step is one nvfp4_gemm_w4a4 call: the copy of A into the tile layout (in the
+workspace) and the GEMM kernel. The default 50 warm-up steps (about 45 ms)
+bring the chip to its steady clock under this load; the first ~25 calls after
+idle run up to 10 % slower while the clock ramps.
 
 Extra figures in the same JSON line: W4A16 decode (M = 1) achieved HBM GB/s on
 the 27B-class layer shapes with weights rotated over >= 1 GiB (CUDA-graph
@@ -12,7 +16,7 @@ replay), the prefill W4A4 with on-device activation quantization, and the
 other square sizes. `roofline` describes the dominant kernel (the W4A4 GEMM);
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-extras] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-extras] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -81,7 +85,8 @@ def w4a4_square(nv, S, steps, warmup, gen=None):
     del cb, sb
     alpha = float(np.float32(1.0) / np.float32(np.float32(gA.item()) * np.float32(gB.item())))
     out = torch.empty((S, S), dtype=torch.bfloat16, device="cuda")
-    ms = time_calls(lambda: nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, alpha, None, "bf16", out), steps, warmup)
+    ws = torch.empty(nv.workspace_bytes(nv.OP_W4A4, S, S, S), dtype=torch.uint8, device="cuda")
+    ms = time_calls(lambda: nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, alpha, None, "bf16", out, ws), steps, warmup)
     return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12
 
 
@@ -151,8 +156,10 @@ def prefill(nv, steps, warmup):
     ig = torch.empty(1, dtype=torch.float32, device="cuda")
     qws = torch.empty(nv.workspace_bytes(nv.OP_QUANTIZE, M, 0, K), dtype=torch.uint8, device="cuda")
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gws = torch.empty(nv.workspace_bytes(nv.OP_W4A4, M, N, K), dtype=torch.uint8, device="cuda")
     q_ms = time_calls(lambda: nv.nvfp4_quantize(xd, codes, scales, g, ig, qws), steps, warmup)
-    g_ms = time_calls(lambda: nv.nvfp4_gemm_w4a4(codes, scales, wp, N, K, alpha_w, ig, "bf16", out), steps, warmup)
+    g_ms = time_calls(lambda: nv.nvfp4_gemm_w4a4(codes, scales, wp, N, K, alpha_w, ig, "bf16", out, gws), steps,
+                      warmup)
     q_bytes = M * K * 2 + M * K // 2 + M * K // 16
     return dict(M=M, N=N, K=K, quantize_us=round(q_ms * 1e3, 1),
                 quantize_GBps=round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
@@ -190,8 +197,8 @@ def cpu_baseline(S=8192, rows=2048, cols=8192):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--size", type=int, default=8192)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -65,7 +65,8 @@ const char *nvfp4_status_string(int status);
 size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
 
 /* Workspace bytes an op needs for (M, N, K); 0 means no workspace is used.
- * The workspace holds split-K partial sums (W4A16) or per-workgroup maxima
+ * The workspace holds A in the prepared tile layout (W4A4: (M rounded up to
+ * 32) * K * 9/16 bytes), split-K partial sums (W4A16) or per-workgroup maxima
  * (quantize); every call overwrites what it reads. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
@@ -102,7 +103,10 @@ nvfp4_status nvfp4_prepare_weight(const uint8_t *w_codes, const uint8_t *w_scale
  *  d        [M][ldd] elements of out_dtype (FP32 or BF16 with round-to-nearest-
  *           even), device, element-aligned; ldd >= N.
  *  M >= 0 (M == 0 is a no-op), N % 32 == 0, K % 64 == 0.
- *  ws/ws_bytes  unused by this op (may be NULL/0). */
+ *  ws  workspace of nvfp4_workspace_bytes(NVFP4_OP_W4A4, M, N, K) bytes, device,
+ *      16-byte aligned, no initialisation needed: the call first copies A into
+ *      it in the prepared tile layout, then runs the GEMM from there. Calls that
+ *      share a workspace must not run concurrently. */
 nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
                              int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
                              void *d, int out_dtype, int64_t ldd, void *ws, size_t ws_bytes,

@@ -149,7 +149,7 @@ def nvfp4_prepare_weight(w_codes, w_scales, scale_kind="e4m3", out=None, bad_cou
     return out, bad_count
 
 
-def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None):
+def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None, ws=None):
     a_codes = _u8(a_codes, "a_codes")
     a_scales = _u8(a_scales, "a_scales")
     w_prep = _u8(w_prep, "w_prep")
@@ -167,8 +167,11 @@ def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, 
         raise ValueError("out must be [M][>=N] rows of out_dtype")
     if alpha_dev is not None and (alpha_dev.dtype != torch.float32 or not alpha_dev.is_cuda):
         raise TypeError("alpha_dev must be a float32 device tensor")
+    if ws is None and M > 0:
+        ws = torch.empty(workspace_bytes(OP_W4A4, M, N, K), dtype=torch.uint8, device=a_codes.device)
+    nws = 0 if ws is None else ws.numel()
     _check(lib().nvfp4_gemm_w4a4(_ptr(a_codes), _ptr(a_scales), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
-                                 _ptr(out), od[0], out.stride(0), None, 0, _stream()))
+                                 _ptr(out), od[0], out.stride(0), _ptr(ws), nws, _stream()))
     return out
 
 

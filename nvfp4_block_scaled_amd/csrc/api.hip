@@ -105,7 +105,7 @@ const char *nvfp4_status_string(int s) {
 
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
   switch (op) {
-    case NVFP4_OP_W4A4: return 0;
+    case NVFP4_OP_W4A4: return w4a4_workspace_bytes(M, K);
     case NVFP4_OP_W4A16: return w4a16_workspace_bytes(M, N, K);
     case NVFP4_OP_QUANTIZE: return quantize_workspace_bytes(M, K);
     default: return 0;

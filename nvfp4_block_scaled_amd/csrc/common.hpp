@@ -104,6 +104,7 @@ struct DeviceInfo {
 nvfp4_status device_info(DeviceInfo *out);
 
 // Workspace sizes of the ops that use one (0 = none).
+size_t w4a4_workspace_bytes(int64_t M, int64_t K);
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t quantize_workspace_bytes(int64_t rows, int64_t K);
 

@@ -9,23 +9,24 @@
 //  * Workgroup tile 256 x 256, four waves in a 2 x 2 arrangement, each owning a
 //    128 x 128 block of D as 4 x 4 MFMA tiles (256 FP32 accumulators per lane,
 //    held in the accumulation registers).
+//  * A is first copied into the workspace in the prepared-weight tile layout
+//    (32 rows x 64 k per 1 KB code tile, 128-byte scale tiles), one 16-byte
+//    unit per thread; W is already in it. A wave's fragment of one 32-row group
+//    for one K chunk is then one contiguous 1 KB load, for A as for W: reading
+//    A in its row-major layout instead touches 32 cache lines per load
+//    instruction, and measured about 14 % slower overall.
 //  * Each wave streams its own packed fragments from global memory straight
 //    into registers: per 64-wide K chunk, 16 packed bytes (32 codes of one row)
 //    and one scale word for each of its four A row groups and four W column
 //    groups. Buffer loads with 32-bit lane offsets and the hardware range check
-//    (ragged rows and columns read as zero). Chunks are loaded two ahead into a
+//    (groups past the matrix read as zero). Chunks are loaded two ahead into a
 //    three-deep register ring; no LDS and no barriers in the main loop. (On
 //    this part, staging the packed bytes through LDS -- shared by the two waves
-//    that use each fragment -- measured no faster: the unpack and the memory
-//    instructions themselves, not L2 bandwidth, bound the loop.)
+//    that use each fragment -- measured no faster.)
 //  * The FP16 operands exist only in registers: cvt_scalef32_pk_f16_fp4 (code
 //    pairs, scale operand 1.0) + v_pk_mul_f16 by the block scale, one vector
 //    instruction per element, unpacked one MFMA step ahead and interleaved one
 //    MFMA to four vector instructions.
-//  * W is read in the prepared layout: 1 KB tiles of 64 16-byte units (unit
-//    32h + r = row r, k in [32h, 32h+32)), so a wave's W fragment load is one
-//    contiguous 1 KB; A is read in the standard packed layout (32 bytes of a
-//    row per chunk).
 //  * Persistent grid (one workgroup per CU) walking the tiles in an XCD-aware,
 //    grouped order: workgroups that run on the same XCD (hardware ids congruent
 //    mod 8) take consecutive tile indices, and consecutive indices cover a
@@ -48,9 +49,39 @@ constexpr int kThreads = 256;
 constexpr int kGroupM = 8;                 // tile-band height of the raster order
 constexpr int LDS_BYTES = 65536;           // epilogue staging: 4 waves x 32 x 128 FP32
 
+// Rows of A rounded up to whole 32-row groups, and the workspace that holds A
+// in the tile layout.
+__host__ __device__ inline int64_t padded_rows(int64_t M) { return (M + 31) / 32 * 32; }
+
+// A [M][K/2] codes + [M][K/16] scales -> the tile layout of the prepared weight
+// for padded_rows(M) rows (rows >= M are zero). A plain byte permutation: the
+// GEMM applies each scale by a multiply, so signed, zero and NaN scales need no
+// folding. Thread = one 16-byte code unit (tile t = g * K/64 + c, unit 32h + r:
+// row 32g + r, chunk bytes [16h, 16h + 16)); the h = 0 thread also moves the
+// row's scale word of the chunk. Writes are contiguous per wave.
+__global__ __launch_bounds__(256) void tile_a_kernel(const uint8_t *__restrict__ a_codes,
+                                                     const uint8_t *__restrict__ a_scales, int64_t M, int64_t K,
+                                                     uint8_t *__restrict__ at) {
+  const int64_t kt = K / 64;
+  const int64_t Mp = padded_rows(M);
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tile = u >> 6;
+  if (tile >= Mp / 32 * kt) return;
+  const int unit = (int)(u & 63), h = unit >> 5, r = unit & 31;
+  const int64_t g = tile / kt, c = tile - g * kt;
+  const int64_t row = g * 32 + r;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  uint32_t sc = 0u;
+  if (row < M) {
+    v = *reinterpret_cast<const u32x4_t *>(a_codes + row * (K / 2) + c * 32 + h * 16);
+    if (h == 0) sc = *reinterpret_cast<const uint32_t *>(a_scales + row * (K / 16) + c * 4);
+  }
+  *reinterpret_cast<u32x4_t *>(at + tile * 1024 + unit * 16) = v;
+  if (h == 0) *reinterpret_cast<uint32_t *>(at + Mp * (K / 2) + tile * 128 + r * 4) = sc;
+}
+
 struct Params {
-  const uint8_t *a_codes;   // [M][K/2]
-  const uint8_t *a_scales;  // [M][K/16]
+  const uint8_t *a_tiled;   // A in the tile layout, padded_rows(M) rows
   const uint8_t *w_prep;    // prepared (N, K)
   void *d;
   int64_t M, N, K, ldd;
@@ -75,15 +106,38 @@ struct TileRsrc {
 // Packed fragments of one chunk for this wave.
 struct ChunkFrags {
   u32x4_t a[4], w[4];      // 32 codes of one row per lane (dword s feeds MFMA step s)
-  half2_t as[4], ws[4];    // the lane's two block scales (blocks 2h, 2h+1) in FP16
+  uint32_t as[4], ws[4];   // the row's four block scales of the chunk (raw E4M3 bytes)
 };
 
+// The lane's two block scales of a chunk (blocks 2h, 2h+1) in FP16. Converted
+// when the chunk's first step is unpacked, not when its loads are issued, so
+// the wait for the scale loads comes a whole chunk after they were issued.
+// Element 2i + b holds group i's scale of block 2h + b. Plain vectors, not
+// arrays, so the values stay in registers.
+struct ChunkScales {
+  half8_t a, w;
+};
+
+__device__ __forceinline__ void convert_scales(const ChunkFrags &f, ChunkScales &sc) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const half2_t xa = e4m3x2_to_f16(f.as[i] >> (16 * h));
+    const half2_t xw = e4m3x2_to_f16(f.ws[i] >> (16 * h));
+    sc.a[2 * i] = xa[0];
+    sc.a[2 * i + 1] = xa[1];
+    sc.w[2 * i] = xw[0];
+    sc.w[2 * i + 1] = xw[1];
+  }
+}
+
 // Exact FP16 operands of MFMA step s (k = 32h + 8s + 0..7) of a chunk.
-__device__ __forceinline__ void unpack_step(const ChunkFrags &f, int s, half8_t a[4], half8_t b[4]) {
+__device__ __forceinline__ void unpack_step(const ChunkFrags &f, const ChunkScales &sc, int s, half8_t a[4],
+                                            half8_t b[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) a[i] = dequant8_f16(f.a[i][s], f.as[i][s >> 1]);
+  for (int i = 0; i < 4; i++) a[i] = dequant8_f16(f.a[i][s], sc.a[2 * i + (s >> 1)]);
 #pragma unroll
-  for (int j = 0; j < 4; j++) b[j] = dequant8_f16(f.w[j][s], f.ws[j][s >> 1]);
+  for (int j = 0; j < 4; j++) b[j] = dequant8_f16(f.w[j][s], sc.w[2 * j + (s >> 1)]);
 }
 
 __device__ __forceinline__ void mfma_step(const half8_t a[4], const half8_t b[4], f32x16_t acc[4][4]) {
@@ -93,9 +147,9 @@ __device__ __forceinline__ void mfma_step(const half8_t a[4], const half8_t b[4]
     for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// Per-lane constant byte offsets (relative to the tile) of this wave's loads:
-// A rows wm*128 + 32i + r at half h, A scale words of those rows, and W tile
-// units `lane` / W scale words of row r for column groups wn*4 + i.
+// Per-lane constant byte offsets (relative to the tile bases) of this wave's
+// loads: tile unit `lane` and scale word of row r, for A row groups wm*4 + i
+// and W column groups wn*4 + i.
 struct WaveOff {
   uint32_t a[4], as[4], w[4], ws[4];
 };
@@ -104,39 +158,41 @@ struct WaveOff {
 // or 32-row group (W); chunks at or past nch read as zeros (length 0).
 __device__ __forceinline__ void load_frags(const TileRsrc &tr, const WaveOff &o, int64_t c, int64_t nch,
                                            ChunkFrags &f) {
-  const int h = (threadIdx.x & 63) >> 5;
   const bool in = c < nch;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(tr.a, in ? tr.a_bytes : 0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(tr.w, in ? tr.w_bytes : 0);
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(tr.as, in ? tr.as_bytes : 0);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(tr.ws, in ? tr.ws_bytes : 0);
-  const int sa = (int)(c * 32), sw = (int)(c * 1024), ssa = (int)(c * 4), ssw = (int)(c * 128);
+  const int sw = (int)(c * 1024), ssw = (int)(c * 128);   // chunk c: next code tile, next scale tile
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    f.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, o.a[i], sa, 0);
+    f.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, o.a[i], sw, 0);
     f.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, o.w[i], sw, 0);
   }
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint32_t xa = __builtin_amdgcn_raw_buffer_load_b32(ras, o.as[i], ssa, 0);
-    const uint32_t xw = __builtin_amdgcn_raw_buffer_load_b32(rws, o.ws[i], ssw, 0);
-    f.as[i] = e4m3x2_to_f16(xa >> (16 * h));
-    f.ws[i] = e4m3x2_to_f16(xw >> (16 * h));
+    f.as[i] = __builtin_amdgcn_raw_buffer_load_b32(ras, o.as[i], ssw, 0);
+    f.ws[i] = __builtin_amdgcn_raw_buffer_load_b32(rws, o.ws[i], ssw, 0);
   }
 }
 
 // One chunk of the main loop. f[P] holds chunk c, f[(P+1)%3] chunk c + 1 (in
 // flight or arrived); chunk c + 2 is requested into f[(P+2)%3]. On entry (a, b)
-// are chunk c's step-0 operands; on exit chunk c + 1's.
+// are chunk c's step-0 operands and sc its scales; on exit chunk c + 1's.
 template <int P>
 __device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff &o, int64_t c, int64_t nch,
-                                             ChunkFrags f[3], half8_t a[4], half8_t b[4], f32x16_t acc[4][4]) {
+                                             ChunkFrags f[3], ChunkScales &sc, half8_t a[4], half8_t b[4],
+                                             f32x16_t acc[4][4]) {
   load_frags(tr, o, c + 2, nch, f[(P + 2) % 3]);
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     half8_t an[4], bn[4];
-    if (s < 3) unpack_step(f[P], s + 1, an, bn);
-    else unpack_step(f[(P + 1) % 3], 0, an, bn);
+    if (s < 3) {
+      unpack_step(f[P], sc, s + 1, an, bn);
+    } else {
+      convert_scales(f[(P + 1) % 3], sc);
+      unpack_step(f[(P + 1) % 3], sc, 0, an, bn);
+    }
     mfma_step(a, b, acc);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -230,15 +286,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
   if ((G & 7) == 0) pid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const float alpha = load_alpha(p.alpha, p.alpha_dev);
   const int64_t nch = p.K / 64;
-  const int64_t kb = p.K / 2, sb = p.K / 16, kt = p.K / 64;
+  const int64_t kt = p.K / 64;
 
   const int lane = t & 63, h = lane >> 5, r = lane & 31;
   WaveOff o;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const int64_t row = wm * 128 + i * 32 + r;
-    o.a[i] = (uint32_t)(row * kb + h * 16);
-    o.as[i] = (uint32_t)(row * sb);
+    o.a[i] = (uint32_t)(((wm * 4 + i) * kt) * 1024 + lane * 16);
+    o.as[i] = (uint32_t)(((wm * 4 + i) * kt) * 128 + r * 4);
     o.w[i] = (uint32_t)(((wn * 4 + i) * kt) * 1024 + lane * 16);
     o.ws[i] = (uint32_t)(((wn * 4 + i) * kt) * 128 + r * 4);
   }
@@ -248,10 +303,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     TileRsrc tr;
-    tr.a = p.a_codes + m0 * kb;
-    tr.a_bytes = (p.M - m0) * kb;
-    tr.as = p.a_scales + m0 * sb;
-    tr.as_bytes = (p.M - m0) * sb;
+    const int64_t Mp = padded_rows(p.M);
+    tr.a = p.a_tiled + (m0 >> 5) * kt * 1024;
+    tr.a_bytes = (Mp - m0) / 32 * kt * 1024;
+    tr.as = p.a_tiled + Mp * p.K / 2 + (m0 >> 5) * kt * 128;
+    tr.as_bytes = (Mp - m0) / 32 * kt * 128;
     tr.w = p.w_prep + (n0 >> 5) * kt * 1024;
     tr.w_bytes = (p.N - n0) / 32 * kt * 1024;
     tr.ws = p.w_prep + p.N * p.K / 2 + (n0 >> 5) * kt * 128;
@@ -263,14 +319,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 4; j++) acc[i][j] = f32x16_t{};
     ChunkFrags f[3];
+    ChunkScales sc;
     half8_t a[4], b[4];
     load_frags(tr, o, 0, nch, f[0]);
     load_frags(tr, o, 1, nch, f[1]);
-    unpack_step(f[0], 0, a, b);
+    convert_scales(f[0], sc);
+    unpack_step(f[0], sc, 0, a, b);
     for (int64_t c = 0; c < nch; c += 3) {
-      chunk_direct<0>(tr, o, c, nch, f, a, b, acc);
-      chunk_direct<1>(tr, o, c + 1, nch, f, a, b, acc);
-      chunk_direct<2>(tr, o, c + 2, nch, f, a, b, acc);
+      chunk_direct<0>(tr, o, c, nch, f, sc, a, b, acc);
+      chunk_direct<1>(tr, o, c + 1, nch, f, sc, a, b, acc);
+      chunk_direct<2>(tr, o, c + 2, nch, f, sc, a, b, acc);
     }
     __syncthreads();
     epilogue<OUT_BF16>(smem, p, m0, n0, wm, wn, alpha, acc);
@@ -282,12 +340,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
 
 using namespace nvfp4;
 
+size_t nvfp4::w4a4_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 64 != 0) return 0;
+  return (size_t)(w4a4::padded_rows(M) * K / 2 + w4a4::padded_rows(M) * K / 16);
+}
+
 extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
                                         int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
                                         void *d, int out_dtype, int64_t ldd, void *ws, size_t ws_bytes,
                                         void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0 || ldd < N) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
@@ -297,22 +358,30 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a
   if (!aligned(a_codes, 16) || !aligned(a_scales, 4) || !aligned(w_prep, 16) || !aligned(d, esz) ||
       (alpha_dev && !aligned(alpha_dev, 4)))
     return NVFP4_ERR_ALIGN;
-  // 32-bit buffer offsets inside one 256-row tile of A and one 256-column tile of W
-  if ((int64_t)w4a4::BM * (K / 2) > 0xFFFFFFFFll || (int64_t)(w4a4::BN / 32) * (K / 64) * 1024 > 0xFFFFFFFFll)
-    return NVFP4_ERR_SHAPE;
+  // 32-bit buffer offsets inside the code tiles of one 256-row (256-column) tile
+  if ((int64_t)(w4a4::BM / 32) * (K / 64) * 1024 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
   const int64_t tiles_m = (M + w4a4::BM - 1) / w4a4::BM;
   const int64_t tiles_n = (N + w4a4::BN - 1) / w4a4::BN;
   if (tiles_m * tiles_n > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
+  const size_t need = w4a4_workspace_bytes(M, K);
+  if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
   DeviceInfo di;
   nvfp4_status st = device_info(&di);
   if (st != NVFP4_OK) return st;
-  w4a4::Params p{a_codes, a_scales, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tiles_m, (int)tiles_n};
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *at = static_cast<uint8_t *>(ws);
+  const int64_t units = w4a4::padded_rows(M) / 32 * (K / 64) * 64;
+  hipLaunchKernelGGL(w4a4::tile_a_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, a_codes, a_scales,
+                     M, K, at);
+  NVFP4_LAUNCH_CHECK();
+  w4a4::Params p{at, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tiles_m, (int)tiles_n};
   const int64_t total = tiles_m * tiles_n;
   const int grid = (int)(total < di.num_cus ? total : di.num_cus);
   if (out_dtype == NVFP4_OUT_BF16)
-    hipLaunchKernelGGL(w4a4::gemm_kernel<true>, dim3(grid), dim3(w4a4::kThreads), 0, (hipStream_t)stream, p);
+    hipLaunchKernelGGL(w4a4::gemm_kernel<true>, dim3(grid), dim3(w4a4::kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(w4a4::gemm_kernel<false>, dim3(grid), dim3(w4a4::kThreads), 0, (hipStream_t)stream, p);
+    hipLaunchKernelGGL(w4a4::gemm_kernel<false>, dim3(grid), dim3(w4a4::kThreads), 0, s, p);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }

@@ -48,12 +48,14 @@ ODD = ctypes.c_void_p(0x10001)
 
 def test_gemm_w4a4_argument_checks():
     f = nv.lib().nvfp4_gemm_w4a4
-    ok = dict(a=FAKE, s=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ad=None, d=FAKE, dt=nv.OUT_BF16, ldd=64)
+    need = nv.lib().nvfp4_workspace_bytes(nv.OP_W4A4, 64, 64, 128)
+    ok = dict(a=FAKE, s=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ad=None, d=FAKE, dt=nv.OUT_BF16, ldd=64,
+              ws=None, nws=0)
 
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["a"], a["s"], a["w"], a["M"], a["N"], a["K"], a["alpha"], a["ad"], a["d"], a["dt"], a["ldd"],
-                 None, 0, None)
+                 a["ws"], a["nws"], None)
     assert call(dt=7) == nv.ERR_DTYPE
     assert call(K=96) == nv.ERR_SHAPE
     assert call(N=48) == nv.ERR_SHAPE
@@ -66,6 +68,9 @@ def test_gemm_w4a4_argument_checks():
     assert call(alpha=float("inf")) == nv.ERR_VALUE
     assert call(a=ODD) == nv.ERR_ALIGN
     assert call(w=ODD) == nv.ERR_ALIGN
+    assert call() == nv.ERR_WORKSPACE             # A is re-tiled into the workspace
+    assert call(ws=FAKE, nws=need - 1) == nv.ERR_WORKSPACE
+    assert call(ws=ODD, nws=need) == nv.ERR_ALIGN
 
 
 def test_gemm_w4a16_argument_checks():
@@ -101,7 +106,10 @@ def test_prepare_and_quantize_argument_checks():
 
 def test_workspace_sizes():
     L = nv.lib()
-    assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 8192, 8192, 8192) == 0
+    # W4A4: A in the prepared tile layout, rows rounded up to 32
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 8192, 8192, 8192) == 8192 * 8192 * 9 // 16
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 33, 64, 128) == 64 * 128 * 9 // 16
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 0, 64, 128) == 0
     assert L.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 0, 5120) >= 4
     assert L.nvfp4_workspace_bytes(7, 1, 1, 1) == 0
     assert L.nvfp4_workspace_init(None, 0, None) == nv.OK
