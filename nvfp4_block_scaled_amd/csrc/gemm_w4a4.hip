@@ -25,8 +25,8 @@
 //    that use each fragment -- measured no faster.)
 //  * The FP16 operands exist only in registers: cvt_scalef32_pk_f16_fp4 (code
 //    pairs, scale operand 1.0) + v_pk_mul_f16 by the block scale, one vector
-//    instruction per element, unpacked one MFMA step ahead and interleaved one
-//    MFMA to four vector instructions.
+//    instruction per element, unpacked one MFMA step ahead and interleaved with
+//    the current step's MFMAs (one scheduling region per step).
 //  * Persistent grid (one workgroup per CU) walking the tiles in an XCD-aware,
 //    grouped order: workgroups that run on the same XCD (hardware ids congruent
 //    mod 8) take consecutive tile indices, and consecutive indices cover a
@@ -179,6 +179,12 @@ __device__ __forceinline__ void load_frags(const TileRsrc &tr, const WaveOff &o,
 // One chunk of the main loop. f[P] holds chunk c, f[(P+1)%3] chunk c + 1 (in
 // flight or arrived); chunk c + 2 is requested into f[(P+2)%3]. On entry (a, b)
 // are chunk c's step-0 operands and sc its scales; on exit chunk c + 1's.
+//
+// Each MFMA step is its own scheduling region (16 MFMAs, each followed by up
+// to five vector instructions of the next step's unpack). Without the region
+// boundaries the scheduler mixes MFMAs of consecutive steps and issues MFMAs
+// on the same accumulator back to back, which stalls each for the previous
+// one's full latency (measured 42 against 36 cycles per MFMA).
 template <int P>
 __device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff &o, int64_t c, int64_t nch,
                                              ChunkFrags f[3], ChunkScales &sc, half8_t a[4], half8_t b[4],
@@ -199,14 +205,14 @@ __device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff &
       a[i] = an[i];
       b[i] = bn[i];
     }
-  }
-  __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);   // the chunk's loads first
 #pragma unroll
-  for (int k = 0; k < 64; k++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    for (int k = 0; k < 16; k++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Epilogue through LDS: each wave writes a 32 x 128 block of alpha * acc to its
