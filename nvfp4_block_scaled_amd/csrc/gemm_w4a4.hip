@@ -44,10 +44,8 @@
 namespace nvfp4 {
 namespace w4a4 {
 
-constexpr int BM = 256, BN = 256;
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;                 // tile-band height of the raster order
-constexpr int LDS_BYTES = 65536;           // epilogue staging: 4 waves x 32 x 128 FP32
 
 // Rows of A rounded up to whole 32-row groups, and the workspace that holds A
 // in the tile layout.
@@ -103,10 +101,12 @@ struct TileRsrc {
   int64_t a_bytes, as_bytes, w_bytes, ws_bytes;
 };
 
-// Packed fragments of one chunk for this wave.
+// Packed fragments of one chunk for this wave: T A row groups and T W column
+// groups (T = MFMA tiles per wave and dimension).
+template <int T>
 struct ChunkFrags {
-  u32x4_t a[4], w[4];      // 32 codes of one row per lane (dword s feeds MFMA step s)
-  uint32_t as[4], ws[4];   // the row's four block scales of the chunk (raw E4M3 bytes)
+  u32x4_t a[T], w[T];      // 32 codes of one row per lane (dword s feeds MFMA step s)
+  uint32_t as[T], ws[T];   // the row's four block scales of the chunk (raw E4M3 bytes)
 };
 
 // The lane's two block scales of a chunk (blocks 2h, 2h+1) in FP16. Converted
@@ -118,10 +118,11 @@ struct ChunkScales {
   half8_t a, w;
 };
 
-__device__ __forceinline__ void convert_scales(const ChunkFrags &f, ChunkScales &sc) {
+template <int T>
+__device__ __forceinline__ void convert_scales(const ChunkFrags<T> &f, ChunkScales &sc) {
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < T; i++) {
     const half2_t xa = e4m3x2_to_f16(f.as[i] >> (16 * h));
     const half2_t xw = e4m3x2_to_f16(f.ws[i] >> (16 * h));
     sc.a[2 * i] = xa[0];
@@ -132,32 +133,36 @@ __device__ __forceinline__ void convert_scales(const ChunkFrags &f, ChunkScales 
 }
 
 // Exact FP16 operands of MFMA step s (k = 32h + 8s + 0..7) of a chunk.
-__device__ __forceinline__ void unpack_step(const ChunkFrags &f, const ChunkScales &sc, int s, half8_t a[4],
-                                            half8_t b[4]) {
+template <int T>
+__device__ __forceinline__ void unpack_step(const ChunkFrags<T> &f, const ChunkScales &sc, int s, half8_t a[T],
+                                            half8_t b[T]) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) a[i] = dequant8_f16(f.a[i][s], sc.a[2 * i + (s >> 1)]);
+  for (int i = 0; i < T; i++) a[i] = dequant8_f16(f.a[i][s], sc.a[2 * i + (s >> 1)]);
 #pragma unroll
-  for (int j = 0; j < 4; j++) b[j] = dequant8_f16(f.w[j][s], sc.w[2 * j + (s >> 1)]);
+  for (int j = 0; j < T; j++) b[j] = dequant8_f16(f.w[j][s], sc.w[2 * j + (s >> 1)]);
 }
 
-__device__ __forceinline__ void mfma_step(const half8_t a[4], const half8_t b[4], f32x16_t acc[4][4]) {
+template <int T>
+__device__ __forceinline__ void mfma_step(const half8_t a[T], const half8_t b[T], f32x16_t acc[T][T]) {
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < T; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < T; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
 // Per-lane constant byte offsets (relative to the tile bases) of this wave's
-// loads: tile unit `lane` and scale word of row r, for A row groups wm*4 + i
-// and W column groups wn*4 + i.
+// loads: tile unit `lane` and scale word of row r, for A row groups wm*T + i
+// and W column groups wn*T + i.
+template <int T>
 struct WaveOff {
-  uint32_t a[4], as[4], w[4], ws[4];
+  uint32_t a[T], as[T], w[T], ws[T];
 };
 
 // Loads of chunk c: the rebased resources keep the range check on the row (A)
 // or 32-row group (W); chunks at or past nch read as zeros (length 0).
-__device__ __forceinline__ void load_frags(const TileRsrc &tr, const WaveOff &o, int64_t c, int64_t nch,
-                                           ChunkFrags &f) {
+template <int T>
+__device__ __forceinline__ void load_frags(const TileRsrc &tr, const WaveOff<T> &o, int64_t c, int64_t nch,
+                                           ChunkFrags<T> &f) {
   const bool in = c < nch;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(tr.a, in ? tr.a_bytes : 0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(tr.w, in ? tr.w_bytes : 0);
@@ -165,12 +170,12 @@ __device__ __forceinline__ void load_frags(const TileRsrc &tr, const WaveOff &o,
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(tr.ws, in ? tr.ws_bytes : 0);
   const int sw = (int)(c * 1024), ssw = (int)(c * 128);   // chunk c: next code tile, next scale tile
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < T; i++) {
     f.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, o.a[i], sw, 0);
     f.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, o.w[i], sw, 0);
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < T; i++) {
     f.as[i] = __builtin_amdgcn_raw_buffer_load_b32(ras, o.as[i], ssw, 0);
     f.ws[i] = __builtin_amdgcn_raw_buffer_load_b32(rws, o.ws[i], ssw, 0);
   }
@@ -180,58 +185,60 @@ __device__ __forceinline__ void load_frags(const TileRsrc &tr, const WaveOff &o,
 // flight or arrived); chunk c + 2 is requested into f[(P+2)%3]. On entry (a, b)
 // are chunk c's step-0 operands and sc its scales; on exit chunk c + 1's.
 //
-// Each MFMA step is its own scheduling region (16 MFMAs, each followed by up
-// to five vector instructions of the next step's unpack). Without the region
-// boundaries the scheduler mixes MFMAs of consecutive steps and issues MFMAs
-// on the same accumulator back to back, which stalls each for the previous
-// one's full latency (measured 42 against 36 cycles per MFMA).
-template <int P>
-__device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff &o, int64_t c, int64_t nch,
-                                             ChunkFrags f[3], ChunkScales &sc, half8_t a[4], half8_t b[4],
-                                             f32x16_t acc[4][4]) {
-  load_frags(tr, o, c + 2, nch, f[(P + 2) % 3]);
+// Each MFMA step is its own scheduling region (T*T MFMAs, each followed by its
+// share of the next step's unpack: 16/T vector instructions, at most five for
+// T = 4). Without the region boundaries the scheduler mixes MFMAs of
+// consecutive steps and issues MFMAs on the same accumulator back to back,
+// which stalls each for the previous one's full latency (measured 42 against
+// 36 cycles per MFMA at T = 4).
+template <int P, int T>
+__device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff<T> &o, int64_t c, int64_t nch,
+                                             ChunkFrags<T> f[3], ChunkScales &sc, half8_t a[T], half8_t b[T],
+                                             f32x16_t acc[T][T]) {
+  constexpr int kValuPerMfma = 16 / T + (T == 4 ? 1 : 0);
+  load_frags<T>(tr, o, c + 2, nch, f[(P + 2) % 3]);
 #pragma unroll
   for (int s = 0; s < 4; s++) {
-    half8_t an[4], bn[4];
+    half8_t an[T], bn[T];
     if (s < 3) {
-      unpack_step(f[P], sc, s + 1, an, bn);
+      unpack_step<T>(f[P], sc, s + 1, an, bn);
     } else {
-      convert_scales(f[(P + 1) % 3], sc);
-      unpack_step(f[(P + 1) % 3], sc, 0, an, bn);
+      convert_scales<T>(f[(P + 1) % 3], sc);
+      unpack_step<T>(f[(P + 1) % 3], sc, 0, an, bn);
     }
-    mfma_step(a, b, acc);
+    mfma_step<T>(a, b, acc);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < T; i++) {
       a[i] = an[i];
       b[i] = bn[i];
     }
-    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);   // the chunk's loads first
+    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 4 * T, 0);   // the chunk's loads first
 #pragma unroll
-    for (int k = 0; k < 16; k++) {
+    for (int k = 0; k < T * T; k++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Epilogue through LDS: each wave writes a 32 x 128 block of alpha * acc to its
+// Epilogue through LDS: each wave writes a 32 x 32T block of alpha * acc to its
 // own LDS region in row-major order, then writes it out as 16-byte row pieces.
-template <bool OUT_BF16>
+template <bool OUT_BF16, int T>
 __device__ __forceinline__ void epilogue(uint8_t *smem, const Params &p, int64_t m0, int64_t n0, int wm, int wn,
-                                         float alpha, f32x16_t acc[4][4]) {
+                                         float alpha, f32x16_t acc[T][T]) {
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
-  constexpr int ROW_BYTES = 128 * ESZ;            // one wave's 128 columns
+  constexpr int ROW_BYTES = 32 * T * ESZ;         // one wave's 32T columns
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, r = lane & 31;
-  uint8_t *reg = smem + wave * (32 * 128 * 4);
-  const int64_t col0 = n0 + wn * 128;
+  uint8_t *reg = smem + wave * (32 * 32 * T * 4);
+  const int64_t col0 = n0 + wn * 32 * T;
   const int64_t ncols = p.N - col0;               // columns of this wave still inside D
   const bool vec_ok = (p.ldd * ESZ) % 16 == 0 && ((uintptr_t)p.d & 15) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < T; i++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < T; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int row = 8 * (e >> 2) + 4 * h + (e & 3);
@@ -246,7 +253,7 @@ __device__ __forceinline__ void epilogue(uint8_t *smem, const Params &p, int64_t
 #pragma unroll
     for (int q = lane; q < 32 * PIECES; q += 64) {
       const int row = q / PIECES, pc = q % PIECES;
-      const int64_t m = m0 + wm * 128 + i * 32 + row;
+      const int64_t m = m0 + wm * 32 * T + i * 32 + row;
       const int64_t c = (int64_t)pc * (16 / ESZ);
       if (m < p.M && c < ncols) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t *>(reg + row * ROW_BYTES + pc * 16);
@@ -278,9 +285,13 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
   tn = w / rows;
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+// T = 4: 256 x 256 workgroup tiles, one workgroup per CU (all 512 registers of
+// a lane in use). T = 2: 128 x 128 tiles for problems with fewer 256 x 256
+// tiles than CUs, two workgroups per CU.
+template <bool OUT_BF16, int T>
+__global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p) {
+  constexpr int BT = 64 * T;                      // workgroup tile edge
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * 32 * 32 * T * 4];
   const int t = threadIdx.x;
   const int wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -294,20 +305,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
   const int64_t nch = p.K / 64;
   const int64_t kt = p.K / 64;
 
-  const int lane = t & 63, h = lane >> 5, r = lane & 31;
-  WaveOff o;
+  const int lane = t & 63, r = lane & 31;
+  WaveOff<T> o;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    o.a[i] = (uint32_t)(((wm * 4 + i) * kt) * 1024 + lane * 16);
-    o.as[i] = (uint32_t)(((wm * 4 + i) * kt) * 128 + r * 4);
-    o.w[i] = (uint32_t)(((wn * 4 + i) * kt) * 1024 + lane * 16);
-    o.ws[i] = (uint32_t)(((wn * 4 + i) * kt) * 128 + r * 4);
+  for (int i = 0; i < T; i++) {
+    o.a[i] = (uint32_t)(((wm * T + i) * kt) * 1024 + lane * 16);
+    o.as[i] = (uint32_t)(((wm * T + i) * kt) * 128 + r * 4);
+    o.w[i] = (uint32_t)(((wn * T + i) * kt) * 1024 + lane * 16);
+    o.ws[i] = (uint32_t)(((wn * T + i) * kt) * 128 + r * 4);
   }
 
   for (int tile = pid; tile < total; tile += G) {
     int tm, tn;
     tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t m0 = (int64_t)tm * BT, n0 = (int64_t)tn * BT;
     TileRsrc tr;
     const int64_t Mp = padded_rows(p.M);
     tr.a = p.a_tiled + (m0 >> 5) * kt * 1024;
@@ -319,25 +330,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     tr.ws = p.w_prep + p.N * p.K / 2 + (n0 >> 5) * kt * 128;
     tr.ws_bytes = (p.N - n0) / 32 * kt * 128;
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[T][T];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < T; i++)
 #pragma unroll
-      for (int j = 0; j < 4; j++) acc[i][j] = f32x16_t{};
-    ChunkFrags f[3];
+      for (int j = 0; j < T; j++) acc[i][j] = f32x16_t{};
+    ChunkFrags<T> f[3];
     ChunkScales sc;
-    half8_t a[4], b[4];
-    load_frags(tr, o, 0, nch, f[0]);
-    load_frags(tr, o, 1, nch, f[1]);
-    convert_scales(f[0], sc);
-    unpack_step(f[0], sc, 0, a, b);
+    half8_t a[T], b[T];
+    load_frags<T>(tr, o, 0, nch, f[0]);
+    load_frags<T>(tr, o, 1, nch, f[1]);
+    convert_scales<T>(f[0], sc);
+    unpack_step<T>(f[0], sc, 0, a, b);
     for (int64_t c = 0; c < nch; c += 3) {
-      chunk_direct<0>(tr, o, c, nch, f, sc, a, b, acc);
-      chunk_direct<1>(tr, o, c + 1, nch, f, sc, a, b, acc);
-      chunk_direct<2>(tr, o, c + 2, nch, f, sc, a, b, acc);
+      chunk_direct<0, T>(tr, o, c, nch, f, sc, a, b, acc);
+      chunk_direct<1, T>(tr, o, c + 1, nch, f, sc, a, b, acc);
+      chunk_direct<2, T>(tr, o, c + 2, nch, f, sc, a, b, acc);
     }
     __syncthreads();
-    epilogue<OUT_BF16>(smem, p, m0, n0, wm, wn, alpha, acc);
+    epilogue<OUT_BF16, T>(smem, p, m0, n0, wm, wn, alpha, acc);
   }
 }
 
@@ -365,16 +376,19 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a
       (alpha_dev && !aligned(alpha_dev, 4)))
     return NVFP4_ERR_ALIGN;
   // 32-bit buffer offsets inside the code tiles of one 256-row (256-column) tile
-  if ((int64_t)(w4a4::BM / 32) * (K / 64) * 1024 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
-  const int64_t tiles_m = (M + w4a4::BM - 1) / w4a4::BM;
-  const int64_t tiles_n = (N + w4a4::BN - 1) / w4a4::BN;
-  if (tiles_m * tiles_n > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
+  if ((int64_t)8 * (K / 64) * 1024 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
+  if ((M + 127) / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
   const size_t need = w4a4_workspace_bytes(M, K);
   if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
   DeviceInfo di;
   nvfp4_status st = device_info(&di);
   if (st != NVFP4_OK) return st;
+  // 256 x 256 tiles unless they cannot fill the CUs; then 128 x 128 tiles
+  const int T = ((M + 255) / 256) * ((N + 255) / 256) >= di.num_cus ? 4 : 2;
+  const int64_t bt = 64 * T;
+  const int64_t tiles_m = (M + bt - 1) / bt;
+  const int64_t tiles_n = (N + bt - 1) / bt;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *at = static_cast<uint8_t *>(ws);
   const int64_t units = w4a4::padded_rows(M) / 32 * (K / 64) * 64;
@@ -383,11 +397,19 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a
   NVFP4_LAUNCH_CHECK();
   w4a4::Params p{at, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tiles_m, (int)tiles_n};
   const int64_t total = tiles_m * tiles_n;
-  const int grid = (int)(total < di.num_cus ? total : di.num_cus);
-  if (out_dtype == NVFP4_OUT_BF16)
-    hipLaunchKernelGGL(w4a4::gemm_kernel<true>, dim3(grid), dim3(w4a4::kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(w4a4::gemm_kernel<false>, dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+  const int64_t slots = (int64_t)di.num_cus * (T == 4 ? 1 : 2);
+  const int grid = (int)(total < slots ? total : slots);
+  if (T == 4) {
+    if (out_dtype == NVFP4_OUT_BF16)
+      hipLaunchKernelGGL((w4a4::gemm_kernel<true, 4>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((w4a4::gemm_kernel<false, 4>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+  } else {
+    if (out_dtype == NVFP4_OUT_BF16)
+      hipLaunchKernelGGL((w4a4::gemm_kernel<true, 2>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((w4a4::gemm_kernel<false, 2>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+  }
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }
