@@ -1,6 +1,6 @@
 // W4A16 NVFP4 GEMM for gfx950: y = alpha * x (W.SFW)^T, x/y BF16, FP32 accumulation.
 //
-// Two kernels, chosen by M:
+// Kernels, chosen by M (and, for decode, by the number of 32-row groups):
 //  * M <= 4 (decode): a weight-streaming kernel on the vector ALUs. A 1024-thread
 //    workgroup owns 16 weight rows (half of a 32-row prepared tile group) over
 //    the whole K; its 16 waves take interleaved pairs of 64-wide K tiles. Each
@@ -11,7 +11,12 @@
 //    kernel is bound by HBM. The K-split is reduced inside the workgroup (lane
 //    butterflies, then LDS over the waves in wave order), so no workgroup ever
 //    waits on another and nothing crosses an XCD within the kernel. x is staged
-//    once per workgroup in LDS and read by broadcast.
+//    once per workgroup in LDS and read by broadcast. With at least two 32-row
+//    groups per CU, a wide variant is used instead: one 512-thread workgroup
+//    per whole group, each wave keeping eight 1 KB tile loads in flight (two
+//    batches of four); all its workgroups are resident at once. (A K split
+//    across workgroups would need an agent-scope release per workgroup, an L2
+//    write-back on this part, which measured several times slower.)
 //  * M > 4: an LDS-tiled MFMA kernel (v_mfma_f32_32x32x16_bf16). BF16 x tiles
 //    are staged through LDS (XOR-swizzled rows, conflict-free 16-byte reads);
 //    weight codes and scales are staged as packed bytes in the prepared tile
@@ -31,7 +36,7 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------- planning
 
 struct Plan {
-  int kind;          // 0 = vector decode kernel, 1 = MFMA tile kernel
+  int kind;          // 0 = vector decode kernel, 1 = MFMA tile kernel, 2 = wide vector decode kernel
   int splits;        // K splits of the tile kernel (1 = none)
   int64_t grid_x;    // workgroups along the output
 };
@@ -53,9 +58,11 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K) {
   const int cus = num_cus_or_default();
   const int64_t ktiles = K / 64;
   if (M <= kDecodeMaxM && M * K * 2 <= kDecodeLdsBytes) {
-    p.kind = 0;
+    // one 32-row group per workgroup once there are two groups per CU; below
+    // that, 16-row workgroups with 16 waves keep more of the chip busy
+    p.kind = N / 32 >= 2 * cus ? 2 : 0;
     p.splits = 1;
-    p.grid_x = N / 16;
+    p.grid_x = p.kind == 2 ? N / 32 : N / 16;
   } else {
     p.kind = 1;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -165,6 +172,112 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const uint16_t *
     for (int w = 1; w < kDecodeWaves; w++) v += red[w][m][rr];
     const float al = load_alpha(alpha, alpha_dev);
     y[m * ldy + blockIdx.x * 16 + rr] = f32_to_bf16_rne(al * v);
+  }
+}
+
+// Wide decode (many row groups): workgroup g covers the 32-row prepared tile
+// group g (rows 32g .. 32g+31) over the whole K with 8 waves; wave w takes the
+// tiles w, w + 8, w + 16, ...; lane l is unit l of each tile (row r = l & 31,
+// k in [32h, 32h + 32) with h = l >> 5), so one wave load is the tile's
+// contiguous 1 KB. Loads run four tiles per wave ahead in a two-batch register
+// ring (non-temporal: the weights are streamed once); the first batch is issued
+// before x is staged. With at least two groups per CU every workgroup is
+// resident at once, and a group is reduced inside its workgroup.
+constexpr int kWideWaves = 8;
+constexpr int kWideAhead = 4;
+
+template <int M>
+__global__ __launch_bounds__(kWideWaves * 64) void decode_wide_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                                    const uint8_t *__restrict__ wp, int64_t N,
+                                                                    int64_t K, float alpha, const float *alpha_dev,
+                                                                    uint16_t *__restrict__ y, int64_t ldy) {
+  constexpr int W = kWideWaves, U = kWideAhead;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];     // [M][K]
+  __shared__ float red[W][M][32];
+  const int64_t T = K / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = lane >> 5, r = lane & 31;
+  const int64_t g = blockIdx.x;
+  const uint8_t *cb = wp + ((g * T) << 10) + lane * 16;
+  const uint8_t *sb = wp + N * K / 2 + ((g * T) << 7) + r * 4;
+  u32x4_t cw0[U], cw1[U];
+  uint32_t sw0[U], sw1[U];
+  auto issue = [&](u32x4_t (&cw)[U], uint32_t (&sw)[U], int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+      const int64_t t = t0 + (int64_t)i * W;
+      if (t < T) {
+        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cb + (t << 10)));
+        sw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + (t << 7)));
+      } else {
+        cw[i] = u32x4_t{0u, 0u, 0u, 0u};
+        sw[i] = 0u;
+      }
+    }
+  };
+  issue(cw0, sw0, wave);
+  for (int64_t u = threadIdx.x; u < M * K / 8; u += W * 64) {
+    const int64_t m = u / (K / 8), c = u - m * (K / 8);
+    *reinterpret_cast<u32x4_t *>(xs + m * K + c * 8) = *reinterpret_cast<const u32x4_t *>(x + m * ldx + c * 8);
+  }
+  __syncthreads();
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; m++) acc[m] = 0.0f;
+  auto compute = [&](const u32x4_t (&cw)[U], const uint32_t (&sw)[U], int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+      const int64_t t = t0 + (int64_t)i * W;
+      if (t < T) {
+        const f32x2_t sc = e4m3x2_to_f32(sw[i] >> (16 * h));
+        const uint16_t *xk = xs + t * 64 + 32 * h;
+#pragma unroll
+        for (int blk = 0; blk < 2; blk++) {
+          float part[M];
+#pragma unroll
+          for (int m = 0; m < M; m++) part[m] = 0.0f;
+#pragma unroll
+          for (int d = 0; d < 2; d++) {
+            const int s = blk * 2 + d;
+            bf16x2_t wv[4];
+            codes8_to_bf16(cw[i][s], wv);
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+              const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xk + m * K + 8 * s);
+#pragma unroll
+              for (int e = 0; e < 4; e++)
+                part[m] = __builtin_amdgcn_fdot2_f32_bf16(wv[e], as_bf16x2(xv[e]), part[m], false);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < M; m++) acc[m] = __builtin_fmaf(part[m], sc[blk], acc[m]);
+        }
+      }
+    }
+  };
+  const int64_t step = (int64_t)W * U;
+  for (int64_t t0 = wave; t0 < T; t0 += 2 * step) {
+    issue(cw1, sw1, t0 + step);
+    compute(cw0, sw0, t0);
+    if (t0 + step >= T) break;
+    issue(cw0, sw0, t0 + 2 * step);
+    compute(cw1, sw1, t0 + step);
+  }
+  // lanes r and r + 32 hold the two K-halves of row r: the same sum in both
+#pragma unroll
+  for (int m = 0; m < M; m++) acc[m] += __shfl_xor(acc[m], 32, 64);
+  if (h == 0)
+#pragma unroll
+    for (int m = 0; m < M; m++) red[wave][m][r] = acc[m];
+  __syncthreads();
+  if (threadIdx.x < M * 32) {
+    const int m = threadIdx.x >> 5, rr = threadIdx.x & 31;
+    float v = red[0][m][rr];
+#pragma unroll
+    for (int w = 1; w < W; w++) v += red[w][m][rr];
+    const float al = load_alpha(alpha, alpha_dev);
+    y[m * ldy + g * 32 + rr] = f32_to_bf16_rne(al * v);
   }
 }
 
@@ -361,7 +474,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (plan.kind == 0) {
+  if (plan.kind == 0 || plan.kind == 2) {
     if (plan.grid_x > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
     const size_t lds = (size_t)(M * K * 2);
 #define NVFP4_DECODE_CASE(MM)                                                                                 \
@@ -369,14 +482,30 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     hipLaunchKernelGGL(w4a16::decode_kernel<MM>, dim3((unsigned)plan.grid_x), dim3(w4a16::kDecodeThreads), lds, \
                        s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy);                                    \
     break;
-    switch ((int)M) {
-      NVFP4_DECODE_CASE(1)
-      NVFP4_DECODE_CASE(2)
-      NVFP4_DECODE_CASE(3)
-      NVFP4_DECODE_CASE(4)
-      default: return NVFP4_ERR_SHAPE;
+#define NVFP4_DECODE_WIDE_CASE(MM)                                                                            \
+  case MM:                                                                                                    \
+    hipLaunchKernelGGL(w4a16::decode_wide_kernel<MM>, dim3((unsigned)plan.grid_x),                            \
+                       dim3(w4a16::kWideWaves * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy); \
+    break;
+    if (plan.kind == 2) {
+      switch ((int)M) {
+        NVFP4_DECODE_WIDE_CASE(1)
+        NVFP4_DECODE_WIDE_CASE(2)
+        NVFP4_DECODE_WIDE_CASE(3)
+        NVFP4_DECODE_WIDE_CASE(4)
+        default: return NVFP4_ERR_SHAPE;
+      }
+    } else {
+      switch ((int)M) {
+        NVFP4_DECODE_CASE(1)
+        NVFP4_DECODE_CASE(2)
+        NVFP4_DECODE_CASE(3)
+        NVFP4_DECODE_CASE(4)
+        default: return NVFP4_ERR_SHAPE;
+      }
     }
 #undef NVFP4_DECODE_CASE
+#undef NVFP4_DECODE_WIDE_CASE
   } else {
     const int64_t tiles_n = (N + w4a16::BN - 1) / w4a16::BN;
     if (plan.grid_x > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;

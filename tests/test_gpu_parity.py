@@ -235,6 +235,18 @@ def test_w4a16_small_shapes(M, N, K):
     assert_close(host(out), y, S, bf16=True, what=f"w4a16 M={M} {N}x{K}")
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("N,K", [(16384, 256), (16416, 1088)])
+def test_w4a16_wide_decode(M, N, K):
+    """Many 32-row groups (>= 2 per CU): the one-group-per-workgroup decode path,
+    including a K that leaves the last tile batch partly empty; full check."""
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 7 + N)
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
+    torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"wide decode M={M} {N}x{K}")
+
+
 @pytest.mark.parametrize("j", range(4))
 @pytest.mark.parametrize("mi", range(5))
 def test_w4a16_decode_shapes(j, mi):
