@@ -13,7 +13,8 @@ idle run up to 10 % slower while the clock ramps.
 Extra figures in the same JSON line: W4A16 decode (M = 1) achieved HBM GB/s on
 the 27B-class layer shapes with weights rotated over >= 1 GiB (CUDA-graph
 replay), the prefill W4A4 with on-device activation quantization, and the
-other square sizes. `roofline` describes the dominant kernel (the W4A4 GEMM);
+other square sizes. `roofline` describes the dominant kernel, the W4A4 GEMM
+kernel, timed alone (nvfp4_gemm_w4a4_tiled on an A tiled beforehand);
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-extras] [--no-cpu-baseline]
@@ -74,7 +75,7 @@ def quantized_square(nv, S, operand, gen):
     return codes, scales, g, inv_g
 
 
-def w4a4_square(nv, S, steps, warmup, gen=None):
+def w4a4_square(nv, S, steps, warmup, gen=None, kernel_only=False):
     import numpy as np
     import torch
     import synth
@@ -87,7 +88,12 @@ def w4a4_square(nv, S, steps, warmup, gen=None):
     out = torch.empty((S, S), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(nv.workspace_bytes(nv.OP_W4A4, S, S, S), dtype=torch.uint8, device="cuda")
     ms = time_calls(lambda: nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, alpha, None, "bf16", out, ws), steps, warmup)
-    return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12
+    if not kernel_only:
+        return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12
+    # the GEMM kernel alone, on A already tiled (the call above = tile copy + this)
+    at = nv.nvfp4_tile_activation(ca, sa)
+    ms_k = time_calls(lambda: nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, alpha, None, "bf16", out), steps, warmup)
+    return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12, ms_k
 
 
 def w4a16_m1(nv, j, reps=3):
@@ -135,6 +141,44 @@ def w4a16_m1(nv, j, reps=3):
                 GBps=round(all_bytes / (best * 1e-3) / 1e9, 1),
                 weight_GBps=round(weight_bytes / (best * 1e-3) / 1e9, 1),
                 hbm_frac=round(all_bytes / (best * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+
+
+def w4a16_m_sweep(nv, j, steps, warmup):
+    """W4A16 on layer shape j at the batch sizes M > 1 of the decode workload (weights
+    rotated over >= 1 GiB so every call streams them from HBM)."""
+    import numpy as np
+    import torch
+    import synth
+    N, K = synth.DECODE_SHAPES[j]
+    w = torch.from_numpy(synth.decode_weight(j)).cuda().view(torch.bfloat16)
+    cw, sw, gW, _ = nv.nvfp4_quantize(w)
+    del w
+    wp, _ = nv.nvfp4_prepare_weight(cw, sw, "ue4m3")
+    del cw, sw
+    R = max(2, -(-(1 << 30) // wp.numel()))
+    copies = [wp] + [wp.clone() for _ in range(R - 1)]
+    alpha = float(np.float32(1.0) / np.float32(gW.item()))
+    res = []
+    for i, M in enumerate(synth.DECODE_MS):
+        if M == 1:
+            continue
+        x = torch.from_numpy(synth.decode_activation(M, j, i)).cuda().view(torch.bfloat16)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = nv.workspace(nv.OP_W4A16, M, N, K)
+        k = [0]
+
+        def step():
+            nv.nvfp4_gemm_w4a16(x, copies[k[0] % R], N, K, alpha, out=out, ws=ws)
+            k[0] += 1
+        ms = time_calls(step, max(steps, R), max(warmup, R))
+        byts = N * K * 9 // 16 + 2 * M * K + 2 * M * N
+        r = dict(M=M, N=N, K=K, us=round(ms * 1e3, 2), TFLOPs=round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                 GBps=round(byts / (ms * 1e-3) / 1e9, 1))
+        log(f"[bench] W4A16 M={M} {N}x{K}: {r}")
+        res.append(r)
+    del copies
+    torch.cuda.empty_cache()
+    return res
 
 
 def prefill(nv, steps, warmup):
@@ -202,6 +246,9 @@ def main():
     ap.add_argument("--size", type=int, default=8192)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the W4A16 M = 1 decode shapes (one JSON line; for profiling the decode kernels)")
+    ap.add_argument("--large", action="store_true", help="also time the 32768^3 square (about 4 GiB of device memory)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -220,10 +267,16 @@ def main():
         return
     import nvfp4_block_scaled_amd as nv
     nv.init()
+    if args.decode_only:
+        import synth
+        print(json.dumps({"w4a16_m1": [w4a16_m1(nv, j) for j in range(len(synth.DECODE_SHAPES))]}), flush=True)
+        return
     S = args.size
     log(f"[bench] W4A4 {S}^3 bf16: {args.warmup} warmup + {args.steps} timed steps")
-    ms, tflops = w4a4_square(nv, S, args.steps, args.warmup)
-    log(f"[bench] W4A4 {S}^3: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s")
+    ms, tflops, ms_k = w4a4_square(nv, S, args.steps, args.warmup, kernel_only=True)
+    k_tflops = 2.0 * S ** 3 / (ms_k * 1e-3) / 1e12
+    log(f"[bench] W4A4 {S}^3: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s; GEMM kernel alone {ms_k:.4f} ms, "
+        f"{k_tflops:.1f} TFLOP/s")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -240,8 +293,9 @@ def main():
         "config": {"workload": f"W4A4 NVFP4 GEMM M=N=K={S}, A and B quantized on device from BF16 N(0,1) "
                                f"(per-16 E4M3 scale amax/6, per-tensor global scale), alpha=1/(gA gB), BF16 out",
                    "M": S, "N": S, "K": S, "out": "bf16"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic},
+        "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(k_tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_kernel (nvfp4_gemm_w4a4_tiled)", "kernel_ms": round(ms_k, 5)},
     }
     if not args.no_extras:
         import synth
@@ -255,11 +309,18 @@ def main():
         pf = prefill(nv, max(5, args.steps // 2), args.warmup)
         log(f"[bench] prefill: {pf}")
         extras["prefill_w4a4"] = pf
+        extras["w4a16_m_sweep"] = w4a16_m_sweep(nv, 2, args.steps, args.warmup)
         sweep = {}
         for s2 in (2048, 4096):
             m2, t2 = w4a4_square(nv, s2, args.steps, args.warmup)
             sweep[str(s2)] = dict(ms=round(m2, 4), TFLOPs=round(t2, 1))
             log(f"[bench] W4A4 {s2}^3: {m2:.4f} ms, {t2:.1f} TFLOP/s")
+        large = [16384] + ([32768] if args.large else [])
+        for s2 in large:
+            # 1 % of rows x8 and 1 % of 16-blocks zeroed, as the large-square workload states
+            m2, t2 = w4a4_square(nv, s2, max(5, args.steps // 10), max(3, args.warmup // 10), gen=synth.square_large)
+            sweep[str(s2)] = dict(ms=round(m2, 4), TFLOPs=round(t2, 1), inputs="outlier rows and zero blocks")
+            log(f"[bench] W4A4 {s2}^3 (outliers, zero blocks): {m2:.4f} ms, {t2:.1f} TFLOP/s")
         extras["w4a4_square"] = sweep
         result["extras"] = extras
     torch.cuda.synchronize()

@@ -105,12 +105,33 @@ nvfp4_status nvfp4_prepare_weight(const uint8_t *w_codes, const uint8_t *w_scale
  *  M >= 0 (M == 0 is a no-op), N % 32 == 0, K % 64 == 0.
  *  ws  workspace of nvfp4_workspace_bytes(NVFP4_OP_W4A4, M, N, K) bytes, device,
  *      16-byte aligned, no initialisation needed: the call first copies A into
- *      it in the prepared tile layout, then runs the GEMM from there. Calls that
- *      share a workspace must not run concurrently. */
+ *      it in the prepared tile layout (nvfp4_tile_activation), then runs the
+ *      GEMM from there (nvfp4_gemm_w4a4_tiled). Calls that share a workspace
+ *      must not run concurrently. */
 nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
                              int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
                              void *d, int out_dtype, int64_t ldd, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* Bytes of an activation in the tile layout: nvfp4_prepared_weight_bytes for M
+ * rounded up to 32 rows (0 for M <= 0 or K % 64 != 0). */
+size_t nvfp4_tiled_activation_bytes(int64_t M, int64_t K);
+
+/* Copies A ([M][K/2] codes, [M][K/16] scale bytes; 16- and 4-byte aligned) into
+ * the tile layout of a prepared weight (see nvfp4_prepare_weight) at a_tiled
+ * (nvfp4_tiled_activation_bytes(M, K) bytes, 16-byte aligned, device), rows
+ * M .. rounded-up-to-32 zero. A plain byte permutation, without the weight's
+ * sign/zero folding (the GEMM multiplies by every scale, so none is needed).
+ * For an activation that feeds several GEMMs: tile it once, then call
+ * nvfp4_gemm_w4a4_tiled. M >= 0 (0 is a no-op), K % 64 == 0. */
+nvfp4_status nvfp4_tile_activation(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
+                                   uint8_t *a_tiled, void *stream);
+
+/* nvfp4_gemm_w4a4 on an A that nvfp4_tile_activation has already tiled; the
+ * other arguments as there. Needs no workspace. */
+nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N, int64_t K,
+                                   float alpha, const float *alpha_dev, void *d, int out_dtype, int64_t ldd,
+                                   void *stream);
 
 /* W4A16 GEMM: y = alpha_eff * x (W.SFW)^T, x and y BF16, FP32 accumulation.
  *  x  [M][ldx] BF16 (uint16 bit patterns), device, 16-byte aligned, ldx % 8 == 0, ldx >= K.

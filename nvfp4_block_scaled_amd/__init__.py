@@ -36,6 +36,10 @@ _SIGS = [
     ("nvfp4_prepare_weight", ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P]),
     ("nvfp4_gemm_w4a4", ctypes.c_int,
      [_P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P]),
+    ("nvfp4_tiled_activation_bytes", ctypes.c_size_t, [_I64, _I64]),
+    ("nvfp4_tile_activation", ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    ("nvfp4_gemm_w4a4_tiled", ctypes.c_int,
+     [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, ctypes.c_int, _I64, _P]),
     ("nvfp4_gemm_w4a16", ctypes.c_int,
      [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _I64, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -172,6 +176,44 @@ def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, 
     nws = 0 if ws is None else ws.numel()
     _check(lib().nvfp4_gemm_w4a4(_ptr(a_codes), _ptr(a_scales), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
                                  _ptr(out), od[0], out.stride(0), _ptr(ws), nws, _stream()))
+    return out
+
+
+def nvfp4_tile_activation(a_codes, a_scales, out=None):
+    """A ([M][K/2] codes, [M][K/16] scales) -> the tile layout (uint8, nvfp4_tiled_activation_bytes)."""
+    a_codes = _u8(a_codes, "a_codes")
+    a_scales = _u8(a_scales, "a_scales")
+    if a_codes.dim() != 2 or a_scales.dim() != 2 or a_scales.shape != (a_codes.shape[0], a_codes.shape[1] // 8):
+        raise ValueError("a_codes must be [M][K/2] and a_scales [M][K/16]")
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    n = int(lib().nvfp4_tiled_activation_bytes(M, K))
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=a_codes.device)
+    elif out.numel() < n or out.dtype != torch.uint8:
+        raise ValueError("out must hold nvfp4_tiled_activation_bytes(M, K) uint8")
+    _check(lib().nvfp4_tile_activation(_ptr(a_codes), _ptr(a_scales), M, K, _ptr(out), _stream()))
+    return out
+
+
+def nvfp4_gemm_w4a4_tiled(a_tiled, M, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None):
+    """nvfp4_gemm_w4a4 on an activation already in the tile layout (nvfp4_tile_activation)."""
+    a_tiled = _u8(a_tiled, "a_tiled")
+    w_prep = _u8(w_prep, "w_prep")
+    if a_tiled.numel() < int(lib().nvfp4_tiled_activation_bytes(M, K)):
+        raise ValueError("a_tiled is smaller than nvfp4_tiled_activation_bytes(M, K)")
+    if w_prep.numel() != prepared_weight_bytes(N, K):
+        raise ValueError("w_prep does not match (N, K)")
+    od = {"bf16": (OUT_BF16, torch.bfloat16), "f32": (OUT_F32, torch.float32)}.get(out_dtype)
+    if od is None:
+        raise TypeError("out_dtype must be 'bf16' or 'f32'")
+    if out is None:
+        out = torch.empty((M, N), dtype=od[1], device=a_tiled.device)
+    elif out.dtype != od[1] or out.dim() != 2 or out.shape[0] != M or out.stride(1) != 1:
+        raise ValueError("out must be [M][>=N] rows of out_dtype")
+    if alpha_dev is not None and (alpha_dev.dtype != torch.float32 or not alpha_dev.is_cuda):
+        raise TypeError("alpha_dev must be a float32 device tensor")
+    _check(lib().nvfp4_gemm_w4a4_tiled(_ptr(a_tiled), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
+                                       _ptr(out), od[0], out.stride(0), _stream()))
     return out
 
 

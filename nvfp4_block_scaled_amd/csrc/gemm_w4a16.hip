@@ -36,12 +36,14 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------- planning
 
 struct Plan {
-  int kind;          // 0 = vector decode kernel, 1 = MFMA tile kernel, 2 = wide vector decode kernel
+  int kind;          // 0 = vector decode kernel, 1 = MFMA tile kernel, 2 = wide vector decode kernel,
+                     // 3 = skinny MFMA kernel
   int splits;        // K splits of the tile kernel (1 = none)
   int64_t grid_x;    // workgroups along the output
 };
 
 constexpr int kDecodeMaxM = 4;
+constexpr int kSkinnyMaxM = 128;
 constexpr int kDecodeThreads = 1024;      // 16 waves per 16-row group
 constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr int kDecodeLdsBytes = 64 * 1024;  // x staged in LDS: M * K * 2 bytes at most
@@ -63,6 +65,10 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K) {
     p.kind = N / 32 >= 2 * cus ? 2 : 0;
     p.splits = 1;
     p.grid_x = p.kind == 2 ? N / 32 : N / 16;
+  } else if (M <= kSkinnyMaxM) {
+    p.kind = 3;
+    p.splits = 1;
+    p.grid_x = N / 32;
   } else {
     p.kind = 1;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -278,6 +284,124 @@ __global__ __launch_bounds__(kWideWaves * 64) void decode_wide_kernel(const uint
     for (int w = 1; w < W; w++) v += red[w][m][rr];
     const float al = load_alpha(alpha, alpha_dev);
     y[m * ldy + g * 32 + rr] = f32_to_bf16_rne(al * v);
+  }
+}
+
+// ---------------------------------------------------------------- skinny MFMA kernel (4 < M <= 128)
+
+// Workgroup g covers the 32-row prepared tile group g over the whole K with 8
+// waves; wave w takes the tiles w, w + 8, ... as in the wide decode kernel. Per
+// tile and MFMA step s (k = 32h + 8s + i, the same K order as the prepared
+// weight units), lane l dequantizes its 8 codes of weight row 32g + (l & 31)
+// exactly to BF16 (E2M1 -> FP32, times the E4M3 scale, -> BF16) as the B
+// operand and loads the matching 8 BF16 of x rows 32 mt + (l & 31) as the A
+// operand of v_mfma_f32_32x32x16_bf16 (MT 32-row x tiles; rows >= M read as
+// zero through the buffer range check). Weights and x fragments are loaded a
+// batch of tiles ahead. Each wave ends with a full 32 x 32 MT partial tile; the
+// waves are added in a fixed tree (4+4, 2+2, 1+1) through LDS.
+constexpr int kSkWaves = 8;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc16(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)n, 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
+  bf16x8_t b;
+  __builtin_memcpy(&b, &v, 16);
+  return b;
+}
+
+template <int MT>
+__global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                             const uint8_t *__restrict__ wp, int64_t M, int64_t N,
+                                                             int64_t K, float alpha, const float *alpha_dev,
+                                                             uint16_t *__restrict__ y, int64_t ldy) {
+  constexpr int W = kSkWaves;
+  constexpr int U = MT == 1 ? 4 : (MT == 2 ? 2 : 1);     // tiles per wave per batch
+  __shared__ f32x16_t red[4][MT][64];
+  const int64_t T = K / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = lane >> 5, r = lane & 31;
+  const int64_t g = blockIdx.x;
+  const uint8_t *cb = wp + ((g * T) << 10) + lane * 16;
+  const uint8_t *sb = wp + N * K / 2 + ((g * T) << 7) + r * 4;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, M * ldx * 2);
+  uint32_t xo[MT];                                 // byte offset of this lane's x row, k = 32h
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) xo[mt] = (uint32_t)(((int64_t)(32 * mt + r) * ldx + 32 * h) * 2);
+
+  struct Batch {
+    u32x4_t cw[U];
+    uint32_t sw[U];
+    u32x4_t xv[U][MT][4];
+  };
+  auto issue = [&](Batch &b, int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+      const int64_t t = t0 + (int64_t)i * W;
+      const bool in = t < T;
+      const int64_t tc = in ? t : 0;
+      b.cw[i] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cb + (tc << 10)))
+                   : u32x4_t{0u, 0u, 0u, 0u};
+      b.sw[i] = in ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + (tc << 7))) : 0u;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+          b.xv[i][mt][s] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo[mt] + (uint32_t)(tc * 128 + 16 * s), 0, 0);
+    }
+  };
+  f32x16_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) acc[mt] = f32x16_t{};
+  auto compute = [&](const Batch &b, int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+      if (t0 + (int64_t)i * W < T) {
+        const f32x2_t sc = e4m3x2_to_f32(b.sw[i] >> (16 * h));
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          const bf16x8_t bv = dequant8_bf16(b.cw[i][s], sc[s >> 1]);
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++)
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b.xv[i][mt][s]), bv, acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  };
+  Batch b0, b1;
+  issue(b0, wave);
+  const int64_t step = (int64_t)W * U;
+  for (int64_t t0 = wave; t0 < T; t0 += 2 * step) {
+    issue(b1, t0 + step);
+    compute(b0, t0);
+    if (t0 + step >= T) break;
+    issue(b0, t0 + 2 * step);
+    compute(b1, t0 + step);
+  }
+  // fixed-order tree over the 8 waves' partial tiles
+#pragma unroll
+  for (int half = 4; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) red[wave - half][mt][lane] = acc[mt];
+    __syncthreads();
+    if (wave < half)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[mt] += red[wave][mt][lane];
+    __syncthreads();
+  }
+  if (wave == 0) {
+    const float al = load_alpha(alpha, alpha_dev);
+    const int64_t n = g * 32 + r;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const int64_t m = 32 * mt + 8 * (j >> 2) + 4 * h + (j & 3);
+        if (m < M) y[m * ldy + n] = f32_to_bf16_rne(al * acc[mt][j]);
+      }
   }
 }
 
@@ -506,6 +630,18 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     }
 #undef NVFP4_DECODE_CASE
 #undef NVFP4_DECODE_WIDE_CASE
+  } else if (plan.kind == 3) {
+    if (plan.grid_x > 0x7FFFFFFF || M * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
+    const unsigned grid = (unsigned)plan.grid_x, threads = w4a16::kSkWaves * 64;
+    if (M <= 32)
+      hipLaunchKernelGGL(w4a16::skinny_kernel<1>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
+                         alpha_dev, y, ldy);
+    else if (M <= 64)
+      hipLaunchKernelGGL(w4a16::skinny_kernel<2>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
+                         alpha_dev, y, ldy);
+    else
+      hipLaunchKernelGGL(w4a16::skinny_kernel<4>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
+                         alpha_dev, y, ldy);
   } else {
     const int64_t tiles_n = (N + w4a16::BN - 1) / w4a16::BN;
     if (plan.grid_x > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;

@@ -362,25 +362,26 @@ size_t nvfp4::w4a4_workspace_bytes(int64_t M, int64_t K) {
   return (size_t)(w4a4::padded_rows(M) * K / 2 + w4a4::padded_rows(M) * K / 16);
 }
 
-extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
-                                        int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
-                                        void *d, int out_dtype, int64_t ldd, void *ws, size_t ws_bytes,
-                                        void *stream) {
+namespace {
+
+nvfp4_status check_gemm_args(const uint8_t *w_prep, int64_t M, int64_t N, int64_t K, float alpha,
+                             const float *alpha_dev, void *d, int out_dtype, int64_t ldd) {
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0 || ldd < N) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
-  if (!a_codes || !a_scales || !w_prep || !d) return NVFP4_ERR_NULL;
+  if (!w_prep || !d) return NVFP4_ERR_NULL;
   if (!(alpha == alpha) || alpha - alpha != 0.0f) return NVFP4_ERR_VALUE;
   const size_t esz = out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
-  if (!aligned(a_codes, 16) || !aligned(a_scales, 4) || !aligned(w_prep, 16) || !aligned(d, esz) ||
-      (alpha_dev && !aligned(alpha_dev, 4)))
-    return NVFP4_ERR_ALIGN;
+  if (!aligned(w_prep, 16) || !aligned(d, esz) || (alpha_dev && !aligned(alpha_dev, 4))) return NVFP4_ERR_ALIGN;
   // 32-bit buffer offsets inside the code tiles of one 256-row (256-column) tile
   if ((int64_t)8 * (K / 64) * 1024 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
   if ((M + 127) / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
-  const size_t need = w4a4_workspace_bytes(M, K);
-  if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
-  if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+// The GEMM kernel proper on A already in the tile layout (arguments checked).
+nvfp4_status launch_gemm(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N, int64_t K, float alpha,
+                         const float *alpha_dev, void *d, int out_dtype, int64_t ldd, hipStream_t s) {
   DeviceInfo di;
   nvfp4_status st = device_info(&di);
   if (st != NVFP4_OK) return st;
@@ -389,13 +390,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a
   const int64_t bt = 64 * T;
   const int64_t tiles_m = (M + bt - 1) / bt;
   const int64_t tiles_n = (N + bt - 1) / bt;
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t *at = static_cast<uint8_t *>(ws);
-  const int64_t units = w4a4::padded_rows(M) / 32 * (K / 64) * 64;
-  hipLaunchKernelGGL(w4a4::tile_a_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, a_codes, a_scales,
-                     M, K, at);
-  NVFP4_LAUNCH_CHECK();
-  w4a4::Params p{at, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tiles_m, (int)tiles_n};
+  w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tiles_m, (int)tiles_n};
   const int64_t total = tiles_m * tiles_n;
   const int64_t slots = (int64_t)di.num_cus * (T == 4 ? 1 : 2);
   const int grid = (int)(total < slots ? total : slots);
@@ -412,4 +407,61 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a
   }
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
+}
+
+void launch_tile_a(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K, uint8_t *at,
+                   hipStream_t s) {
+  const int64_t units = w4a4::padded_rows(M) / 32 * (K / 64) * 64;
+  hipLaunchKernelGGL(w4a4::tile_a_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, a_codes, a_scales,
+                     M, K, at);
+}
+
+}  // namespace
+
+extern "C" size_t nvfp4_tiled_activation_bytes(int64_t M, int64_t K) { return w4a4_workspace_bytes(M, K); }
+
+extern "C" nvfp4_status nvfp4_tile_activation(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
+                                              uint8_t *a_tiled, void *stream) {
+  if (M < 0 || K <= 0 || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_tiled) return NVFP4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(a_scales, 4) || !aligned(a_tiled, 16)) return NVFP4_ERR_ALIGN;
+  if (w4a4::padded_rows(M) / 32 * (K / 64) * 64 / 256 + 1 > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
+  DeviceInfo di;
+  nvfp4_status st = device_info(&di);
+  if (st != NVFP4_OK) return st;
+  launch_tile_a(a_codes, a_scales, M, K, a_tiled, (hipStream_t)stream);
+  NVFP4_LAUNCH_CHECK();
+  return NVFP4_OK;
+}
+
+extern "C" nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N,
+                                              int64_t K, float alpha, const float *alpha_dev, void *d,
+                                              int out_dtype, int64_t ldd, void *stream) {
+  nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, d, out_dtype, ldd);
+  if (st != NVFP4_OK || M == 0) return st;
+  if (!a_tiled) return NVFP4_ERR_NULL;
+  if (!aligned(a_tiled, 16)) return NVFP4_ERR_ALIGN;
+  return launch_gemm(a_tiled, w_prep, M, N, K, alpha, alpha_dev, d, out_dtype, ldd, (hipStream_t)stream);
+}
+
+extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
+                                        int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
+                                        void *d, int out_dtype, int64_t ldd, void *ws, size_t ws_bytes,
+                                        void *stream) {
+  nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, d, out_dtype, ldd);
+  if (st != NVFP4_OK || M == 0) return st;
+  if (!a_codes || !a_scales) return NVFP4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(a_scales, 4)) return NVFP4_ERR_ALIGN;
+  const size_t need = w4a4_workspace_bytes(M, K);
+  if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != NVFP4_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *at = static_cast<uint8_t *>(ws);
+  launch_tile_a(a_codes, a_scales, M, K, at, s);
+  NVFP4_LAUNCH_CHECK();
+  return launch_gemm(at, w_prep, M, N, K, alpha, alpha_dev, d, out_dtype, ldd, s);
 }

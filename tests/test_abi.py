@@ -73,6 +73,33 @@ def test_gemm_w4a4_argument_checks():
     assert call(ws=ODD, nws=need) == nv.ERR_ALIGN
 
 
+def test_tile_activation_and_tiled_gemm_argument_checks():
+    L = nv.lib()
+    assert L.nvfp4_tiled_activation_bytes(33, 128) == 64 * 128 * 9 // 16
+    assert L.nvfp4_tiled_activation_bytes(32, 96) == 0
+    t = L.nvfp4_tile_activation
+    assert t(FAKE, FAKE, 64, 96, FAKE, None) == nv.ERR_SHAPE
+    assert t(FAKE, FAKE, -1, 128, FAKE, None) == nv.ERR_SHAPE
+    assert t(FAKE, FAKE, 0, 128, FAKE, None) == nv.OK
+    assert t(None, FAKE, 64, 128, FAKE, None) == nv.ERR_NULL
+    assert t(FAKE, FAKE, 64, 128, None, None) == nv.ERR_NULL
+    assert t(ODD, FAKE, 64, 128, FAKE, None) == nv.ERR_ALIGN
+    assert t(FAKE, FAKE, 64, 128, ODD, None) == nv.ERR_ALIGN
+    g = L.nvfp4_gemm_w4a4_tiled
+
+    def call(at=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, d=FAKE, dt=nv.OUT_BF16, ldd=64):
+        return g(at, w, M, N, K, alpha, None, d, dt, ldd, None)
+    assert call(dt=5) == nv.ERR_DTYPE
+    assert call(K=96) == nv.ERR_SHAPE
+    assert call(N=40) == nv.ERR_SHAPE
+    assert call(M=0) == nv.OK
+    assert call(at=None) == nv.ERR_NULL
+    assert call(w=None) == nv.ERR_NULL
+    assert call(alpha=float("nan")) == nv.ERR_VALUE
+    assert call(at=ODD) == nv.ERR_ALIGN
+    assert call(d=ODD) == nv.ERR_ALIGN
+
+
 def test_gemm_w4a16_argument_checks():
     f = nv.lib().nvfp4_gemm_w4a16
 

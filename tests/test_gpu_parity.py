@@ -129,6 +129,34 @@ def test_w4a4_ragged_shapes(M, N, K, out_dtype):
     assert_close(host(out), D, S, bf16=out_dtype == "bf16", what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,K", [(64, 128), (77, 320), (1, 64)])
+def test_tile_activation_bytes_match_oracle_layout(M, K):
+    """The activation tile layout is the prepared-weight index map (no folds needed:
+    positive, non-zero scales), rows past M zero."""
+    a, sa = _random_nvfp4(M * 13 + K, M, K)
+    at = nv.nvfp4_tile_activation(dev(a), dev(sa))
+    torch.cuda.synchronize()
+    Mp = -(-M // 32) * 32
+    a_pad = np.zeros((Mp, K // 2), np.uint8)
+    s_pad = np.zeros((Mp, K // 16), np.uint8)
+    a_pad[:M], s_pad[:M] = a, sa
+    ref, bad = prepared.prepare_weight(a_pad, s_pad, "e4m3")
+    assert bad == 0
+    assert np.array_equal(host(at), ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 320, 192), (2048, 2048, 512)])
+def test_w4a4_tiled_entry_matches_standard(M, N, K):
+    a, sa = _random_nvfp4(M + N, M, K)
+    b, sb = _random_nvfp4(M + N + 1, N, K)
+    wp, _ = _prep(b, sb)
+    std = nv.nvfp4_gemm_w4a4(dev(a), dev(sa), wp, N, K, 0.5, None, "bf16")
+    at = nv.nvfp4_tile_activation(dev(a), dev(sa))
+    til = nv.nvfp4_gemm_w4a4_tiled(at, M, wp, N, K, 0.5, None, "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(std, til)
+
+
 def test_w4a4_closed_forms():
     M = N = 64
     K = 256
