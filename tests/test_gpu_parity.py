@@ -85,6 +85,29 @@ def test_quantize_edge_values():
     assert g.item() == 1.0 and not codes.any() and not scales.any()
 
 
+def test_quantize_all_bf16_patterns():
+    """Every finite BF16 value, in blocks of widely different magnitude: the E2M1
+    rounding (hardware conversion in the library) against the oracle's stated rule."""
+    b = np.arange(65536, dtype=np.uint32)
+    b = b[((b >> 7) & 0xFF) != 0xFF].astype(np.uint16)          # drop Inf / NaN patterns
+    r = np.random.default_rng(5)
+    x = r.permutation(b)
+    x = x[: x.size // 64 * 64].reshape(-1, 64)
+    codes, scales, g, _ = nv.nvfp4_quantize(dev(x).view(torch.bfloat16))
+    c_ref, s_ref, g_ref, _ = quantize.quantize(x)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    assert np.float32(g.item()) == np.float32(g_ref)
+    # the same patterns scaled into one binade per row, so many blocks sit near the top of the grid
+    y = x.copy()
+    y &= 0x807F
+    y |= np.uint16(0x3F80)
+    codes, scales, g, _ = nv.nvfp4_quantize(dev(y).view(torch.bfloat16))
+    c_ref, s_ref, g_ref, _ = quantize.quantize(y)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+
+
 def test_quantize_prefill_activation_full():
     x, _ = synth.prefill_activation()
     codes, scales, g, inv_g = nv.nvfp4_quantize(dev(x).view(torch.bfloat16))
