@@ -17,7 +17,12 @@
 //    batches of four); all its workgroups are resident at once. (A K split
 //    across workgroups would need an agent-scope release per workgroup, an L2
 //    write-back on this part, which measured several times slower.)
-//  * M > 4: an LDS-tiled MFMA kernel (v_mfma_f32_32x32x16_bf16). BF16 x tiles
+//  * 4 < M <= 64 (and M <= 4 when x does not fit in LDS): the skinny MFMA
+//    kernel, the decode structure with v_mfma_f32_32x32x16_bf16 on one or two
+//    32-row x tiles (below).
+//  * M > 64 with enough output tiles to fill half the CUs: the big MFMA kernel,
+//    built like the W4A4 kernel (below).
+//  * otherwise: an LDS-tiled MFMA kernel (v_mfma_f32_32x32x16_bf16). BF16 x tiles
 //    are staged through LDS (XOR-swizzled rows, conflict-free 16-byte reads);
 //    weight codes and scales are staged as packed bytes in the prepared tile
 //    format and dequantized exactly to BF16 in registers (E2M1 -> FP32, times
@@ -37,13 +42,13 @@ constexpr int kThreads = 256;
 
 struct Plan {
   int kind;          // 0 = vector decode kernel, 1 = MFMA tile kernel, 2 = wide vector decode kernel,
-                     // 3 = skinny MFMA kernel
+                     // 3 = skinny MFMA kernel, 4 = big MFMA kernel
   int splits;        // K splits of the tile kernel (1 = none)
   int64_t grid_x;    // workgroups along the output
 };
 
 constexpr int kDecodeMaxM = 4;
-constexpr int kSkinnyMaxM = 128;
+constexpr int kSkinnyMaxM = 64;
 constexpr int kDecodeThreads = 1024;      // 16 waves per 16-row group
 constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr int kDecodeLdsBytes = 64 * 1024;  // x staged in LDS: M * K * 2 bytes at most
@@ -53,6 +58,13 @@ static int num_cus_or_default() {
   DeviceInfo d;
   if (device_info(&d) == NVFP4_OK && d.num_cus > 0) return d.num_cus;
   return 256;
+}
+
+// Output tiles of the big kernel: 256 x 256 when those fill the CUs, else 128 x 128.
+static int big_tile_t(int64_t M, int64_t N, int cus) { return ((M + 255) / 256) * ((N + 255) / 256) >= cus ? 4 : 2; }
+static int64_t big_tiles(int64_t M, int64_t N, int cus) {
+  const int64_t bt = 64 * big_tile_t(M, N, cus);
+  return ((M + bt - 1) / bt) * ((N + bt - 1) / bt);
 }
 
 static Plan make_plan(int64_t M, int64_t N, int64_t K) {
@@ -69,6 +81,11 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K) {
     p.kind = 3;
     p.splits = 1;
     p.grid_x = N / 32;
+  } else if (big_tiles(M, N, cus) * 2 >= cus) {
+    // enough output tiles for the persistent kernel; otherwise the split-K tile kernel
+    p.kind = 4;
+    p.splits = 1;
+    p.grid_x = 0;
   } else {
     p.kind = 1;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -287,7 +304,7 @@ __global__ __launch_bounds__(kWideWaves * 64) void decode_wide_kernel(const uint
   }
 }
 
-// ---------------------------------------------------------------- skinny MFMA kernel (4 < M <= 128)
+// ---------------------------------------------------------------- skinny MFMA kernel (4 < M <= 64)
 
 // Workgroup g covers the 32-row prepared tile group g over the whole K with 8
 // waves; wave w takes the tiles w, w + 8, ... as in the wide decode kernel. Per
@@ -318,7 +335,7 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *_
                                                              int64_t K, float alpha, const float *alpha_dev,
                                                              uint16_t *__restrict__ y, int64_t ldy) {
   constexpr int W = kSkWaves;
-  constexpr int U = MT == 1 ? 4 : (MT == 2 ? 2 : 1);     // tiles per wave per batch
+  constexpr int U = MT == 1 ? 4 : 2;                        // tiles per wave per batch
   __shared__ f32x16_t red[4][MT][64];
   const int64_t T = K / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -404,6 +421,276 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *_
       }
   }
 }
+
+// ---------------------------------------------------------------- big MFMA kernel (M > 64)
+
+// The W4A4 kernel's structure with x in BF16. Persistent workgroups of 4 waves
+// (2 x 2) over 64T x 64T output tiles (T = 4: 256 x 256, one workgroup per CU;
+// T = 2: 128 x 128), each wave owning T x T v_mfma_f32_32x32x16_bf16 tiles.
+//  * W: each wave loads its T column groups' fragments of a 64-wide K chunk
+//    straight into registers (one contiguous 1 KB each plus a scale word), two
+//    chunks ahead in a three-deep ring, and dequantizes them exactly to BF16
+//    (E2M1 -> FP32, times the E4M3 scale, -> BF16) one MFMA step ahead.
+//  * x: the tile's 64T rows x 64 k BF16 (8T KB) are loaded one chunk ahead with
+//    coalesced 16-byte loads (rows past M read as zero through the buffer range
+//    check), written into one of two LDS buffers with 16-byte units XOR-swizzled
+//    by row, and read back as MFMA fragments without bank conflicts. One LDS-only
+//    barrier per chunk; the x loads are issued before the W loads so waiting for
+//    them does not wait for the W prefetch.
+//  * One scheduling region per MFMA step, as in the W4A4 kernel.
+namespace big {
+
+constexpr int kThreads = 256;
+constexpr int kGroupM = 8;
+
+struct Params {
+  const uint16_t *x;
+  int64_t ldx;
+  const uint8_t *wp;
+  uint16_t *y;
+  int64_t ldy, M, N, K;
+  float alpha;
+  const float *alpha_dev;
+  int tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)n, 0x00020000);
+}
+
+template <int T>
+struct WFrags {
+  u32x4_t w[T];
+  uint32_t ws[T];
+};
+
+template <int T>
+struct XRegs {
+  u32x4_t v[2 * T];
+};
+
+struct TileBase {
+  const uint8_t *x, *w, *ws;
+  int64_t x_bytes, w_bytes, ws_bytes;
+};
+
+template <int T>
+__device__ __forceinline__ void load_w(const TileBase &tb, const uint32_t (&ow)[T], const uint32_t (&ows)[T],
+                                       int64_t c, int64_t nch, WFrags<T> &f) {
+  const bool in = c < nch;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(tb.w, in ? tb.w_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(tb.ws, in ? tb.ws_bytes : 0);
+#pragma unroll
+  for (int j = 0; j < T; j++) f.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, ow[j], (int)(c * 1024), 0);
+#pragma unroll
+  for (int j = 0; j < T; j++) f.ws[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ows[j], (int)(c * 128), 0);
+}
+
+// x chunk c of the tile: thread t loads units q = t + 256 i (row q >> 3, unit q & 7).
+template <int T>
+__device__ __forceinline__ void load_x(const TileBase &tb, int64_t ldx, int64_t c, int64_t nch, XRegs<T> &xr) {
+  const __amdgpu_buffer_rsrc_t rx = rsrc(tb.x, c < nch ? tb.x_bytes : 0);
+#pragma unroll
+  for (int i = 0; i < 2 * T; i++) {
+    const int q = (int)threadIdx.x + kThreads * i;
+    const uint32_t off = (uint32_t)(((int64_t)(q >> 3) * ldx + c * 64 + (q & 7) * 8) * 2);
+    xr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void store_x(uint8_t *buf, const XRegs<T> &xr) {
+#pragma unroll
+  for (int i = 0; i < 2 * T; i++) {
+    const int q = (int)threadIdx.x + kThreads * i;
+    const int row = q >> 3, u = q & 7;
+    *reinterpret_cast<u32x4_t *>(buf + row * 128 + ((u ^ (row & 7)) << 4)) = xr.v[i];
+  }
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// x fragments of MFMA step s from LDS: k = 32h + 8s .. +7 of row wm*32T + 32i + r.
+template <int T>
+__device__ __forceinline__ void read_x(const uint8_t *buf, int s, int wm, bf16x8_t (&a)[T]) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+  const int u = 4 * h + s;
+#pragma unroll
+  for (int i = 0; i < T; i++) {
+    const int row = wm * 32 * T + 32 * i + r;
+    a[i] = *reinterpret_cast<const bf16x8_t *>(buf + row * 128 + ((u ^ (row & 7)) << 4));
+  }
+}
+
+// W fragments of MFMA step s, dequantized from dword s.
+template <int T>
+__device__ __forceinline__ void deq_w(const WFrags<T> &f, const f32x2_t (&sc)[T], int s, bf16x8_t (&b)[T]) {
+#pragma unroll
+  for (int j = 0; j < T; j++) b[j] = dequant8_bf16(f.w[j][s], sc[j][s >> 1]);
+}
+
+template <int T>
+__device__ __forceinline__ void scales_of(const WFrags<T> &f, f32x2_t (&sc)[T]) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int j = 0; j < T; j++) sc[j] = e4m3x2_to_f32(f.ws[j] >> (16 * h));
+}
+
+// One chunk. f[P] holds chunk c's W, f[(P+1)%3] chunk c + 1's; LDS buffer c & 1
+// holds chunk c's x. On entry (a, b) are step 0's operands and sc chunk c's
+// scales; on exit, chunk c + 1's.
+template <int P, int T>
+__device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uint32_t (&ow)[T],
+                                      const uint32_t (&ows)[T], int64_t c, int64_t nch, WFrags<T> (&f)[3],
+                                      f32x2_t (&sc)[T], uint8_t *smem, int wm, bf16x8_t (&a)[T], bf16x8_t (&b)[T],
+                                      f32x16_t (&acc)[T][T]) {
+  constexpr int kValu = 16 / T + 1;                 // dequant instructions per MFMA, rounded up
+  XRegs<T> xr;
+  load_x<T>(tb, ldx, c + 1, nch, xr);
+  load_w<T>(tb, ow, ows, c + 2, nch, f[(P + 2) % 3]);
+  uint8_t *cur = smem + (c & 1) * (64 * T * 128);
+  uint8_t *nxt = smem + ((c + 1) & 1) * (64 * T * 128);
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    bf16x8_t an[T], bn[T];
+    if (s < 3) {
+      read_x<T>(cur, s + 1, wm, an);
+      deq_w<T>(f[P], sc, s + 1, bn);
+    } else {
+      scales_of<T>(f[(P + 1) % 3], sc);
+      deq_w<T>(f[(P + 1) % 3], sc, 0, bn);
+    }
+#pragma unroll
+    for (int i = 0; i < T; i++)
+#pragma unroll
+      for (int j = 0; j < T; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < T; i++) {
+      if (s < 3) a[i] = an[i];
+      b[i] = bn[i];
+    }
+    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 4 * T, 0);
+#pragma unroll
+    for (int k = 0; k < T * T; k++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+      if (s < 3 && k < T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  store_x<T>(nxt, xr);
+  lds_barrier();
+  read_x<T>(nxt, 0, wm, a);   // the next chunk's step-0 x, now that it is in LDS
+}
+
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int per_band = kGroupM * tiles_n;
+  const int band = t / per_band;
+  const int first = band * kGroupM;
+  const int rows = min(kGroupM, tiles_m - first);
+  const int w = t - band * per_band;
+  tm = first + w % rows;
+  tn = w / rows;
+}
+
+template <int T>
+__global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p) {
+  constexpr int BT = 64 * T;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BT * 128];   // two x chunks; reused by the epilogue
+  const int t = threadIdx.x, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = t & 63, h = lane >> 5, r = lane & 31;
+  const int total = p.tiles_m * p.tiles_n;
+  const int G = gridDim.x;
+  int pid = blockIdx.x;
+  if ((G & 7) == 0) pid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const float alpha = load_alpha(p.alpha, p.alpha_dev);
+  const int64_t nch = p.K / 64, kt = p.K / 64;
+  uint32_t ow[T], ows[T];
+#pragma unroll
+  for (int j = 0; j < T; j++) {
+    ow[j] = (uint32_t)(((wn * T + j) * kt) * 1024 + lane * 16);
+    ows[j] = (uint32_t)(((wn * T + j) * kt) * 128 + r * 4);
+  }
+  for (int tile = pid; tile < total; tile += G) {
+    int tm, tn;
+    tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BT, n0 = (int64_t)tn * BT;
+    TileBase tb;
+    tb.x = reinterpret_cast<const uint8_t *>(p.x + m0 * p.ldx);
+    tb.x_bytes = (p.M - m0) * p.ldx * 2;
+    tb.w = p.wp + (n0 >> 5) * kt * 1024;
+    tb.w_bytes = (p.N - n0) / 32 * kt * 1024;
+    tb.ws = p.wp + p.N * p.K / 2 + (n0 >> 5) * kt * 128;
+    tb.ws_bytes = (p.N - n0) / 32 * kt * 128;
+
+    f32x16_t acc[T][T];
+#pragma unroll
+    for (int i = 0; i < T; i++)
+#pragma unroll
+      for (int j = 0; j < T; j++) acc[i][j] = f32x16_t{};
+    WFrags<T> f[3];
+    f32x2_t sc[T];
+    bf16x8_t a[T], b[T];
+    {
+      XRegs<T> xr;
+      load_x<T>(tb, p.ldx, 0, nch, xr);
+      load_w<T>(tb, ow, ows, 0, nch, f[0]);
+      load_w<T>(tb, ow, ows, 1, nch, f[1]);
+      store_x<T>(smem, xr);
+    }
+    lds_barrier();
+    scales_of<T>(f[0], sc);
+    read_x<T>(smem, 0, wm, a);
+    deq_w<T>(f[0], sc, 0, b);
+    for (int64_t c = 0; c < nch; c += 3) {
+      chunk<0, T>(tb, p.ldx, ow, ows, c, nch, f, sc, smem, wm, a, b, acc);
+      chunk<1, T>(tb, p.ldx, ow, ows, c + 1, nch, f, sc, smem, wm, a, b, acc);
+      chunk<2, T>(tb, p.ldx, ow, ows, c + 2, nch, f, sc, smem, wm, a, b, acc);
+    }
+    // epilogue: per wave 32 x 32T staging of BF16 in LDS (after every wave is done with x)
+    __syncthreads();
+    constexpr int ROW_BYTES = 32 * T * 2;
+    uint8_t *reg = smem + wave * (32 * ROW_BYTES);
+    const int64_t col0 = n0 + wn * 32 * T;
+    const int64_t ncols = p.N - col0;
+    const bool vec_ok = (p.ldy * 2) % 16 == 0 && ((uintptr_t)p.y & 15) == 0;
+#pragma unroll
+    for (int i = 0; i < T; i++) {
+#pragma unroll
+      for (int j = 0; j < T; j++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int row = 8 * (e >> 2) + 4 * h + (e & 3);
+          *reinterpret_cast<uint16_t *>(reg + row * ROW_BYTES + (j * 32 + r) * 2) = f32_to_bf16_rne(alpha * acc[i][j][e]);
+        }
+      __syncthreads();
+      constexpr int PIECES = ROW_BYTES / 16;
+      for (int q = lane; q < 32 * PIECES; q += 64) {
+        const int row = q / PIECES, pc = q % PIECES;
+        const int64_t m = m0 + wm * 32 * T + i * 32 + row;
+        const int64_t cc = (int64_t)pc * 8;
+        if (m < p.M && cc < ncols) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t *>(reg + row * ROW_BYTES + pc * 16);
+          uint16_t *dst = p.y + m * p.ldy + col0 + cc;
+          if (vec_ok) {
+            *reinterpret_cast<u32x4_t *>(dst) = v;
+          } else {
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(&v);
+            for (int e2 = 0; e2 < 8; e2++) dst[e2] = src[e2];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace big
 
 // ---------------------------------------------------------------- MFMA tile kernel (M > 4)
 
@@ -630,17 +917,28 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     }
 #undef NVFP4_DECODE_CASE
 #undef NVFP4_DECODE_WIDE_CASE
+  } else if (plan.kind == 4) {
+    if ((int64_t)256 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
+    const int T = w4a16::big_tile_t(M, N, di.num_cus);
+    const int64_t bt = 64 * T;
+    const int64_t tiles_m = (M + bt - 1) / bt, tiles_n = (N + bt - 1) / bt;
+    if (tiles_m * tiles_n > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
+    w4a16::big::Params bp{x, ldx, w_prep, y, ldy, M, N, K, alpha, alpha_dev, (int)tiles_m, (int)tiles_n};
+    const int64_t slots = (int64_t)di.num_cus * (T == 4 ? 1 : 2);
+    const int64_t total = tiles_m * tiles_n;
+    const unsigned grid = (unsigned)(total < slots ? total : slots);
+    if (T == 4)
+      hipLaunchKernelGGL(w4a16::big::big_kernel<4>, dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);
+    else
+      hipLaunchKernelGGL(w4a16::big::big_kernel<2>, dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);
   } else if (plan.kind == 3) {
     if (plan.grid_x > 0x7FFFFFFF || M * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
     const unsigned grid = (unsigned)plan.grid_x, threads = w4a16::kSkWaves * 64;
     if (M <= 32)
       hipLaunchKernelGGL(w4a16::skinny_kernel<1>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
                          alpha_dev, y, ldy);
-    else if (M <= 64)
-      hipLaunchKernelGGL(w4a16::skinny_kernel<2>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
-                         alpha_dev, y, ldy);
     else
-      hipLaunchKernelGGL(w4a16::skinny_kernel<4>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
+      hipLaunchKernelGGL(w4a16::skinny_kernel<2>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
                          alpha_dev, y, ldy);
   } else {
     const int64_t tiles_n = (N + w4a16::BN - 1) / w4a16::BN;

@@ -298,6 +298,17 @@ def test_w4a16_wide_decode(M, N, K):
     assert_close(host(out), y, S, bf16=True, what=f"wide decode M={M} {N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1000, 2080, 320), (2600, 8224, 128)])
+def test_w4a16_big_ragged(M, N, K):
+    """Larger M with ragged rows and columns on the persistent MFMA path (128 x 128
+    tiles for the first shape, 256 x 256 for the second); full check."""
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, M + N + K)
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
+    torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"w4a16 big {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("j", range(4))
 @pytest.mark.parametrize("mi", range(5))
 def test_w4a16_decode_shapes(j, mi):
