@@ -13,8 +13,8 @@
 //    waits on another and nothing crosses an XCD within the kernel. x is staged
 //    once per workgroup in LDS and read by broadcast. With at least two 32-row
 //    groups per CU, a wide variant is used instead: one 512-thread workgroup
-//    per whole group, each wave keeping eight 1 KB tile loads in flight (two
-//    batches of four); all its workgroups are resident at once. (A K split
+//    per whole group, each wave keeping four 1 KB tile loads in flight (two
+//    batches of two); all its workgroups are resident at once. (A K split
 //    across workgroups would need an agent-scope release per workgroup, an L2
 //    write-back on this part, which measured several times slower.)
 //  * 4 < M <= 64 (and M <= 4 when x does not fit in LDS): the skinny MFMA
@@ -202,12 +202,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const uint16_t *
 // group g (rows 32g .. 32g+31) over the whole K with 8 waves; wave w takes the
 // tiles w, w + 8, w + 16, ...; lane l is unit l of each tile (row r = l & 31,
 // k in [32h, 32h + 32) with h = l >> 5), so one wave load is the tile's
-// contiguous 1 KB. Loads run four tiles per wave ahead in a two-batch register
+// contiguous 1 KB. Loads run two tiles per wave ahead in a two-batch register
 // ring (non-temporal: the weights are streamed once); the first batch is issued
 // before x is staged. With at least two groups per CU every workgroup is
 // resident at once, and a group is reduced inside its workgroup.
 constexpr int kWideWaves = 8;
-constexpr int kWideAhead = 4;
+constexpr int kWideAhead = 2;
 
 template <int M>
 __global__ __launch_bounds__(kWideWaves * 64) void decode_wide_kernel(const uint16_t *__restrict__ x, int64_t ldx,
