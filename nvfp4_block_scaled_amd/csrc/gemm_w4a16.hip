@@ -49,6 +49,7 @@ struct Plan {
 
 constexpr int kDecodeMaxM = 4;
 constexpr int kSkinnyMaxM = 64;
+constexpr int kSkinnyDirectMaxM = 16;   // up to here the skinny kernel reads x rows directly
 constexpr int kDecodeThreads = 1024;      // 16 waves per 16-row group
 constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr int kDecodeLdsBytes = 64 * 1024;  // x staged in LDS: M * K * 2 bytes at most
@@ -97,7 +98,12 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-static size_t workspace_for(const Plan &p, int64_t M, int64_t N) {
+// The skinny kernel reads x from the workspace in MFMA fragment order:
+// roundup32(M) rows x K BF16.
+static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 32 * 32) * (size_t)K * 2; }
+
+static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
+  if (p.kind == 3) return M > kSkinnyDirectMaxM ? skinny_x_bytes(M, K) : 0;
   if (p.splits <= 1) return 0;
   return (size_t)p.splits * (size_t)M * (size_t)N * 4;
 }
@@ -312,9 +318,12 @@ __global__ __launch_bounds__(kWideWaves * 64) void decode_wide_kernel(const uint
 // weight units), lane l dequantizes its 8 codes of weight row 32g + (l & 31)
 // exactly to BF16 (E2M1 -> FP32, times the E4M3 scale, -> BF16) as the B
 // operand and loads the matching 8 BF16 of x rows 32 mt + (l & 31) as the A
-// operand of v_mfma_f32_32x32x16_bf16 (MT 32-row x tiles; rows >= M read as
-// zero through the buffer range check). Weights and x fragments are loaded a
-// batch of tiles ahead. Each wave ends with a full 32 x 32 MT partial tile; the
+// operand of v_mfma_f32_32x32x16_bf16 (MT 32-row x tiles). For M > 16 (XF) x is
+// first copied into the workspace in fragment order (tile t, step s, x tile mt:
+// 64 lanes x 16 bytes, rows >= M zero), so each fragment load is one contiguous
+// 1 KB instead of 32 scattered rows; for M <= 16 the scattered direct reads
+// cost less than the copy (rows >= M read as zero through the buffer range
+// check). Weights and x fragments are loaded a batch of tiles ahead. Each wave ends with a full 32 x 32 MT partial tile; the
 // waves are added in a fixed tree (4+4, 2+2, 1+1) through LDS.
 constexpr int kSkWaves = 8;
 
@@ -329,11 +338,31 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return b;
 }
 
-template <int MT>
+// x [M][ldx] BF16 -> fragment order: unit u = ((t * 4 + s) * MT + mt) * 64 + lane
+// holds x[32 mt + (lane & 31)][64 t + 32 (lane >> 5) + 8 s .. +8] (zero past M).
+__global__ __launch_bounds__(256) void tile_x_kernel(const uint16_t *__restrict__ x, int64_t ldx, int64_t M,
+                                                     int64_t K, int MT, u32x4_t *__restrict__ xf) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t units = K / 64 * 4 * MT * 64;
+  if (u >= units) return;
+  const int lane = (int)(u & 63);
+  const int64_t rest = u >> 6;
+  const int mt = (int)(rest % MT);
+  const int64_t ts = rest / MT;
+  const int s = (int)(ts & 3);
+  const int64_t t = ts >> 2;
+  const int64_t row = 32 * mt + (lane & 31);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (row < M) v = *reinterpret_cast<const u32x4_t *>(x + row * ldx + t * 64 + 32 * (lane >> 5) + 8 * s);
+  xf[u] = v;
+}
+
+template <int MT, bool XF>
 __global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *__restrict__ x, int64_t ldx,
                                                              const uint8_t *__restrict__ wp, int64_t M, int64_t N,
                                                              int64_t K, float alpha, const float *alpha_dev,
-                                                             uint16_t *__restrict__ y, int64_t ldy) {
+                                                             uint16_t *__restrict__ y, int64_t ldy,
+                                                             const uint8_t *__restrict__ xf) {
   constexpr int W = kSkWaves;
   constexpr int U = MT == 1 ? 4 : 2;                        // tiles per wave per batch
   __shared__ f32x16_t red[4][MT][64];
@@ -343,8 +372,9 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *_
   const int64_t g = blockIdx.x;
   const uint8_t *cb = wp + ((g * T) << 10) + lane * 16;
   const uint8_t *sb = wp + N * K / 2 + ((g * T) << 7) + r * 4;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, M * ldx * 2);
-  uint32_t xo[MT];                                 // byte offset of this lane's x row, k = 32h
+  const uint8_t *xl = XF ? xf + lane * 16 : nullptr;   // this lane's unit of every x fragment
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, XF ? 0 : M * ldx * 2);
+  uint32_t xo[MT];                                 // direct reads: byte offset of this lane's x row, k = 32h
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) xo[mt] = (uint32_t)(((int64_t)(32 * mt + r) * ldx + 32 * h) * 2);
 
@@ -366,7 +396,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *_
       for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int s = 0; s < 4; s++)
-          b.xv[i][mt][s] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo[mt] + (uint32_t)(tc * 128 + 16 * s), 0, 0);
+          b.xv[i][mt][s] = XF ? *reinterpret_cast<const u32x4_t *>(xl + (((tc * 4 + s) * MT + mt) << 10))
+                              : __builtin_amdgcn_raw_buffer_load_b128(rx, xo[mt] + (uint32_t)(tc * 128 + 16 * s), 0, 0);
     }
   };
   f32x16_t acc[MT];
@@ -860,7 +891,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0) return 0;
   w4a16::Plan p = w4a16::make_plan(M, N, K);
-  return w4a16::workspace_for(p, M, N);
+  return w4a16::workspace_for(p, M, N, K);
 }
 
 }  // namespace nvfp4
@@ -881,7 +912,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   nvfp4_status st = device_info(&di);
   if (st != NVFP4_OK) return st;
   const w4a16::Plan plan = w4a16::make_plan(M, N, K);
-  const size_t need = w4a16::workspace_for(plan, M, N);
+  const size_t need = w4a16::workspace_for(plan, M, N, K);
   if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
@@ -933,13 +964,23 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
       hipLaunchKernelGGL(w4a16::big::big_kernel<2>, dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);
   } else if (plan.kind == 3) {
     if (plan.grid_x > 0x7FFFFFFF || M * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
+    const int MT = M <= 32 ? 1 : 2;
+    const bool xf_path = M > w4a16::kSkinnyDirectMaxM;
+    uint8_t *xf = static_cast<uint8_t *>(ws);
+    if (xf_path) {
+      const int64_t units = K / 64 * 4 * MT * 64;
+      hipLaunchKernelGGL(w4a16::tile_x_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, x, ldx, M, K,
+                         MT, reinterpret_cast<u32x4_t *>(xf));
+      NVFP4_LAUNCH_CHECK();
+    }
     const unsigned grid = (unsigned)plan.grid_x, threads = w4a16::kSkWaves * 64;
-    if (M <= 32)
-      hipLaunchKernelGGL(w4a16::skinny_kernel<1>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
-                         alpha_dev, y, ldy);
-    else
-      hipLaunchKernelGGL(w4a16::skinny_kernel<2>, dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, alpha,
-                         alpha_dev, y, ldy);
+#define NVFP4_SKINNY(MTV, XFV)                                                                                  \
+  hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV>), dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, \
+                     alpha, alpha_dev, y, ldy, xf)
+    if (!xf_path) NVFP4_SKINNY(1, false);
+    else if (MT == 1) NVFP4_SKINNY(1, true);
+    else NVFP4_SKINNY(2, true);
+#undef NVFP4_SKINNY
   } else {
     const int64_t tiles_n = (N + w4a16::BN - 1) / w4a16::BN;
     if (plan.grid_x > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
