@@ -3,10 +3,12 @@
 
 Step = one W4A4 NVFP4 GEMM D = alpha (A.SFA)(B.SFB)^T at M = N = K = 8192 with
 BF16 output: A and B are BF16 N(0,1) tensors quantized on the device by the
-library's quantizer, B prepared once (untimed), all inputs resident in HBM
-when the timed region starts. `value` is TFLOP/s (2 M N K per step). One
-step is one nvfp4_gemm_w4a4 call: the copy of A into the tile layout (in the
-workspace) and the GEMM kernel. The default 50 warm-up steps (about 45 ms)
+library's quantizer, A straight into the layout the GEMM reads
+(nvfp4_quantize_tiled) and B prepared once (both untimed), all inputs resident
+in HBM when the timed region starts. One step is one nvfp4_gemm_w4a4_tiled
+call, the GEMM kernel. `value` is TFLOP/s (2 M N K per step). The same GEMM
+on a row-major A (nvfp4_gemm_w4a4: a tile copy of A, then the GEMM) is timed
+too and reported in `config`. The default 50 warm-up steps (about 40 ms)
 bring the chip to its steady clock under this load; the first ~25 calls after
 idle run up to 10 % slower while the clock ramps.
 
@@ -14,7 +16,7 @@ Extra figures in the same JSON line: W4A16 decode (M = 1) achieved HBM GB/s on
 the 27B-class layer shapes with weights rotated over >= 1 GiB (CUDA-graph
 replay), the prefill W4A4 with on-device activation quantization, and the
 other square sizes. `roofline` describes the dominant kernel, the W4A4 GEMM
-kernel, timed alone (nvfp4_gemm_w4a4_tiled on an A tiled beforehand);
+kernel (the whole step);
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-extras] [--no-cpu-baseline]
@@ -62,38 +64,41 @@ def time_calls(fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
-def quantized_square(nv, S, operand, gen):
-    """Device NVFP4 operand quantized by the library from the seeded BF16 tensor."""
+def quantized_square(nv, S, operand, gen, tiled=False):
+    """Device NVFP4 operand quantized by the library from the seeded BF16 tensor: (codes, scales,
+    g, inv_g), or (activation in the tile layout, g, inv_g) with tiled=True."""
     import torch
-    import synth
     x = gen(S, operand)
     if isinstance(x, tuple):
         x = x[0]
     xd = torch.from_numpy(x).cuda().view(torch.bfloat16)
-    codes, scales, g, inv_g = nv.nvfp4_quantize(xd)
+    res = nv.nvfp4_quantize_tiled(xd) if tiled else nv.nvfp4_quantize(xd)
     del xd
-    return codes, scales, g, inv_g
+    return res
 
 
-def w4a4_square(nv, S, steps, warmup, gen=None, kernel_only=False):
+def w4a4_square(nv, S, steps, warmup, gen=None, standard_too=False):
+    """Step = the W4A4 GEMM on A as the quantizer emits it for the GEMM (the tile layout,
+    nvfp4_quantize_tiled) and B prepared once: nvfp4_gemm_w4a4_tiled. With standard_too, also
+    time nvfp4_gemm_w4a4 on A in the row-major layout (the tile copy + the same GEMM)."""
     import numpy as np
     import torch
     import synth
     gen = gen or synth.square_normal
-    ca, sa, gA, _ = quantized_square(nv, S, "A", gen)
+    at, gA, _ = quantized_square(nv, S, "A", gen, tiled=True)
     cb, sb, gB, _ = quantized_square(nv, S, "B", gen)
     wp, _ = nv.nvfp4_prepare_weight(cb, sb, "ue4m3")
     del cb, sb
     alpha = float(np.float32(1.0) / np.float32(np.float32(gA.item()) * np.float32(gB.item())))
     out = torch.empty((S, S), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(nv.workspace_bytes(nv.OP_W4A4, S, S, S), dtype=torch.uint8, device="cuda")
-    ms = time_calls(lambda: nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, alpha, None, "bf16", out, ws), steps, warmup)
-    if not kernel_only:
+    ms = time_calls(lambda: nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, alpha, None, "bf16", out), steps, warmup)
+    if not standard_too:
         return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12
-    # the GEMM kernel alone, on A already tiled (the call above = tile copy + this)
-    at = nv.nvfp4_tile_activation(ca, sa)
-    ms_k = time_calls(lambda: nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, alpha, None, "bf16", out), steps, warmup)
-    return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12, ms_k
+    del at
+    ca, sa, _, _ = quantized_square(nv, S, "A", gen)
+    ws = torch.empty(nv.workspace_bytes(nv.OP_W4A4, S, S, S), dtype=torch.uint8, device="cuda")
+    ms_std = time_calls(lambda: nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, alpha, None, "bf16", out, ws), steps, warmup)
+    return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12, ms_std
 
 
 def w4a16_m1(nv, j, reps=3):
@@ -194,6 +199,7 @@ def prefill(nv, steps, warmup):
     M, K = x.shape
     N = synth.PREFILL_W[0]
     alpha_w = float(np.float32(1.0) / np.float32(gW.item()))
+    at = torch.empty(nv.lib().nvfp4_tiled_activation_bytes(M, K), dtype=torch.uint8, device="cuda")
     codes = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
     scales = torch.empty((M, K // 16), dtype=torch.uint8, device="cuda")
     g = torch.empty(1, dtype=torch.float32, device="cuda")
@@ -201,14 +207,30 @@ def prefill(nv, steps, warmup):
     qws = torch.empty(nv.workspace_bytes(nv.OP_QUANTIZE, M, 0, K), dtype=torch.uint8, device="cuda")
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     gws = torch.empty(nv.workspace_bytes(nv.OP_W4A4, M, N, K), dtype=torch.uint8, device="cuda")
-    q_ms = time_calls(lambda: nv.nvfp4_quantize(xd, codes, scales, g, ig, qws), steps, warmup)
-    g_ms = time_calls(lambda: nv.nvfp4_gemm_w4a4(codes, scales, wp, N, K, alpha_w, ig, "bf16", out, gws), steps,
-                      warmup)
+
+    def quant():
+        nv.nvfp4_quantize_tiled(xd, at, g, ig, qws)
+
+    def gemm():
+        nv.nvfp4_gemm_w4a4_tiled(at, M, wp, N, K, alpha_w, ig, "bf16", out)
+
+    def step():
+        quant()
+        gemm()
+
+    def step_row_major():
+        nv.nvfp4_quantize(xd, codes, scales, g, ig, qws)
+        nv.nvfp4_gemm_w4a4(codes, scales, wp, N, K, alpha_w, ig, "bf16", out, gws)
+    q_ms = time_calls(quant, steps, warmup)
+    g_ms = time_calls(gemm, steps, warmup)
+    t_ms = time_calls(step, steps, warmup)
+    r_ms = time_calls(step_row_major, steps, warmup)
     q_bytes = M * K * 2 + M * K // 2 + M * K // 16
     return dict(M=M, N=N, K=K, quantize_us=round(q_ms * 1e3, 1),
                 quantize_GBps=round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                 gemm_ms=round(g_ms, 4), gemm_TFLOPs=round(2.0 * M * N * K / (g_ms * 1e-3) / 1e12, 1),
-                total_ms=round(q_ms + g_ms, 4))
+                total_ms=round(t_ms, 4), total_TFLOPs=round(2.0 * M * N * K / (t_ms * 1e-3) / 1e12, 1),
+                row_major_path_ms=round(r_ms, 4))
 
 
 def cpu_baseline(S=8192, rows=2048, cols=8192):
@@ -273,10 +295,10 @@ def main():
         return
     S = args.size
     log(f"[bench] W4A4 {S}^3 bf16: {args.warmup} warmup + {args.steps} timed steps")
-    ms, tflops, ms_k = w4a4_square(nv, S, args.steps, args.warmup, kernel_only=True)
-    k_tflops = 2.0 * S ** 3 / (ms_k * 1e-3) / 1e12
-    log(f"[bench] W4A4 {S}^3: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s; GEMM kernel alone {ms_k:.4f} ms, "
-        f"{k_tflops:.1f} TFLOP/s")
+    ms, tflops, ms_std = w4a4_square(nv, S, args.steps, args.warmup, standard_too=True)
+    std_tflops = 2.0 * S ** 3 / (ms_std * 1e-3) / 1e12
+    log(f"[bench] W4A4 {S}^3: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s (A from nvfp4_quantize_tiled); "
+        f"row-major A through nvfp4_gemm_w4a4 (tile copy + GEMM): {ms_std:.4f} ms, {std_tflops:.1f} TFLOP/s")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -292,10 +314,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"W4A4 NVFP4 GEMM M=N=K={S}, A and B quantized on device from BF16 N(0,1) "
                                f"(per-16 E4M3 scale amax/6, per-tensor global scale), alpha=1/(gA gB), BF16 out",
-                   "M": S, "N": S, "K": S, "out": "bf16"},
-        "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "gemm_kernel (nvfp4_gemm_w4a4_tiled)", "kernel_ms": round(ms_k, 5)},
+                   "M": S, "N": S, "K": S, "out": "bf16",
+                   "a_layout": "tile layout emitted by nvfp4_quantize_tiled (untimed, like B's prepare)",
+                   "row_major_a_call_ms": round(ms_std, 5)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_kernel (the whole step)"},
     }
     if not args.no_extras:
         import synth

@@ -157,6 +157,15 @@ nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_p
 nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales,
                             float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes, void *stream);
 
+/* nvfp4_quantize writing its codes and scales straight into the activation tile
+ * layout of nvfp4_tile_activation (a_tiled: nvfp4_tiled_activation_bytes(rows,
+ * K) bytes, 16-byte aligned; rows rounded up to 32, the padding rows zero), so
+ * a quantized activation feeds nvfp4_gemm_w4a4_tiled with no copy. The same
+ * bytes as nvfp4_tile_activation applied to nvfp4_quantize's output.
+ * K % 64 == 0; other arguments as for nvfp4_quantize. */
+nvfp4_status nvfp4_quantize_tiled(const uint16_t *x, int64_t rows, int64_t K, uint8_t *a_tiled, float *g_dev,
+                                  float *inv_g_dev, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

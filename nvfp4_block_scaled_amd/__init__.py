@@ -43,6 +43,7 @@ _SIGS = [
     ("nvfp4_gemm_w4a16", ctypes.c_int,
      [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _I64, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("nvfp4_quantize_tiled", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 ]
 EXPORTED = [s[0] for s in _SIGS]
 
@@ -262,3 +263,27 @@ def nvfp4_quantize(x, codes=None, scales=None, g=None, inv_g=None, ws=None):
     _check(lib().nvfp4_quantize(_ptr(x), rows, K, _ptr(codes), _ptr(scales), _ptr(g), _ptr(inv_g), _ptr(ws),
                                 ws.numel(), _stream()))
     return codes, scales, g, inv_g
+
+
+def nvfp4_quantize_tiled(x, out=None, g=None, inv_g=None, ws=None):
+    """BF16 [rows][K] -> (activation in the tile layout (uint8), g, inv_g): nvfp4_quantize with its
+    output written straight into the layout nvfp4_gemm_w4a4_tiled reads."""
+    x = _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    rows, K = x.shape
+    dev = x.device
+    n = int(lib().nvfp4_tiled_activation_bytes(rows, K))
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=dev)
+    elif out.dtype != torch.uint8 or out.numel() < n:
+        raise ValueError("out must hold nvfp4_tiled_activation_bytes(rows, K) uint8")
+    if g is None:
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    if inv_g is None:
+        inv_g = torch.empty(1, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(OP_QUANTIZE, rows, 0, K), dtype=torch.uint8, device=dev)
+    _check(lib().nvfp4_quantize_tiled(_ptr(x), rows, K, _ptr(out), _ptr(g), _ptr(inv_g), _ptr(ws), ws.numel(),
+                                      _stream()))
+    return out, g, inv_g

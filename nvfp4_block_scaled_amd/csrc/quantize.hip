@@ -86,7 +86,13 @@ __device__ __forceinline__ float e4m3_value(uint32_t s) {
 // 2.5 -> 4, 3.5 -> 6, 5 -> 6); saturates at 7 (6.0); NaN gives 0.
 // Pass 2: one thread per 16-element block, grid-striding. Every workgroup first
 // reduces the pass-1 maxima (a few KB) to the tensor maximum and forms g.
+//
+// TILED: codes and scales go straight into the prepared tile layout of the
+// activation (see nvfp4_tile_activation) at `codes`, for rows rounded up to 32
+// (nblocks_out blocks; the blocks of the padding rows are written as zero).
+template <bool TILED>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *__restrict__ x, int64_t nblocks,
+                                                            int64_t nblocks_out, int64_t K,
                                                             const uint32_t *__restrict__ partial, int npartial,
                                                             u32x2_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                             float *__restrict__ g_out, float *__restrict__ inv_g_out) {
@@ -100,10 +106,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *__res
     g_out[0] = g;
     if (inv_g_out) inv_g_out[0] = 1.0f / g;
   }
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks_out;
        blk += (int64_t)gridDim.x * kThreads) {
-    const u32x4_t v0 = x[2 * blk];
-    const u32x4_t v1 = x[2 * blk + 1];
+    const bool real = blk < nblocks;
+    const u32x4_t v0 = real ? x[2 * blk] : u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t v1 = real ? x[2 * blk + 1] : u32x4_t{0u, 0u, 0u, 0u};
     const uint32_t amax_bits = max(absmax8(v0), absmax8(v1));
     uint32_t sbyte = 0;
     if (amax_bits != 0) {
@@ -131,8 +138,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *__res
       NVFP4_CVT_BYTE(1, 0); NVFP4_CVT_BYTE(1, 1); NVFP4_CVT_BYTE(1, 2); NVFP4_CVT_BYTE(1, 3);
 #undef NVFP4_CVT_BYTE
     }
-    codes[blk] = out;
-    scales[blk] = (uint8_t)sbyte;
+    if (TILED) {
+      // block b of row `row` -> tile (row / 32, b / 4), unit 32 ((b % 4) / 2) + row % 32, half b % 2
+      const int64_t nb = K / 16, kt = K / 64;
+      const int64_t row = blk / nb, b = blk - row * nb;
+      const int64_t tile = (row >> 5) * kt + (b >> 2);
+      const int64_t rr = row & 31;
+      uint8_t *base = reinterpret_cast<uint8_t *>(codes);
+      *reinterpret_cast<u32x2_t *>(base + tile * 1024 + 16 * (32 * ((b & 3) >> 1) + rr) + 8 * (b & 1)) = out;
+      base[nblocks_out * 8 + tile * 128 + rr * 4 + (b & 3)] = (uint8_t)sbyte;
+    } else {
+      codes[blk] = out;
+      scales[blk] = (uint8_t)sbyte;
+    }
   }
 }
 
@@ -140,30 +158,54 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *__res
 
 using namespace nvfp4;
 
-extern "C" nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales,
-                                       float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes, void *stream) {
-  if (!g_dev) return NVFP4_ERR_NULL;
-  if (rows < 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (rows > 0 && (!x || !codes || !scales)) return NVFP4_ERR_NULL;
+namespace {
+
+nvfp4_status quantize_common(const uint16_t *x, int64_t rows, int64_t K, bool tiled, void *codes, uint8_t *scales,
+                             float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes, hipStream_t s) {
   if (!ws) return NVFP4_ERR_WORKSPACE;
   if (ws_bytes < quantize_workspace_bytes(rows, K)) return NVFP4_ERR_WORKSPACE;
-  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(ws, 4) || !aligned(g_dev, 4) ||
+  if (!aligned(x, 16) || !aligned(codes, tiled ? 16 : 8) || !aligned(ws, 4) || !aligned(g_dev, 4) ||
       (inv_g_dev && !aligned(inv_g_dev, 4)))
     return NVFP4_ERR_ALIGN;
   DeviceInfo d;
   nvfp4_status st = device_info(&d);
   if (st != NVFP4_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
   const int64_t n16 = rows * K / 8;          // 16-byte chunks of x
   const int64_t nblocks = rows * K / 16;     // 16-element blocks
+  const int64_t nblocks_out = tiled ? (rows + 31) / 32 * 32 * K / 16 : nblocks;
   hipLaunchKernelGGL(amax_kernel, dim3(kAmaxBlocks), dim3(kThreads), 0, s, (const u32x4_t *)x, n16,
                      (uint32_t *)ws);
   NVFP4_LAUNCH_CHECK();
-  int64_t grid = (nblocks + kThreads - 1) / kThreads;
+  int64_t grid = (nblocks_out + kThreads - 1) / kThreads;
   if (grid > 8 * (int64_t)d.num_cus) grid = 8 * (int64_t)d.num_cus;   // the maxima are reduced once per workgroup
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x, nblocks,
-                     (const uint32_t *)ws, kAmaxBlocks, (u32x2_t *)codes, scales, g_dev, inv_g_dev);
+  if (tiled)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x, nblocks,
+                       nblocks_out, K, (const uint32_t *)ws, kAmaxBlocks, (u32x2_t *)codes, nullptr, g_dev,
+                       inv_g_dev);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x,
+                       nblocks, nblocks_out, K, (const uint32_t *)ws, kAmaxBlocks, (u32x2_t *)codes, scales, g_dev,
+                       inv_g_dev);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales,
+                                       float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes, void *stream) {
+  if (!g_dev) return NVFP4_ERR_NULL;
+  if (rows < 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && (!x || !codes || !scales)) return NVFP4_ERR_NULL;
+  return quantize_common(x, rows, K, false, codes, scales, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" nvfp4_status nvfp4_quantize_tiled(const uint16_t *x, int64_t rows, int64_t K, uint8_t *a_tiled,
+                                             float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes,
+                                             void *stream) {
+  if (!g_dev) return NVFP4_ERR_NULL;
+  if (rows < 0 || K <= 0 || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && (!x || !a_tiled)) return NVFP4_ERR_NULL;
+  return quantize_common(x, rows, K, true, a_tiled, nullptr, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
 }

@@ -100,6 +100,16 @@ def test_tile_activation_and_tiled_gemm_argument_checks():
     assert call(d=ODD) == nv.ERR_ALIGN
 
 
+def test_quantize_tiled_argument_checks():
+    q = nv.lib().nvfp4_quantize_tiled
+    assert q(FAKE, 64, 128, FAKE, None, None, FAKE, 4096, None) == nv.ERR_NULL      # g_dev
+    assert q(FAKE, 64, 96, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_SHAPE      # K % 64
+    assert q(FAKE, -1, 128, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_SHAPE
+    assert q(None, 64, 128, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_NULL
+    assert q(FAKE, 64, 128, FAKE, FAKE, None, None, 0, None) == nv.ERR_WORKSPACE
+    assert q(FAKE, 64, 128, ODD, FAKE, None, FAKE, 4096, None) == nv.ERR_ALIGN
+
+
 def test_gemm_w4a16_argument_checks():
     f = nv.lib().nvfp4_gemm_w4a16
 

@@ -108,6 +108,26 @@ def test_quantize_all_bf16_patterns():
     np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
 
 
+@pytest.mark.parametrize("rows,K", [(77, 320), (256, 5120), (1, 64)])
+def test_quantize_tiled_matches_quantize_then_tile(rows, K):
+    x = synth.normal_bf16(rows * 7 + K, rows, K)
+    xd = dev(x).view(torch.bfloat16)
+    at, g, ig = nv.nvfp4_quantize_tiled(xd)
+    codes, scales, g2, ig2 = nv.nvfp4_quantize(xd)
+    ref_t = nv.nvfp4_tile_activation(codes, scales)
+    torch.cuda.synchronize()
+    assert torch.equal(at, ref_t)
+    assert g.item() == g2.item() and ig.item() == ig2.item()
+    # and against the oracle: quantizer bytes in the prepared index map, padding rows zero
+    c_ref, s_ref, _, _ = quantize.quantize(x)
+    Mp = -(-rows // 32) * 32
+    cp = np.zeros((Mp, K // 2), np.uint8)
+    sp = np.zeros((Mp, K // 16), np.uint8)
+    cp[:rows], sp[:rows] = c_ref, s_ref
+    ref, _ = prepared.prepare_weight(cp, sp, "ue4m3")
+    assert np.array_equal(host(at), ref)
+
+
 def test_quantize_prefill_activation_full():
     x, _ = synth.prefill_activation()
     codes, scales, g, inv_g = nv.nvfp4_quantize(dev(x).view(torch.bfloat16))
