@@ -81,22 +81,45 @@ __device__ __forceinline__ float e4m3_value(uint32_t s) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));          // 2^(e-7) * (1 + m/8)
 }
 
-// E2M1 magnitude code of v >= 0: the number of rounding thresholds v passes,
-// with ties sent to the even code (0.25 -> 0, 0.75 -> 2, 1.25 -> 2, 1.75 -> 4,
-// 2.5 -> 4, 3.5 -> 6, 5 -> 6); saturates at 7 (6.0); NaN gives 0.
-// Pass 2: one thread per 16-element block, grid-striding. Every workgroup first
-// reduces the pass-1 maxima (a few KB) to the tensor maximum and forms g.
-//
-// TILED: codes and scales go straight into the prepared tile layout of the
-// activation (see nvfp4_tile_activation) at `codes`, for rows rounded up to 32
-// (nblocks_out blocks; the blocks of the padding rows are written as zero).
-template <bool TILED>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *__restrict__ x, int64_t nblocks,
-                                                            int64_t nblocks_out, int64_t K,
-                                                            const uint32_t *__restrict__ partial, int npartial,
-                                                            u32x2_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                                            float *__restrict__ g_out, float *__restrict__ inv_g_out) {
-  __shared__ uint32_t red[kThreads / 64 + 1];
+// One 16-element block (two 16-byte chunks of BF16) under the global scale g:
+// the scale byte (E4M3 of amax_b / 6 * g, 0 for an all-zero block) in *sbyte
+// and the eight code bytes, element 2i in the low nibble of byte i.
+__device__ __forceinline__ u32x2_t quantize_block(const u32x4_t v0, const u32x4_t v1, float g, uint32_t *sbyte) {
+  const uint32_t amax_bits = max(absmax8(v0), absmax8(v1));
+  uint32_t sb = 0;
+  if (amax_bits != 0) {
+    const float amax_b = __uint_as_float(amax_bits << 16);
+    const float t = amax_b / 6.0f;
+    const float u = t * g;
+    sb = e4m3_rne_sat(u);
+  }
+  *sbyte = sb;
+  u32x2_t out = {0u, 0u};
+  if (sb != 0) {
+    const float s = e4m3_value(sb);
+    const float r = g / s;
+    uint32_t words[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      words[i] = v0[i];
+      words[4 + i] = v1[i];
+    }
+    // two BF16 elements per word, element 2i in the low half -> low nibble of byte i
+#define NVFP4_CVT_BYTE(D, B)                                                                             \
+  out[D] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[D], __uint_as_float(words[4 * D + B] << 16) * r,  \
+                                                    __uint_as_float(words[4 * D + B] & 0xFFFF0000u) * r, \
+                                                    1.0f, B)
+    NVFP4_CVT_BYTE(0, 0); NVFP4_CVT_BYTE(0, 1); NVFP4_CVT_BYTE(0, 2); NVFP4_CVT_BYTE(0, 3);
+    NVFP4_CVT_BYTE(1, 0); NVFP4_CVT_BYTE(1, 1); NVFP4_CVT_BYTE(1, 2); NVFP4_CVT_BYTE(1, 3);
+#undef NVFP4_CVT_BYTE
+  }
+  return out;
+}
+
+// Every workgroup of pass 2 first reduces the pass-1 maxima (a few KB) to the
+// tensor maximum and forms g (block 0 stores g and 1/g).
+__device__ __forceinline__ float global_scale(const uint32_t *__restrict__ partial, int npartial, uint32_t *red,
+                                              float *__restrict__ g_out, float *__restrict__ inv_g_out) {
   uint32_t m = 0;
   for (int i = threadIdx.x; i < npartial; i += kThreads) m = max(m, partial[i]);
   m = block_max_u32(m, red);
@@ -106,51 +129,57 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *__res
     g_out[0] = g;
     if (inv_g_out) inv_g_out[0] = 1.0f / g;
   }
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks_out;
+  return g;
+}
+
+// Pass 2, row-major output: one thread per 16-element block, grid-striding.
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *__restrict__ x, int64_t nblocks,
+                                                            const uint32_t *__restrict__ partial, int npartial,
+                                                            u32x2_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                            float *__restrict__ g_out, float *__restrict__ inv_g_out) {
+  __shared__ uint32_t red[kThreads / 64 + 1];
+  const float g = global_scale(partial, npartial, red, g_out, inv_g_out);
+  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
        blk += (int64_t)gridDim.x * kThreads) {
-    const bool real = blk < nblocks;
-    const u32x4_t v0 = real ? x[2 * blk] : u32x4_t{0u, 0u, 0u, 0u};
-    const u32x4_t v1 = real ? x[2 * blk + 1] : u32x4_t{0u, 0u, 0u, 0u};
-    const uint32_t amax_bits = max(absmax8(v0), absmax8(v1));
-    uint32_t sbyte = 0;
-    if (amax_bits != 0) {
-      const float amax_b = __uint_as_float(amax_bits << 16);
-      const float t = amax_b / 6.0f;
-      const float u = t * g;
-      sbyte = e4m3_rne_sat(u);
-    }
-    u32x2_t out = {0u, 0u};
-    if (sbyte != 0) {
-      const float s = e4m3_value(sbyte);
-      const float r = g / s;
-      uint32_t words[8];
+    uint32_t sbyte;
+    codes[blk] = quantize_block(x[2 * blk], x[2 * blk + 1], g, &sbyte);
+    scales[blk] = (uint8_t)sbyte;
+  }
+}
+
+// Pass 2, tile-layout output (the layout nvfp4_tile_activation writes): one
+// wave per tile of 32 rows x 64 K, grid-striding over the tiles in their
+// storage order. Lane 32 h + r quantizes blocks 2h and 2h+1 of the tile's row
+// r; its 16 code bytes are unit 32 h + r of the tile's 1 KiB of codes and its
+// two scale bytes sit at 4 r + 2h of the tile's 128 scale bytes, so a wave
+// stores 1 KiB and 128 B contiguously. Rows from `rows` up to the next
+// multiple of 32 read as zero and are written as zero.
+__global__ __launch_bounds__(kThreads) void quantize_tiled_kernel(const u32x4_t *__restrict__ x, int64_t rows,
+                                                                  int64_t K, int64_t ntiles,
+                                                                  const uint32_t *__restrict__ partial, int npartial,
+                                                                  uint8_t *__restrict__ out, float *__restrict__ g_out,
+                                                                  float *__restrict__ inv_g_out) {
+  __shared__ uint32_t red[kThreads / 64 + 1];
+  const float g = global_scale(partial, npartial, red, g_out, inv_g_out);
+  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+  const int64_t kt = K / 64, x_row = K / 8;          // tiles along K; 16-byte chunks per row of x
+  u32x4_t *const code_out = reinterpret_cast<u32x4_t *>(out);
+  uint16_t *const scale_out = reinterpret_cast<uint16_t *>(out + ntiles * 1024);
+  const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t tile = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile < ntiles; tile += wstride) {
+    const int64_t rg = tile / kt, kk = tile - rg * kt;
+    const int64_t row = rg * 32 + r;
+    u32x4_t v[4] = {};
+    if (row < rows) {
+      const u32x4_t *src = x + row * x_row + kk * 8 + h * 4;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        words[i] = v0[i];
-        words[4 + i] = v1[i];
-      }
-      // two BF16 elements per word, element 2i in the low half -> low nibble of byte i
-#define NVFP4_CVT_BYTE(D, B)                                                                             \
-  out[D] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[D], __uint_as_float(words[4 * D + B] << 16) * r,  \
-                                                    __uint_as_float(words[4 * D + B] & 0xFFFF0000u) * r, \
-                                                    1.0f, B)
-      NVFP4_CVT_BYTE(0, 0); NVFP4_CVT_BYTE(0, 1); NVFP4_CVT_BYTE(0, 2); NVFP4_CVT_BYTE(0, 3);
-      NVFP4_CVT_BYTE(1, 0); NVFP4_CVT_BYTE(1, 1); NVFP4_CVT_BYTE(1, 2); NVFP4_CVT_BYTE(1, 3);
-#undef NVFP4_CVT_BYTE
+      for (int i = 0; i < 4; i++) v[i] = src[i];
     }
-    if (TILED) {
-      // block b of row `row` -> tile (row / 32, b / 4), unit 32 ((b % 4) / 2) + row % 32, half b % 2
-      const int64_t nb = K / 16, kt = K / 64;
-      const int64_t row = blk / nb, b = blk - row * nb;
-      const int64_t tile = (row >> 5) * kt + (b >> 2);
-      const int64_t rr = row & 31;
-      uint8_t *base = reinterpret_cast<uint8_t *>(codes);
-      *reinterpret_cast<u32x2_t *>(base + tile * 1024 + 16 * (32 * ((b & 3) >> 1) + rr) + 8 * (b & 1)) = out;
-      base[nblocks_out * 8 + tile * 128 + rr * 4 + (b & 3)] = (uint8_t)sbyte;
-    } else {
-      codes[blk] = out;
-      scales[blk] = (uint8_t)sbyte;
-    }
+    uint32_t s0, s1;
+    const u32x2_t c0 = quantize_block(v[0], v[1], g, &s0);
+    const u32x2_t c1 = quantize_block(v[2], v[3], g, &s1);
+    code_out[tile * 64 + lane] = u32x4_t{c0[0], c0[1], c1[0], c1[1]};
+    scale_out[tile * 64 + 2 * r + h] = (uint16_t)(s0 | (s1 << 8));
   }
 }
 
@@ -172,21 +201,21 @@ nvfp4_status quantize_common(const uint16_t *x, int64_t rows, int64_t K, bool ti
   if (st != NVFP4_OK) return st;
   const int64_t n16 = rows * K / 8;          // 16-byte chunks of x
   const int64_t nblocks = rows * K / 16;     // 16-element blocks
-  const int64_t nblocks_out = tiled ? (rows + 31) / 32 * 32 * K / 16 : nblocks;
   hipLaunchKernelGGL(amax_kernel, dim3(kAmaxBlocks), dim3(kThreads), 0, s, (const u32x4_t *)x, n16,
                      (uint32_t *)ws);
   NVFP4_LAUNCH_CHECK();
-  int64_t grid = (nblocks_out + kThreads - 1) / kThreads;
-  if (grid > 8 * (int64_t)d.num_cus) grid = 8 * (int64_t)d.num_cus;   // the maxima are reduced once per workgroup
-  if (grid < 1) grid = 1;
-  if (tiled)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x, nblocks,
-                       nblocks_out, K, (const uint32_t *)ws, kAmaxBlocks, (u32x2_t *)codes, nullptr, g_dev,
-                       inv_g_dev);
-  else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x,
-                       nblocks, nblocks_out, K, (const uint32_t *)ws, kAmaxBlocks, (u32x2_t *)codes, scales, g_dev,
-                       inv_g_dev);
+  // every workgroup reduces the pass-1 maxima once, so the grid is capped
+  const int64_t max_grid = 8 * (int64_t)d.num_cus;
+  if (tiled) {
+    const int64_t ntiles = (rows + 31) / 32 * (K / 64);
+    const int64_t grid = std::max<int64_t>(1, std::min(max_grid, (ntiles + kThreads / 64 - 1) / (kThreads / 64)));
+    hipLaunchKernelGGL(quantize_tiled_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x, rows, K,
+                       ntiles, (const uint32_t *)ws, kAmaxBlocks, (uint8_t *)codes, g_dev, inv_g_dev);
+  } else {
+    const int64_t grid = std::max<int64_t>(1, std::min(max_grid, (nblocks + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x, nblocks,
+                       (const uint32_t *)ws, kAmaxBlocks, (u32x2_t *)codes, scales, g_dev, inv_g_dev);
+  }
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }
