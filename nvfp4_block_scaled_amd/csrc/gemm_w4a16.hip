@@ -1,22 +1,21 @@
 // W4A16 NVFP4 GEMM for gfx950: y = alpha * x (W.SFW)^T, x/y BF16, FP32 accumulation.
 //
 // Kernels, chosen by M (and, for decode, by the number of 32-row groups):
-//  * M <= 4 (decode): a weight-streaming kernel on the vector ALUs. A 1024-thread
-//    workgroup owns 16 weight rows (half of a 32-row prepared tile group) over
-//    the whole K; its 16 waves take interleaved pairs of 64-wide K tiles. Each
-//    lane streams 16 packed bytes (32 codes of one row) per tile, converts code
-//    pairs to exact unscaled BF16 (cvt_scalef32_pk_bf16_fp4), dots them with x
-//    in FP32 (v_dot2_f32_bf16) and multiplies each 16-block's partial sum by
-//    its scale once: about 1.1 vector instructions per weight at M = 1, so the
-//    kernel is bound by HBM. The K-split is reduced inside the workgroup (lane
-//    butterflies, then LDS over the waves in wave order), so no workgroup ever
-//    waits on another and nothing crosses an XCD within the kernel. x is staged
-//    once per workgroup in LDS and read by broadcast. With at least two 32-row
-//    groups per CU, a wide variant is used instead: one 512-thread workgroup
-//    per whole group, each wave keeping four 1 KB tile loads in flight (two
-//    batches of two); all its workgroups are resident at once. (A K split
-//    across workgroups would need an agent-scope release per workgroup, an L2
-//    write-back on this part, which measured several times slower.)
+//  * M <= 4 (decode): a weight-streaming kernel on the vector ALUs. A workgroup
+//    owns one 32-row prepared tile group over the whole K; its waves (12, or 8
+//    once there are two groups per CU) take interleaved 64-wide K tiles, one
+//    contiguous 1 KB tile per wave load. Each lane streams 16 packed bytes (32
+//    codes of one row) per tile, converts code pairs to exact unscaled BF16
+//    (cvt_scalef32_pk_bf16_fp4), dots them with x in FP32 (v_dot2_f32_bf16)
+//    and multiplies each 16-block's partial sum by its scale once: about 1.3
+//    vector instructions per weight at M = 1. The loads are range-checked
+//    buffer loads issued unconditionally two batches ahead, so a wave waits
+//    only for the batch it is about to use. The K-split is reduced inside the
+//    workgroup (lane butterfly, then LDS over the waves in wave order), so no
+//    workgroup ever waits on another and nothing crosses an XCD within the
+//    kernel. x is staged once per workgroup in LDS and read by broadcast. (A K
+//    split across workgroups would need an agent-scope release per workgroup,
+//    an L2 write-back on this part, which measured several times slower.)
 //  * 4 < M <= 64 (and M <= 4 when x does not fit in LDS): the skinny MFMA
 //    kernel, the decode structure with v_mfma_f32_32x32x16_bf16 on one or two
 //    32-row x tiles (below).
@@ -38,20 +37,34 @@ namespace w4a16 {
 
 constexpr int kThreads = 256;
 
+// Buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc16(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)n, 0x00020000);
+}
+constexpr int kNonTemporal = 2;   // cache-policy bits of a streamed load
+
 // ---------------------------------------------------------------- planning
 
 struct Plan {
-  int kind;          // 0 = vector decode kernel, 1 = MFMA tile kernel, 2 = wide vector decode kernel,
-                     // 3 = skinny MFMA kernel, 4 = big MFMA kernel
+  int kind;          // 0 = vector decode kernel, 1 = MFMA tile kernel, 3 = skinny MFMA kernel,
+                     // 4 = big MFMA kernel
   int splits;        // K splits of the tile kernel (1 = none)
+  int dec;           // launch shape of the decode kernel (kDecodeShapes)
   int64_t grid_x;    // workgroups along the output
 };
+
+// Launch shapes of the vector decode kernel: R weight rows per workgroup, W
+// waves, U tile loads per wave and ring batch.
+struct DecodeShape {
+  int R, W, U;
+};
+constexpr DecodeShape kDecodeShapes[] = {{32, 8, 2}, {32, 12, 2}};
 
 constexpr int kDecodeMaxM = 4;
 constexpr int kSkinnyMaxM = 64;
 constexpr int kSkinnyDirectMaxM = 16;   // up to here the skinny kernel reads x rows directly
-constexpr int kDecodeThreads = 1024;      // 16 waves per 16-row group
-constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr int kDecodeLdsBytes = 64 * 1024;  // x staged in LDS: M * K * 2 bytes at most
 constexpr int BM = 256, BN = 128;         // tile kernel
 
@@ -68,16 +81,21 @@ static int64_t big_tiles(int64_t M, int64_t N, int cus) {
   return ((M + bt - 1) / bt) * ((N + bt - 1) / bt);
 }
 
+// One 32-row group per workgroup. Eight waves once there are two groups per
+// CU; with fewer groups, twelve waves keep more loads in flight per CU (more
+// waves or deeper rings, or 8- and 16-row workgroups over more CUs, measured
+// slower on the 27B-class decode shapes).
+static int decode_shape(int64_t N, int cus) { return N / 32 >= 2 * cus ? 0 : 1; }
+
 static Plan make_plan(int64_t M, int64_t N, int64_t K) {
   Plan p{};
   const int cus = num_cus_or_default();
   const int64_t ktiles = K / 64;
   if (M <= kDecodeMaxM && M * K * 2 <= kDecodeLdsBytes) {
-    // one 32-row group per workgroup once there are two groups per CU; below
-    // that, 16-row workgroups with 16 waves keep more of the chip busy
-    p.kind = N / 32 >= 2 * cus ? 2 : 0;
+    p.kind = 0;
     p.splits = 1;
-    p.grid_x = p.kind == 2 ? N / 32 : N / 16;
+    p.dec = decode_shape(N, cus);
+    p.grid_x = N / kDecodeShapes[p.dec].R;
   } else if (M <= kSkinnyMaxM) {
     p.kind = 3;
     p.splits = 1;
@@ -110,138 +128,48 @@ static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
 
 // ---------------------------------------------------------------- decode kernel (M <= 4)
 
-// Workgroup b owns weight rows [16 b, 16 b + 16): rows 16 (b & 1) .. of the
-// 32-row prepared tile group b / 2. Lane (r = lane & 15, q = lane >> 4) of wave
-// w handles row r, tile 2 p + (q >> 1) and K-half (q & 1) of that tile, for the
-// tile pairs p = w, w + 16, w + 32, ...: one wave load reads two contiguous
-// 512-byte half-tiles.
-template <int M>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const uint16_t *__restrict__ x, int64_t ldx,
-                                                                const uint8_t *__restrict__ wp, int64_t N,
-                                                                int64_t K, float alpha, const float *alpha_dev,
-                                                                uint16_t *__restrict__ y, int64_t ldy) {
+// Workgroup b owns the R weight rows R (b % (32/R)) + [0, R) of the 32-row
+// prepared tile group b / (32/R), over the whole K, with W waves. A wave load
+// covers 32/R consecutive tiles: lane l takes tile l / 2R of them, K-half
+// h = (l / R) & 1 and row r = l % R, i.e. unit 32 h + row of the tile, so the
+// load reads 2 (32/R) contiguous runs of 16 R bytes (one 1 KB run for R = 32).
+// Wave w takes the tile groups w, w + W, w + 2W, ...; the loads run U groups
+// per wave ahead in a two-batch register ring (non-temporal: the weights are
+// streamed once), and the first batch is issued before x is staged in LDS. Per 16-element
+// block the BF16 products go through fdot2 into an FP32 partial that is scaled
+// once; the row's lanes are added by a butterfly (the same bits in every lane)
+// and the waves in wave order through LDS.
+template <int M, int R, int W, int U>
+__global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                        const uint8_t *__restrict__ wp, int64_t N, int64_t K,
+                                                        float alpha, const float *alpha_dev,
+                                                        uint16_t *__restrict__ y, int64_t ldy) {
+  constexpr int TPL = 32 / R;                       // tiles per wave load
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];     // [M][K]
-  __shared__ float red[kDecodeWaves][M][16];
+  __shared__ float red[W][M][R];
   const int64_t T = K / 64;
-  for (int64_t u = threadIdx.x; u < M * K / 8; u += kDecodeThreads) {
-    const int64_t m = u / (K / 8), c = u - m * (K / 8);
-    *reinterpret_cast<u32x4_t *>(xs + m * K + c * 8) = *reinterpret_cast<const u32x4_t *>(x + m * ldx + c * 8);
-  }
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 15, q = lane >> 4, th = q >> 1, kh = q & 1;
-  const int64_t ng = blockIdx.x >> 1;
-  const int row = (blockIdx.x & 1) * 16 + r;                 // row inside the 32-row tile
-  const uint8_t *codes = wp + ((ng * T) << 10) + 16 * (32 * kh + row);
-  const uint8_t *scl = wp + N * K / 2 + ((ng * T) << 7) + row * 4;
-  float acc[M];
-#pragma unroll
-  for (int m = 0; m < M; m++) acc[m] = 0.0f;
-  const int64_t pairs = (T + 1) / 2;
-  constexpr int U = 2;  // tile pairs in flight per wave
-  for (int64_t p0 = wave; p0 < pairs; p0 += (int64_t)kDecodeWaves * U) {
-    u32x4_t cw[U];
-    uint32_t sw[U];
-#pragma unroll
-    for (int i = 0; i < U; i++) {
-      const int64_t t = 2 * (p0 + (int64_t)i * kDecodeWaves) + th;
-      if (t < T) {
-        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(codes + (t << 10)));
-        sw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(scl + (t << 7)));
-      } else {
-        cw[i] = u32x4_t{0u, 0u, 0u, 0u};
-        sw[i] = 0u;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < U; i++) {
-      const int64_t t = 2 * (p0 + (int64_t)i * kDecodeWaves) + th;
-      if (t >= T) continue;
-      const f32x2_t sc = e4m3x2_to_f32(sw[i] >> (16 * kh));
-      const uint16_t *xk = xs + t * 64 + 32 * kh;
-#pragma unroll
-      for (int blk = 0; blk < 2; blk++) {
-        float part[M];
-#pragma unroll
-        for (int m = 0; m < M; m++) part[m] = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 2; d++) {
-          const int s = blk * 2 + d;
-          bf16x2_t wv[4];
-          codes8_to_bf16(cw[i][s], wv);
-#pragma unroll
-          for (int m = 0; m < M; m++) {
-            const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xk + m * K + 8 * s);
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              part[m] = __builtin_amdgcn_fdot2_f32_bf16(wv[e], as_bf16x2(xv[e]), part[m], false);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < M; m++) acc[m] = __builtin_fmaf(part[m], sc[blk], acc[m]);
-      }
-    }
-  }
-  // lanes r, r+16, r+32, r+48 hold the four (tile, half) streams of row r:
-  // ((q0 + q1) + (q2 + q3)), the same bits in all four lanes
-#pragma unroll
-  for (int m = 0; m < M; m++) {
-    acc[m] += __shfl_xor(acc[m], 16, 64);
-    acc[m] += __shfl_xor(acc[m], 32, 64);
-  }
-  if (q == 0)
-#pragma unroll
-    for (int m = 0; m < M; m++) red[wave][m][r] = acc[m];
-  __syncthreads();
-  if (threadIdx.x < M * 16) {
-    const int m = threadIdx.x >> 4, rr = threadIdx.x & 15;
-    float v = red[0][m][rr];
-#pragma unroll
-    for (int w = 1; w < kDecodeWaves; w++) v += red[w][m][rr];
-    const float al = load_alpha(alpha, alpha_dev);
-    y[m * ldy + blockIdx.x * 16 + rr] = f32_to_bf16_rne(al * v);
-  }
-}
-
-// Wide decode (many row groups): workgroup g covers the 32-row prepared tile
-// group g (rows 32g .. 32g+31) over the whole K with 8 waves; wave w takes the
-// tiles w, w + 8, w + 16, ...; lane l is unit l of each tile (row r = l & 31,
-// k in [32h, 32h + 32) with h = l >> 5), so one wave load is the tile's
-// contiguous 1 KB. Loads run two tiles per wave ahead in a two-batch register
-// ring (non-temporal: the weights are streamed once); the first batch is issued
-// before x is staged. With at least two groups per CU every workgroup is
-// resident at once, and a group is reduced inside its workgroup.
-constexpr int kWideWaves = 8;
-constexpr int kWideAhead = 2;
-
-template <int M>
-__global__ __launch_bounds__(kWideWaves * 64) void decode_wide_kernel(const uint16_t *__restrict__ x, int64_t ldx,
-                                                                    const uint8_t *__restrict__ wp, int64_t N,
-                                                                    int64_t K, float alpha, const float *alpha_dev,
-                                                                    uint16_t *__restrict__ y, int64_t ldy) {
-  constexpr int W = kWideWaves, U = kWideAhead;
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];     // [M][K]
-  __shared__ float red[W][M][32];
-  const int64_t T = K / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = lane >> 5, r = lane & 31;
-  const int64_t g = blockIdx.x;
-  const uint8_t *cb = wp + ((g * T) << 10) + lane * 16;
-  const uint8_t *sb = wp + N * K / 2 + ((g * T) << 7) + r * 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tl = lane / (2 * R), h = (lane / R) & 1, r = lane % R;
+  const int64_t g = blockIdx.x / TPL;
+  const int row0 = (int)(blockIdx.x % TPL) * R;      // first row of the workgroup inside the group
+  // Every load is unconditional: the resource of tile group j0 + i W starts at
+  // its first tile and ends at the last tile of the row group, so the lanes
+  // past it read zeros, and the waits before a compute step can leave the
+  // next batch in flight.
+  const uint8_t *cbase = wp + ((g * T) << 10);
+  const uint8_t *sbase = wp + N * K / 2 + ((g * T) << 7);
+  const uint32_t oc = 16u * (32 * h + row0 + r) + ((uint32_t)tl << 10), os = 4u * (row0 + r) + ((uint32_t)tl << 7);
+  const int64_t groups = (T + TPL - 1) / TPL;
   u32x4_t cw0[U], cw1[U];
   uint32_t sw0[U], sw1[U];
-  auto issue = [&](u32x4_t (&cw)[U], uint32_t (&sw)[U], int64_t t0) {
+  auto issue = [&](u32x4_t (&cw)[U], uint32_t (&sw)[U], int64_t j0) {
 #pragma unroll
     for (int i = 0; i < U; i++) {
-      const int64_t t = t0 + (int64_t)i * W;
-      if (t < T) {
-        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cb + (t << 10)));
-        sw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + (t << 7)));
-      } else {
-        cw[i] = u32x4_t{0u, 0u, 0u, 0u};
-        sw[i] = 0u;
-      }
+      const int64_t tu = (j0 + (int64_t)i * W) * TPL, rem = T - tu;
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc16(cbase + (tu << 10), rem > 0 ? rem << 10 : 0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc16(sbase + (tu << 7), rem > 0 ? rem << 7 : 0);
+      cw[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, kNonTemporal);
+      sw[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, kNonTemporal);
     }
   };
   issue(cw0, sw0, wave);
@@ -254,59 +182,60 @@ __global__ __launch_bounds__(kWideWaves * 64) void decode_wide_kernel(const uint
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; m++) acc[m] = 0.0f;
-  auto compute = [&](const u32x4_t (&cw)[U], const uint32_t (&sw)[U], int64_t t0) {
+  auto compute = [&](const u32x4_t (&cw)[U], const uint32_t (&sw)[U], int64_t j0) {
 #pragma unroll
     for (int i = 0; i < U; i++) {
-      const int64_t t = t0 + (int64_t)i * W;
-      if (t < T) {
-        const f32x2_t sc = e4m3x2_to_f32(sw[i] >> (16 * h));
-        const uint16_t *xk = xs + t * 64 + 32 * h;
+      const int64_t t = (j0 + (int64_t)i * W) * TPL + tl;
+      if (t >= T) continue;
+      const f32x2_t sc = e4m3x2_to_f32(sw[i] >> (16 * h));
+      const uint16_t *xk = xs + t * 64 + 32 * h;
 #pragma unroll
-        for (int blk = 0; blk < 2; blk++) {
-          float part[M];
+      for (int blk = 0; blk < 2; blk++) {
+        float part[M];
 #pragma unroll
-          for (int m = 0; m < M; m++) part[m] = 0.0f;
+        for (int m = 0; m < M; m++) part[m] = 0.0f;
 #pragma unroll
-          for (int d = 0; d < 2; d++) {
-            const int s = blk * 2 + d;
-            bf16x2_t wv[4];
-            codes8_to_bf16(cw[i][s], wv);
+        for (int d = 0; d < 2; d++) {
+          const int st = blk * 2 + d;
+          bf16x2_t wv[4];
+          codes8_to_bf16(cw[i][st], wv);
 #pragma unroll
-            for (int m = 0; m < M; m++) {
-              const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xk + m * K + 8 * s);
+          for (int m = 0; m < M; m++) {
+            const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xk + m * K + 8 * st);
 #pragma unroll
-              for (int e = 0; e < 4; e++)
-                part[m] = __builtin_amdgcn_fdot2_f32_bf16(wv[e], as_bf16x2(xv[e]), part[m], false);
-            }
+            for (int e = 0; e < 4; e++)
+              part[m] = __builtin_amdgcn_fdot2_f32_bf16(wv[e], as_bf16x2(xv[e]), part[m], false);
           }
-#pragma unroll
-          for (int m = 0; m < M; m++) acc[m] = __builtin_fmaf(part[m], sc[blk], acc[m]);
         }
+#pragma unroll
+        for (int m = 0; m < M; m++) acc[m] = __builtin_fmaf(part[m], sc[blk], acc[m]);
       }
     }
   };
   const int64_t step = (int64_t)W * U;
-  for (int64_t t0 = wave; t0 < T; t0 += 2 * step) {
-    issue(cw1, sw1, t0 + step);
-    compute(cw0, sw0, t0);
-    if (t0 + step >= T) break;
-    issue(cw0, sw0, t0 + 2 * step);
-    compute(cw1, sw1, t0 + step);
+  for (int64_t j0 = wave; j0 < groups; j0 += 2 * step) {
+    issue(cw1, sw1, j0 + step);
+    compute(cw0, sw0, j0);
+    if (j0 + step >= groups) break;
+    issue(cw0, sw0, j0 + 2 * step);
+    compute(cw1, sw1, j0 + step);
   }
-  // lanes r and r + 32 hold the two K-halves of row r: the same sum in both
+  // lanes r + R j (j < 64 / R) hold the (tile, half) streams of row r
 #pragma unroll
-  for (int m = 0; m < M; m++) acc[m] += __shfl_xor(acc[m], 32, 64);
-  if (h == 0)
+  for (int m = 0; m < M; m++)
+#pragma unroll
+    for (int off = R; off < 64; off <<= 1) acc[m] += __shfl_xor(acc[m], off, 64);
+  if (lane < R)
 #pragma unroll
     for (int m = 0; m < M; m++) red[wave][m][r] = acc[m];
   __syncthreads();
-  if (threadIdx.x < M * 32) {
-    const int m = threadIdx.x >> 5, rr = threadIdx.x & 31;
+  if (threadIdx.x < M * R) {
+    const int m = threadIdx.x / R, rr = threadIdx.x % R;
     float v = red[0][m][rr];
 #pragma unroll
     for (int w = 1; w < W; w++) v += red[w][m][rr];
     const float al = load_alpha(alpha, alpha_dev);
-    y[m * ldy + g * 32 + rr] = f32_to_bf16_rne(al * v);
+    y[m * ldy + g * 32 + row0 + rr] = f32_to_bf16_rne(al * v);
   }
 }
 
@@ -326,11 +255,6 @@ __global__ __launch_bounds__(kWideWaves * 64) void decode_wide_kernel(const uint
 // check). Weights and x fragments are loaded a batch of tiles ahead. Each wave ends with a full 32 x 32 MT partial tile; the
 // waves are added in a fixed tree (4+4, 2+2, 1+1) through LDS.
 constexpr int kSkWaves = 8;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc16(const void *base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)n, 0x00020000);
-}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   bf16x8_t b;
@@ -916,38 +840,26 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (plan.kind == 0 || plan.kind == 2) {
+  if (plan.kind == 0) {
     if (plan.grid_x > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
     const size_t lds = (size_t)(M * K * 2);
-#define NVFP4_DECODE_CASE(MM)                                                                                 \
-  case MM:                                                                                                    \
-    hipLaunchKernelGGL(w4a16::decode_kernel<MM>, dim3((unsigned)plan.grid_x), dim3(w4a16::kDecodeThreads), lds, \
-                       s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy);                                    \
-    break;
-#define NVFP4_DECODE_WIDE_CASE(MM)                                                                            \
-  case MM:                                                                                                    \
-    hipLaunchKernelGGL(w4a16::decode_wide_kernel<MM>, dim3((unsigned)plan.grid_x),                            \
-                       dim3(w4a16::kWideWaves * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy); \
-    break;
-    if (plan.kind == 2) {
-      switch ((int)M) {
-        NVFP4_DECODE_WIDE_CASE(1)
-        NVFP4_DECODE_WIDE_CASE(2)
-        NVFP4_DECODE_WIDE_CASE(3)
-        NVFP4_DECODE_WIDE_CASE(4)
-        default: return NVFP4_ERR_SHAPE;
-      }
-    } else {
-      switch ((int)M) {
-        NVFP4_DECODE_CASE(1)
-        NVFP4_DECODE_CASE(2)
-        NVFP4_DECODE_CASE(3)
-        NVFP4_DECODE_CASE(4)
-        default: return NVFP4_ERR_SHAPE;
-      }
+    const int key = plan.dec * 8 + (int)M;
+#define NVFP4_DECODE_CASE(D, MM)                                                                               \
+  case D * 8 + MM: {                                                                                           \
+    constexpr w4a16::DecodeShape sh = w4a16::kDecodeShapes[D];                                                 \
+    hipLaunchKernelGGL((w4a16::decode_kernel<MM, sh.R, sh.W, sh.U>), dim3((unsigned)plan.grid_x),            \
+                       dim3(sh.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy);               \
+    break;                                                                                                     \
+  }
+#define NVFP4_DECODE_SHAPE(D) \
+  NVFP4_DECODE_CASE(D, 1) NVFP4_DECODE_CASE(D, 2) NVFP4_DECODE_CASE(D, 3) NVFP4_DECODE_CASE(D, 4)
+    switch (key) {
+      NVFP4_DECODE_SHAPE(0)
+      NVFP4_DECODE_SHAPE(1)
+      default: return NVFP4_ERR_SHAPE;
     }
+#undef NVFP4_DECODE_SHAPE
 #undef NVFP4_DECODE_CASE
-#undef NVFP4_DECODE_WIDE_CASE
   } else if (plan.kind == 4) {
     if ((int64_t)256 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
     const int T = w4a16::big_tile_t(M, N, di.num_cus);
