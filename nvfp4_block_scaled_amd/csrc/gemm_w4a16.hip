@@ -252,9 +252,13 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
 // 64 lanes x 16 bytes, rows >= M zero), so each fragment load is one contiguous
 // 1 KB instead of 32 scattered rows; for M <= 16 the scattered direct reads
 // cost less than the copy (rows >= M read as zero through the buffer range
-// check). Weights and x fragments are loaded a batch of tiles ahead. Each wave ends with a full 32 x 32 MT partial tile; the
-// waves are added in a fixed tree (4+4, 2+2, 1+1) through LDS.
-constexpr int kSkWaves = 8;
+// check). Weights and x fragments are loaded one tile per wave ahead (a
+// two-tile register ring): the x fragments cost 16 MT registers per tile, and
+// deeper rings lowered the occupancy enough to measure slower. Each wave ends
+// with a full 32 x 32 MT partial tile; the waves are added in a fixed tree
+// (4+4, 2+2, 1+1) through LDS.
+constexpr int kSkWaves = 8;   // a power of two
+constexpr int kSkAhead = 1;   // tiles per wave and ring batch
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   bf16x8_t b;
@@ -288,8 +292,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *_
                                                              uint16_t *__restrict__ y, int64_t ldy,
                                                              const uint8_t *__restrict__ xf) {
   constexpr int W = kSkWaves;
-  constexpr int U = MT == 1 ? 4 : 2;                        // tiles per wave per batch
-  __shared__ f32x16_t red[4][MT][64];
+  constexpr int U = kSkAhead;                          // tiles per wave per batch
+  __shared__ f32x16_t red[W / 2][MT][64];
   const int64_t T = K / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, r = lane & 31;
@@ -352,9 +356,9 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *_
     issue(b0, t0 + 2 * step);
     compute(b1, t0 + step);
   }
-  // fixed-order tree over the 8 waves' partial tiles
+  // fixed-order tree over the waves' partial tiles (W/2 + W/2, ..., 1 + 1)
 #pragma unroll
-  for (int half = 4; half >= 1; half >>= 1) {
+  for (int half = W / 2; half >= 1; half >>= 1) {
     if (wave >= half && wave < 2 * half)
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) red[wave - half][mt][lane] = acc[mt];
