@@ -66,9 +66,11 @@ size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
 
 /* Workspace bytes an op needs for (M, N, K); 0 means no workspace is used.
  * The workspace holds A in the prepared tile layout (W4A4: (M rounded up to
- * 32) * K * 9/16 bytes), x in MFMA fragment order (W4A16, 16 < M <= 64) or
- * split-K partial sums (W4A16, some M > 64), or per-workgroup maxima
- * (quantize); every call overwrites what it reads. */
+ * 32) * K * 9/16 bytes), x in MFMA fragment order (W4A16, 16 < M <= 64),
+ * FP32 partial tiles of output tiles split along K (W4A16, M > 64 when the
+ * tiles do not fill whole rounds of the CUs; the size depends on the device's
+ * CU count), or per-workgroup maxima (quantize); every call overwrites what it
+ * reads. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* Zeroes a workspace on `stream` with a fill kernel (no hipMemset, so it may be

@@ -19,17 +19,12 @@
 //  * 4 < M <= 64 (and M <= 4 when x does not fit in LDS): the skinny MFMA
 //    kernel, the decode structure with v_mfma_f32_32x32x16_bf16 on one or two
 //    32-row x tiles (below).
-//  * M > 64 with enough output tiles to fill half the CUs: the big MFMA kernel,
-//    built like the W4A4 kernel (below).
-//  * otherwise: an LDS-tiled MFMA kernel (v_mfma_f32_32x32x16_bf16). BF16 x tiles
-//    are staged through LDS (XOR-swizzled rows, conflict-free 16-byte reads);
-//    weight codes and scales are staged as packed bytes in the prepared tile
-//    format and dequantized exactly to BF16 in registers (E2M1 -> FP32, times
-//    the E4M3 scale in FP32, exact; -> BF16, exact). When the output tiles alone
-//    cannot fill the CUs, K is split across workgroups: each writes an FP32
-//    partial tile to the workspace and a second kernel adds the partials in
-//    split order 0, 1, 2, ... and applies the epilogue, so the result does not
-//    depend on scheduling.
+//  * M > 64: the big MFMA kernel, built like the W4A4 kernel (below), on
+//    persistent workgroups. Output tiles that do not fill whole rounds of the
+//    CUs, or are fewer than the CUs, are split along K: each split range writes
+//    an FP32 partial tile to the workspace and a fix-up kernel adds the partials
+//    in workgroup order and applies the epilogue, so the result does not depend
+//    on scheduling.
 #include "common.hpp"
 
 namespace nvfp4 {
@@ -48,9 +43,7 @@ constexpr int kNonTemporal = 2;   // cache-policy bits of a streamed load
 // ---------------------------------------------------------------- planning
 
 struct Plan {
-  int kind;          // 0 = vector decode kernel, 1 = MFMA tile kernel, 3 = skinny MFMA kernel,
-                     // 4 = big MFMA kernel
-  int splits;        // K splits of the tile kernel (1 = none)
+  int kind;          // 0 = vector decode kernel, 3 = skinny MFMA kernel, 4 = big MFMA kernel
   int dec;           // launch shape of the decode kernel (kDecodeShapes)
   int64_t grid_x;    // workgroups along the output
 };
@@ -66,7 +59,6 @@ constexpr int kDecodeMaxM = 4;
 constexpr int kSkinnyMaxM = 64;
 constexpr int kSkinnyDirectMaxM = 16;   // up to here the skinny kernel reads x rows directly
 constexpr int kDecodeLdsBytes = 64 * 1024;  // x staged in LDS: M * K * 2 bytes at most
-constexpr int BM = 256, BN = 128;         // tile kernel
 
 static int num_cus_or_default() {
   DeviceInfo d;
@@ -76,10 +68,6 @@ static int num_cus_or_default() {
 
 // Output tiles of the big kernel: 256 x 256 when those fill the CUs, else 128 x 128.
 static int big_tile_t(int64_t M, int64_t N, int cus) { return ((M + 255) / 256) * ((N + 255) / 256) >= cus ? 4 : 2; }
-static int64_t big_tiles(int64_t M, int64_t N, int cus) {
-  const int64_t bt = 64 * big_tile_t(M, N, cus);
-  return ((M + bt - 1) / bt) * ((N + bt - 1) / bt);
-}
 
 // One 32-row group per workgroup. Eight waves once there are two groups per
 // CU; with fewer groups, twelve waves keep more loads in flight per CU (more
@@ -90,28 +78,15 @@ static int decode_shape(int64_t N, int cus) { return N / 32 >= 2 * cus ? 0 : 1; 
 static Plan make_plan(int64_t M, int64_t N, int64_t K) {
   Plan p{};
   const int cus = num_cus_or_default();
-  const int64_t ktiles = K / 64;
   if (M <= kDecodeMaxM && M * K * 2 <= kDecodeLdsBytes) {
     p.kind = 0;
-    p.splits = 1;
     p.dec = decode_shape(N, cus);
     p.grid_x = N / kDecodeShapes[p.dec].R;
   } else if (M <= kSkinnyMaxM) {
     p.kind = 3;
-    p.splits = 1;
     p.grid_x = N / 32;
-  } else if (big_tiles(M, N, cus) * 2 >= cus) {
-    // enough output tiles for the persistent kernel; otherwise the split-K tile kernel
-    p.kind = 4;
-    p.splits = 1;
-    p.grid_x = 0;
   } else {
-    p.kind = 1;
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    p.grid_x = tiles;
-    int64_t s = 1;
-    while (tiles * s < cus && s * 2 <= ktiles / 4 && s < 16) s *= 2;
-    p.splits = (int)s;
+    p.kind = 4;
   }
   return p;
 }
@@ -120,10 +95,65 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K) {
 // roundup32(M) rows x K BF16.
 static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 32 * 32) * (size_t)K * 2; }
 
+// Schedule of the big kernel.
+//  * 256 x 256 tiles (one workgroup per CU): G = CUs persistent workgroups
+//    each run full / G whole tiles; the rem = total - full tiles left over are
+//    split along K over all G workgroups.
+//  * 128 x 128 tiles (two workgroups per CU), at least as many as CUs: one
+//    workgroup per tile up to two per CU, then whole rounds; a CU running two
+//    workgroups loses little against one that runs one, and splitting these
+//    tiles measured slower.
+//  * Fewer 128 x 128 tiles than CUs: every tile is split along K into S equal
+//    ranges, G = S x tiles workgroups. S = CUs / tiles (one workgroup per CU),
+//    or 2 CUs / tiles when that is below 3; at most 8 and K / 1024 (short
+//    ranges lose their prologue and fix-up to the split); no split below 3.
+//    On the 27B-class layers a CU running two short ranges finished well after
+//    the CUs running one, so the split keeps to one per CU where it can.
+// Split ranges write FP32 partials (two slots per workgroup) that a fix-up
+// kernel adds in workgroup order.
+constexpr int kMaxKSplit = 8;
+
+struct BigSched {
+  int T;
+  int64_t tiles_m, tiles_n, total, G, full, rem;
+};
+
+static BigSched big_sched(int64_t M, int64_t N, int64_t K, int cus) {
+  BigSched b{};
+  b.T = big_tile_t(M, N, cus);
+  const int64_t bt = 64 * b.T;
+  b.tiles_m = (M + bt - 1) / bt;
+  b.tiles_n = (N + bt - 1) / bt;
+  b.total = b.tiles_m * b.tiles_n;
+  const int64_t slots = (int64_t)cus * (b.T == 4 ? 1 : 2);
+  if (b.T == 4) {
+    b.G = b.total < slots ? b.total : slots;
+    b.full = b.total / b.G * b.G;
+  } else if (b.total >= cus) {
+    b.G = b.total < slots ? b.total : slots;
+    b.full = b.total;
+  } else {
+    int64_t S = cus / b.total;                // one workgroup per CU ...
+    if (S < 3) S = slots / b.total;            // ... else two
+    if (S > kMaxKSplit) S = kMaxKSplit;
+    if (S > K / 1024) S = K / 1024;            // at least 16 chunks per range
+    if (S < 3) S = 1;                          // a two-way split measured slower than none
+    b.G = S * b.total;
+    b.full = S == 1 ? b.total : 0;
+  }
+  b.rem = b.total - b.full;
+  return b;
+}
+
+static size_t big_partial_bytes(int T) { return (size_t)T * T * 16384; }   // 4 waves x T x T x 64 lanes x 16 FP32
+
 static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
   if (p.kind == 3) return M > kSkinnyDirectMaxM ? skinny_x_bytes(M, K) : 0;
-  if (p.splits <= 1) return 0;
-  return (size_t)p.splits * (size_t)M * (size_t)N * 4;
+  if (p.kind == 4) {
+    const BigSched b = big_sched(M, N, K, num_cus_or_default());
+    return b.rem > 0 ? (size_t)b.G * 2 * big_partial_bytes(b.T) : 0;
+  }
+  return 0;
 }
 
 // ---------------------------------------------------------------- decode kernel (M <= 4)
@@ -411,7 +441,25 @@ struct Params {
   float alpha;
   const float *alpha_dev;
   int tiles_m, tiles_n;
+  int full;          // tiles [0, full) run whole, persistent over gridDim.x workgroups
+  int rem;           // tiles [full, full + rem) are split along K over all workgroups
+  float *partials;   // 2 slots per workgroup of partial tiles (rem > 0)
 };
+
+// One partial tile: 4 waves x T x T MFMA tiles x 64 lanes x 16 FP32, in the
+// accumulator layout.
+template <int T>
+constexpr int64_t partial_floats() {
+  return (int64_t)4 * T * T * 64 * 16;
+}
+
+// Chunk range [s, e) of workgroup `pid` in the split part: the rem x nch
+// (tile, chunk) units cut into G contiguous, nearly equal ranges. As rem < G,
+// a range is shorter than one tile and touches at most two.
+__device__ __forceinline__ void split_range(int64_t pid, int64_t G, int64_t units, int64_t &s, int64_t &e) {
+  s = pid * units / G;
+  e = (pid + 1) * units / G;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
@@ -557,13 +605,101 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
   tn = w / rows;
 }
 
+// Chunks [c0, c0 + n) of tile `tile` into acc (zeroed first). The tile bases
+// are moved to chunk c0, so chunk c of the loop is chunk c0 + c of the tile and
+// the loads past the range are empty.
+template <int T>
+__device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t c0, int64_t n, uint8_t *smem,
+                                              const uint32_t (&ow)[T], const uint32_t (&ows)[T], int wm,
+                                              f32x16_t (&acc)[T][T], int64_t &m0, int64_t &n0) {
+  constexpr int BT = 64 * T;
+  const int64_t kt = p.K / 64;
+  int tm, tn;
+  tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
+  m0 = (int64_t)tm * BT;
+  n0 = (int64_t)tn * BT;
+  TileBase tb;
+  tb.x = reinterpret_cast<const uint8_t *>(p.x + m0 * p.ldx + c0 * 64);
+  tb.x_bytes = (p.M - m0) * p.ldx * 2 - c0 * 128;
+  tb.w = p.wp + ((n0 >> 5) * kt + c0) * 1024;
+  tb.w_bytes = (p.N - n0) / 32 * kt * 1024 - c0 * 1024;
+  tb.ws = p.wp + p.N * p.K / 2 + ((n0 >> 5) * kt + c0) * 128;
+  tb.ws_bytes = (p.N - n0) / 32 * kt * 128 - c0 * 128;
+
+#pragma unroll
+  for (int i = 0; i < T; i++)
+#pragma unroll
+    for (int j = 0; j < T; j++) acc[i][j] = f32x16_t{};
+  WFrags<T> f[3];
+  f32x2_t sc[T];
+  bf16x8_t a[T], b[T];
+  __syncthreads();   // the previous tile's waves are done with the LDS buffers
+  {
+    XRegs<T> xr;
+    load_x<T>(tb, p.ldx, 0, n, xr);
+    load_w<T>(tb, ow, ows, 0, n, f[0]);
+    load_w<T>(tb, ow, ows, 1, n, f[1]);
+    store_x<T>(smem, xr);
+  }
+  lds_barrier();
+  scales_of<T>(f[0], sc);
+  read_x<T>(smem, 0, wm, a);
+  deq_w<T>(f[0], sc, 0, b);
+  for (int64_t c = 0; c < n; c += 3) {
+    chunk<0, T>(tb, p.ldx, ow, ows, c, n, f, sc, smem, wm, a, b, acc);
+    chunk<1, T>(tb, p.ldx, ow, ows, c + 1, n, f, sc, smem, wm, a, b, acc);
+    chunk<2, T>(tb, p.ldx, ow, ows, c + 2, n, f, sc, smem, wm, a, b, acc);
+  }
+}
+
+// Epilogue of a whole tile: per wave 32 x 32T staging of BF16 in LDS (after
+// every wave is done with x), then 16-byte row pieces.
+template <int T>
+__device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, float alpha, int64_t m0, int64_t n0,
+                                              int wave, int wm, int wn, f32x16_t (&acc)[T][T]) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+  __syncthreads();
+  constexpr int ROW_BYTES = 32 * T * 2;
+  uint8_t *reg = smem + wave * (32 * ROW_BYTES);
+  const int64_t col0 = n0 + wn * 32 * T;
+  const int64_t ncols = p.N - col0;
+  const bool vec_ok = (p.ldy * 2) % 16 == 0 && ((uintptr_t)p.y & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < T; i++) {
+#pragma unroll
+    for (int j = 0; j < T; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        const int row = 8 * (e >> 2) + 4 * h + (e & 3);
+        *reinterpret_cast<uint16_t *>(reg + row * ROW_BYTES + (j * 32 + r) * 2) = f32_to_bf16_rne(alpha * acc[i][j][e]);
+      }
+    __syncthreads();
+    constexpr int PIECES = ROW_BYTES / 16;
+    for (int q = lane; q < 32 * PIECES; q += 64) {
+      const int row = q / PIECES, pc = q % PIECES;
+      const int64_t m = m0 + wm * 32 * T + i * 32 + row;
+      const int64_t cc = (int64_t)pc * 8;
+      if (m < p.M && cc < ncols) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(reg + row * ROW_BYTES + pc * 16);
+        uint16_t *dst = p.y + m * p.ldy + col0 + cc;
+        if (vec_ok) {
+          *reinterpret_cast<u32x4_t *>(dst) = v;
+        } else {
+          const uint16_t *src = reinterpret_cast<const uint16_t *>(&v);
+          for (int e2 = 0; e2 < 8; e2++) dst[e2] = src[e2];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int T>
 __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p) {
   constexpr int BT = 64 * T;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BT * 128];   // two x chunks; reused by the epilogue
   const int t = threadIdx.x, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
-  const int lane = t & 63, h = lane >> 5, r = lane & 31;
-  const int total = p.tiles_m * p.tiles_n;
+  const int lane = t & 63, r = lane & 31;
   const int G = gridDim.x;
   int pid = blockIdx.x;
   if ((G & 7) == 0) pid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
@@ -575,244 +711,79 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p)
     ow[j] = (uint32_t)(((wn * T + j) * kt) * 1024 + lane * 16);
     ows[j] = (uint32_t)(((wn * T + j) * kt) * 128 + r * 4);
   }
-  for (int tile = pid; tile < total; tile += G) {
-    int tm, tn;
-    tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * BT, n0 = (int64_t)tn * BT;
-    TileBase tb;
-    tb.x = reinterpret_cast<const uint8_t *>(p.x + m0 * p.ldx);
-    tb.x_bytes = (p.M - m0) * p.ldx * 2;
-    tb.w = p.wp + (n0 >> 5) * kt * 1024;
-    tb.w_bytes = (p.N - n0) / 32 * kt * 1024;
-    tb.ws = p.wp + p.N * p.K / 2 + (n0 >> 5) * kt * 128;
-    tb.ws_bytes = (p.N - n0) / 32 * kt * 128;
+  f32x16_t acc[T][T];
+  int64_t m0, n0;
+  for (int tile = pid; tile < p.full; tile += G) {
+    tile_mainloop<T>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
+    tile_epilogue<T>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
+  }
+  if (p.rem > 0) {
+    int64_t s, e;
+    split_range(pid, G, (int64_t)p.rem * nch, s, e);
+    for (int seg = 0; s < e; seg++) {
+      const int64_t rho = s / nch, c0 = s - rho * nch, c1 = min(nch, c0 + (e - s));
+      tile_mainloop<T>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm, acc, m0, n0);
+      float *dst = p.partials + ((int64_t)pid * 2 + seg) * partial_floats<T>() + (int64_t)wave * T * T * 1024 +
+                   lane * 16;
+#pragma unroll
+      for (int i = 0; i < T; i++)
+#pragma unroll
+        for (int j = 0; j < T; j++)
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            *reinterpret_cast<f32x4_t *>(dst + (i * T + j) * 1024 + 4 * q) =
+                f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      s += c1 - c0;
+    }
+  }
+}
 
-    f32x16_t acc[T][T];
+// Split tiles: workgroup (rho, part) takes 1024 of tile full + rho's
+// accumulator elements (thread t: lane t % 64, elements 4 (t / 64) .. + 3 of
+// that lane in wave-tile `part`), adds them over every workgroup whose range
+// touches the tile, in workgroup order, then applies alpha and the BF16
+// conversion. 4 T^2 workgroups per tile.
+template <int T>
+__global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
+  const int rho = blockIdx.x / (4 * T * T), part = blockIdx.x % (4 * T * T);   // part = (wave, i, j)
+  const int wave = part / (T * T), i = (part / T) % T, j = part % T;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6, h = lane >> 5, r = lane & 31;
+  const int64_t nch = p.K / 64, units = (int64_t)p.rem * nch;
+  const int64_t lo = (int64_t)rho * nch, hi = lo + nch;   // the tile's units
+  int tm, tn;
+  tile_coords(p.full + rho, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * 64 * T, n0 = (int64_t)tn * 64 * T;
+  // first workgroup whose range ends past lo
+  int64_t first = lo * G / units;
+  if (first > 0) first--;
+  for (;;) {
+    int64_t s, e;
+    split_range(first, G, units, s, e);
+    if (e > lo || first == G - 1) break;
+    first++;
+  }
+  const int64_t off = (int64_t)part * 1024 + lane * 16 + 4 * q;
+  f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t w = first; w < G; w++) {
+    int64_t s, e;
+    split_range(w, G, units, s, e);
+    if (s >= hi) break;
+    if (e <= lo || s == e) continue;
+    const int seg = s >= lo ? 0 : 1;
+    v += *reinterpret_cast<const f32x4_t *>(p.partials + (w * 2 + seg) * partial_floats<T>() + off);
+  }
+  const float alpha = load_alpha(p.alpha, p.alpha_dev);
+  const int64_t col = n0 + wn * 32 * T + 32 * j + r;
 #pragma unroll
-    for (int i = 0; i < T; i++)
-#pragma unroll
-      for (int j = 0; j < T; j++) acc[i][j] = f32x16_t{};
-    WFrags<T> f[3];
-    f32x2_t sc[T];
-    bf16x8_t a[T], b[T];
-    {
-      XRegs<T> xr;
-      load_x<T>(tb, p.ldx, 0, nch, xr);
-      load_w<T>(tb, ow, ows, 0, nch, f[0]);
-      load_w<T>(tb, ow, ows, 1, nch, f[1]);
-      store_x<T>(smem, xr);
-    }
-    lds_barrier();
-    scales_of<T>(f[0], sc);
-    read_x<T>(smem, 0, wm, a);
-    deq_w<T>(f[0], sc, 0, b);
-    for (int64_t c = 0; c < nch; c += 3) {
-      chunk<0, T>(tb, p.ldx, ow, ows, c, nch, f, sc, smem, wm, a, b, acc);
-      chunk<1, T>(tb, p.ldx, ow, ows, c + 1, nch, f, sc, smem, wm, a, b, acc);
-      chunk<2, T>(tb, p.ldx, ow, ows, c + 2, nch, f, sc, smem, wm, a, b, acc);
-    }
-    // epilogue: per wave 32 x 32T staging of BF16 in LDS (after every wave is done with x)
-    __syncthreads();
-    constexpr int ROW_BYTES = 32 * T * 2;
-    uint8_t *reg = smem + wave * (32 * ROW_BYTES);
-    const int64_t col0 = n0 + wn * 32 * T;
-    const int64_t ncols = p.N - col0;
-    const bool vec_ok = (p.ldy * 2) % 16 == 0 && ((uintptr_t)p.y & 15) == 0;
-#pragma unroll
-    for (int i = 0; i < T; i++) {
-#pragma unroll
-      for (int j = 0; j < T; j++)
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-          const int row = 8 * (e >> 2) + 4 * h + (e & 3);
-          *reinterpret_cast<uint16_t *>(reg + row * ROW_BYTES + (j * 32 + r) * 2) = f32_to_bf16_rne(alpha * acc[i][j][e]);
-        }
-      __syncthreads();
-      constexpr int PIECES = ROW_BYTES / 16;
-      for (int q = lane; q < 32 * PIECES; q += 64) {
-        const int row = q / PIECES, pc = q % PIECES;
-        const int64_t m = m0 + wm * 32 * T + i * 32 + row;
-        const int64_t cc = (int64_t)pc * 8;
-        if (m < p.M && cc < ncols) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t *>(reg + row * ROW_BYTES + pc * 16);
-          uint16_t *dst = p.y + m * p.ldy + col0 + cc;
-          if (vec_ok) {
-            *reinterpret_cast<u32x4_t *>(dst) = v;
-          } else {
-            const uint16_t *src = reinterpret_cast<const uint16_t *>(&v);
-            for (int e2 = 0; e2 < 8; e2++) dst[e2] = src[e2];
-          }
-        }
-      }
-      __syncthreads();
-    }
+  for (int k = 0; k < 4; k++) {
+    const int e = 4 * q + k;
+    const int64_t m = m0 + wm * 32 * T + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+    if (m < p.M && col < p.N) p.y[m * p.ldy + col] = f32_to_bf16_rne(alpha * v[k]);
   }
 }
 
 }  // namespace big
-
-// ---------------------------------------------------------------- MFMA tile kernel (M > 4)
-
-// LDS stage (one 64-wide K chunk): x tile [256 rows][64 bf16] with the eight
-// 16-byte units of each row XOR-swizzled by (row & 7); W codes [4 groups][1 KB]
-// and W scales [4 groups][128 B] in the prepared format.
-constexpr int X_BYTES = BM * 128;
-constexpr int WC_OFF = X_BYTES;
-constexpr int WS_OFF = WC_OFF + (BN / 32) * 1024;
-constexpr int STAGE = WS_OFF + (BN / 32) * 128;   // 37376
-
-struct TileParams {
-  const uint16_t *x;
-  int64_t ldx;
-  const uint8_t *wp;
-  int64_t M, N, K;
-  float alpha;
-  const float *alpha_dev;
-  uint16_t *y;
-  int64_t ldy;
-  int tiles_n, splits;
-  float *partial;
-};
-
-struct TileRegs {
-  u32x4_t xv[8];   // x: 256 rows x 8 units / 256 threads
-  u32x4_t wc;      // W codes: 4 KB / 256 threads
-  uint32_t wsc;    // W scales: 512 B / 128 threads (as dwords)
-};
-
-__device__ __forceinline__ void tile_load(const TileParams &p, int64_t m0, int64_t n0, int64_t kt, TileRegs &r) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int q = t + kThreads * i;        // (row, unit)
-    const int row = q >> 3, u = q & 7;
-    const int64_t m = m0 + row;
-    if (m < p.M)
-      r.xv[i] = *reinterpret_cast<const u32x4_t *>(p.x + m * p.ldx + kt * 64 + u * 8);
-    else
-      r.xv[i] = u32x4_t{0u, 0u, 0u, 0u};
-  }
-  const int64_t T = p.K / 64;
-  {
-    const int g = t >> 6, u = t & 63;
-    const int64_t ng = (n0 >> 5) + g;
-    if (ng * 32 < p.N)
-      r.wc = *reinterpret_cast<const u32x4_t *>(p.wp + ((ng * T + kt) << 10) + u * 16);
-    else
-      r.wc = u32x4_t{0u, 0u, 0u, 0u};
-  }
-  if (t < 128) {
-    const int g = t >> 5, u = t & 31;
-    const int64_t ng = (n0 >> 5) + g;
-    if (ng * 32 < p.N)
-      r.wsc = *reinterpret_cast<const uint32_t *>(p.wp + p.N * p.K / 2 + ((ng * T + kt) << 7) + u * 4);
-    else
-      r.wsc = 0u;
-  }
-}
-
-__device__ __forceinline__ void tile_store(uint8_t *lds, const TileRegs &r) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int q = t + kThreads * i;
-    const int row = q >> 3, u = q & 7;
-    *reinterpret_cast<u32x4_t *>(lds + row * 128 + ((u ^ (row & 7)) << 4)) = r.xv[i];
-  }
-  *reinterpret_cast<u32x4_t *>(lds + WC_OFF + (t >> 6) * 1024 + (t & 63) * 16) = r.wc;
-  if (t < 128) *reinterpret_cast<uint32_t *>(lds + WS_OFF + (t >> 5) * 128 + (t & 31) * 4) = r.wsc;
-}
-
-// Wave (wm, wn) owns rows [128 wm, 128 wm + 128) and columns [64 wn, 64 wn + 64)
-// of the 256 x 128 tile: 4 x 2 MFMA tiles.
-__device__ __forceinline__ void tile_compute(const uint8_t *lds, int wm, int wn, f32x16_t acc[4][2]) {
-  const int lane = threadIdx.x & 63;
-  const int h = lane >> 5, r = lane & 31;
-  u32x4_t wf[2];
-  f32x2_t sc[2];
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int g = wn * 2 + j;
-    wf[j] = *reinterpret_cast<const u32x4_t *>(lds + WC_OFF + g * 1024 + 16 * (32 * h + r));
-    const uint32_t sw = *reinterpret_cast<const uint32_t *>(lds + WS_OFF + g * 128 + r * 4);
-    sc[j] = e4m3x2_to_f32(sw >> (16 * h));
-  }
-#pragma unroll
-  for (int s = 0; s < 4; s++) {
-    bf16x8_t b[2], a[4];
-#pragma unroll
-    for (int j = 0; j < 2; j++) b[j] = dequant8_bf16(wf[j][s], sc[j][s >> 1]);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int row = wm * 128 + i * 32 + r;
-      const int u = 4 * h + s;               // k = 32h + 8s .. +7
-      a[i] = *reinterpret_cast<const bf16x8_t *>(lds + row * 128 + ((u ^ (row & 7)) << 4));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-__global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  const int tile = blockIdx.x;
-  const int split = blockIdx.y;
-  const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  const int64_t T = p.K / 64;
-  const int64_t kt0 = split * T / p.splits, kt1 = (split + 1) * T / p.splits;
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = f32x16_t{};
-  TileRegs regs;
-  tile_load(p, m0, n0, kt0, regs);
-  tile_store(smem, regs);
-  __syncthreads();
-  for (int64_t kt = kt0; kt < kt1; kt++) {
-    const bool more = kt + 1 < kt1;
-    if (more) tile_load(p, m0, n0, kt + 1, regs);
-    tile_compute(smem + ((kt - kt0) & 1) * STAGE, wm, wn, acc);
-    if (more) tile_store(smem + ((kt - kt0 + 1) & 1) * STAGE, regs);
-    __syncthreads();
-  }
-  const int lane = threadIdx.x & 63;
-  const int h = lane >> 5, r = lane & 31;
-  const float al = load_alpha(p.alpha, p.alpha_dev);
-  float *part = p.partial + (int64_t)split * p.M * p.N;
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int64_t n = n0 + wn * 64 + j * 32 + r;
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int e = 0; e < 16; e++) {
-        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m >= p.M) continue;
-        if (p.splits == 1)
-          p.y[m * p.ldy + n] = f32_to_bf16_rne(al * acc[i][j][e]);
-        else
-          part[m * p.N + n] = acc[i][j][e];
-      }
-    }
-}
-
-// Fixed-order sum of the split partials: y = alpha * (P_0 + P_1 + ... + P_{S-1}).
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partial, int splits, int64_t M,
-                                                            int64_t N, float alpha, const float *alpha_dev,
-                                                            uint16_t *__restrict__ y, int64_t ldy) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= M * N) return;
-  const int64_t m = idx / N, n = idx - m * N;
-  float v = partial[idx];
-  for (int s = 1; s < splits; s++) v += partial[(int64_t)s * M * N + idx];
-  y[m * ldy + n] = f32_to_bf16_rne(load_alpha(alpha, alpha_dev) * v);
-}
 
 }  // namespace w4a16
 
@@ -866,18 +837,25 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
 #undef NVFP4_DECODE_CASE
   } else if (plan.kind == 4) {
     if ((int64_t)256 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
-    const int T = w4a16::big_tile_t(M, N, di.num_cus);
-    const int64_t bt = 64 * T;
-    const int64_t tiles_m = (M + bt - 1) / bt, tiles_n = (N + bt - 1) / bt;
-    if (tiles_m * tiles_n > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
-    w4a16::big::Params bp{x, ldx, w_prep, y, ldy, M, N, K, alpha, alpha_dev, (int)tiles_m, (int)tiles_n};
-    const int64_t slots = (int64_t)di.num_cus * (T == 4 ? 1 : 2);
-    const int64_t total = tiles_m * tiles_n;
-    const unsigned grid = (unsigned)(total < slots ? total : slots);
-    if (T == 4)
+    const w4a16::BigSched b = w4a16::big_sched(M, N, K, di.num_cus);
+    if (b.total > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
+    w4a16::big::Params bp{x,     ldx,           w_prep,        y,           ldy,          M,
+                          N,     K,             alpha,         alpha_dev,   (int)b.tiles_m, (int)b.tiles_n,
+                          (int)b.full, (int)b.rem, static_cast<float *>(ws)};
+    const unsigned grid = (unsigned)b.G;
+    if (b.T == 4)
       hipLaunchKernelGGL(w4a16::big::big_kernel<4>, dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);
     else
       hipLaunchKernelGGL(w4a16::big::big_kernel<2>, dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);
+    if (b.rem > 0) {
+      NVFP4_LAUNCH_CHECK();
+      if (b.T == 4)
+        hipLaunchKernelGGL(w4a16::big::big_fixup_kernel<4>, dim3((unsigned)(b.rem * 64)), dim3(w4a16::big::kThreads),
+                           0, s, bp, (int)b.G);
+      else
+        hipLaunchKernelGGL(w4a16::big::big_fixup_kernel<2>, dim3((unsigned)(b.rem * 16)), dim3(w4a16::big::kThreads),
+                           0, s, bp, (int)b.G);
+    }
   } else if (plan.kind == 3) {
     if (plan.grid_x > 0x7FFFFFFF || M * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
     const int MT = M <= 32 ? 1 : 2;
@@ -897,20 +875,6 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     else if (MT == 1) NVFP4_SKINNY(1, true);
     else NVFP4_SKINNY(2, true);
 #undef NVFP4_SKINNY
-  } else {
-    const int64_t tiles_n = (N + w4a16::BN - 1) / w4a16::BN;
-    if (plan.grid_x > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
-    float *partial = need ? reinterpret_cast<float *>(ws) : nullptr;
-    w4a16::TileParams p{x, ldx, w_prep, M, N, K, alpha, alpha_dev, y, ldy, (int)tiles_n, plan.splits, partial};
-    hipLaunchKernelGGL(w4a16::tile_kernel, dim3((unsigned)plan.grid_x, (unsigned)plan.splits), dim3(w4a16::kThreads), 0,
-                       s, p);
-    NVFP4_LAUNCH_CHECK();
-    if (plan.splits > 1) {
-      const int64_t blocks = (M * N + 255) / 256;
-      if (blocks > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
-      hipLaunchKernelGGL(w4a16::splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, partial, plan.splits,
-                         M, N, alpha, alpha_dev, y, ldy);
-    }
   }
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;

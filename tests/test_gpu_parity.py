@@ -318,10 +318,17 @@ def test_w4a16_wide_decode(M, N, K):
     assert_close(host(out), y, S, bf16=True, what=f"wide decode M={M} {N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1000, 2080, 320), (2600, 8224, 128)])
+@pytest.mark.parametrize("M,N,K", [(1000, 2080, 320), (100, 512, 1024), (65, 4096, 4160), (200, 34816, 192),
+                                   (2600, 8224, 128), (256, 65792, 64), (300, 56320, 192)])
 def test_w4a16_big_ragged(M, N, K):
-    """Larger M with ragged rows and columns on the persistent MFMA path (128 x 128
-    tiles for the first shape, 256 x 256 for the second); full check."""
+    """Larger M with ragged rows and columns on the persistent MFMA path; full check.
+    Fewer 128 x 128 tiles than CUs, each split along K with a fix-up: 1000 x 2080 x 320
+    (136 tiles in 3 ranges of 5 chunks, so ranges straddle tiles), 100 x 512 x 1024 (4
+    tiles in 8 aligned ranges), 65 x 4096 x 4160 (65 chunks in 8 unaligned ranges).
+    200 x 34816: 544 ragged 128 x 128 tiles for 512 slots (an uneven last round). 256 x 256
+    tiles, the ones past the last full round split along K over all workgroups: 2600 x
+    8224 (107 of 363 tiles); 256 x 65792 x 64 (one tile of one chunk, so every other
+    workgroup's range is empty); 300 x 56320 (184 ragged tiles, about two chunks each)."""
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M + N + K)
     out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
     torch.cuda.synchronize()
