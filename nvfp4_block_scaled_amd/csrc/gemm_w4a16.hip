@@ -271,8 +271,8 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
 
 // ---------------------------------------------------------------- skinny MFMA kernel (4 < M <= 64)
 
-// Workgroup g covers the 32-row prepared tile group g over the whole K with 8
-// waves; wave w takes the tiles w, w + 8, ... as in the wide decode kernel. Per
+// Workgroup g covers the 32-row prepared tile group g over the whole K with W
+// waves; wave w takes the tiles w, w + W, ... as in the decode kernel. Per
 // tile and MFMA step s (k = 32h + 8s + i, the same K order as the prepared
 // weight units), lane l dequantizes its 8 codes of weight row 32g + (l & 31)
 // exactly to BF16 (E2M1 -> FP32, times the E4M3 scale, -> BF16) as the B
@@ -286,9 +286,12 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
 // two-tile register ring): the x fragments cost 16 MT registers per tile, and
 // deeper rings lowered the occupancy enough to measure slower. Each wave ends
 // with a full 32 x 32 MT partial tile; the waves are added in a fixed tree
-// (4+4, 2+2, 1+1) through LDS.
-constexpr int kSkWaves = 8;   // a power of two
+// (W/2 + W/2, ..., 1 + 1) through LDS. W = 8 waves, or 16 when there are
+// fewer row groups than CUs (more loads in flight on each busy CU; measured
+// 17 % faster at M = 8 on 5120 x 17408, slower on 34816 x 5120).
 constexpr int kSkAhead = 1;   // tiles per wave and ring batch
+
+static int skinny_waves(int64_t N, int cus) { return N / 32 < cus ? 16 : 8; }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   bf16x8_t b;
@@ -315,13 +318,12 @@ __global__ __launch_bounds__(256) void tile_x_kernel(const uint16_t *__restrict_
   xf[u] = v;
 }
 
-template <int MT, bool XF>
-__global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+template <int MT, bool XF, int W>
+__global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restrict__ x, int64_t ldx,
                                                              const uint8_t *__restrict__ wp, int64_t M, int64_t N,
                                                              int64_t K, float alpha, const float *alpha_dev,
                                                              uint16_t *__restrict__ y, int64_t ldy,
                                                              const uint8_t *__restrict__ xf) {
-  constexpr int W = kSkWaves;
   constexpr int U = kSkAhead;                          // tiles per wave per batch
   __shared__ f32x16_t red[W / 2][MT][64];
   const int64_t T = K / 64;
@@ -867,13 +869,20 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
                          MT, reinterpret_cast<u32x4_t *>(xf));
       NVFP4_LAUNCH_CHECK();
     }
-    const unsigned grid = (unsigned)plan.grid_x, threads = w4a16::kSkWaves * 64;
-#define NVFP4_SKINNY(MTV, XFV)                                                                                  \
-  hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV>), dim3(grid), dim3(threads), 0, s, x, ldx, w_prep, M, N, K, \
-                     alpha, alpha_dev, y, ldy, xf)
-    if (!xf_path) NVFP4_SKINNY(1, false);
-    else if (MT == 1) NVFP4_SKINNY(1, true);
-    else NVFP4_SKINNY(2, true);
+    const unsigned grid = (unsigned)plan.grid_x;
+    const int W = w4a16::skinny_waves(N, di.num_cus);
+#define NVFP4_SKINNY(MTV, XFV, WV)                                                                              \
+  hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV, WV>), dim3(grid), dim3(WV * 64), 0, s, x, ldx, w_prep, M, N, \
+                     K, alpha, alpha_dev, y, ldy, xf)
+    if (W == 16) {
+      if (!xf_path) NVFP4_SKINNY(1, false, 16);
+      else if (MT == 1) NVFP4_SKINNY(1, true, 16);
+      else NVFP4_SKINNY(2, true, 16);
+    } else {
+      if (!xf_path) NVFP4_SKINNY(1, false, 8);
+      else if (MT == 1) NVFP4_SKINNY(1, true, 8);
+      else NVFP4_SKINNY(2, true, 8);
+    }
 #undef NVFP4_SKINNY
   }
   NVFP4_LAUNCH_CHECK();
