@@ -296,7 +296,7 @@ def _w4a16_case(M, N, K, seed, alpha=0.75):
     return x, b, sb, wp, alpha
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 17, 32, 64, 128, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 12, 16, 17, 32, 64, 128, 300])
 @pytest.mark.parametrize("N,K", [(96, 192), (320, 640)])
 def test_w4a16_small_shapes(M, N, K):
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 31 + N)
@@ -304,6 +304,19 @@ def test_w4a16_small_shapes(M, N, K):
     torch.cuda.synchronize()
     y, S = gemm.w4a16(x, b, sb, alpha)
     assert_close(host(out), y, S, bf16=True, what=f"w4a16 M={M} {N}x{K}")
+
+
+@pytest.mark.parametrize("M", [6, 16])
+@pytest.mark.parametrize("N,K", [(17408, 4160), (2048, 8192)])
+def test_w4a16_skinny_long_k(M, N, K):
+    """M <= 16 (x rows read directly, rows >= M zero) with many tiles per wave: 544 row
+    groups (8 waves per workgroup, 65 tiles over them) and 64 row groups (16 waves, 8
+    tiles each); full check."""
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 7 + N + K)
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
+    torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"w4a16 skinny M={M} {N}x{K}")
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
