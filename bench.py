@@ -275,7 +275,7 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
