@@ -172,6 +172,25 @@ def test_w4a4_ragged_shapes(M, N, K, out_dtype):
     assert_close(host(out), D, S, bf16=out_dtype == "bf16", what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("out_dtype,pad", [("bf16", 3), ("f32", 4)])
+def test_w4a4_big_tiles_ragged_strided_out(out_dtype, pad):
+    """256 x 256 workgroup tiles (17 x 17 of them) with ragged rows and columns, written into
+    an output whose rows are longer than N: BF16 rows of N + 3 (not 16-byte aligned, the
+    element-store path) and FP32 rows of N + 4. The padding must stay untouched; full check."""
+    M, N, K = 4100, 4128, 128
+    a, sa = _random_nvfp4(M + 5, M, K)
+    b, sb = _random_nvfp4(N + 6, N, K)
+    wp, bad = _prep(b, sb)
+    assert bad == 0
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    big = torch.full((M, N + pad), -7.0, dtype=dt, device="cuda")
+    out = nv.nvfp4_gemm_w4a4(dev(a), dev(sa), wp, N, K, 0.81, None, out_dtype, out=big[:, :N])
+    torch.cuda.synchronize()
+    assert torch.all(big[:, N:] == -7.0), "columns past N were written"
+    D, S = gemm.w4a4_exact(a, sa, b, sb, 0.81)
+    assert_close(host(out), D, S, bf16=out_dtype == "bf16", what=f"strided {out_dtype} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,K", [(64, 128), (77, 320), (1, 64)])
 def test_tile_activation_bytes_match_oracle_layout(M, K):
     """The activation tile layout is the prepared-weight index map (no folds needed:
