@@ -165,7 +165,8 @@ static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
 // load reads 2 (32/R) contiguous runs of 16 R bytes (one 1 KB run for R = 32).
 // Wave w takes the tile groups w, w + W, w + 2W, ...; the loads run U groups
 // per wave ahead in a two-batch register ring (non-temporal: the weights are
-// streamed once), and the first batch is issued before x is staged in LDS. Per 16-element
+// streamed once), and the first batch is issued between x's first loads and
+// their stores into LDS. Per 16-element
 // block the BF16 products go through fdot2 into an FP32 partial that is scaled
 // once; the row's lanes are added by a butterfly (the same bits in every lane)
 // and the waves in wave order through LDS.
@@ -202,8 +203,26 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
       sw[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, kNonTemporal);
     }
   };
+  // x: the first kXEarly 16-byte units per thread are requested before the first
+  // weight batch (unconditionally: threads past the end read x's first unit and
+  // drop it), so staging them waits for x alone; any rest after it.
+  constexpr int kXEarly = 2;
+  const int64_t nx = (int64_t)M * K / 8;
+  u32x4_t xe[kXEarly];
+#pragma unroll
+  for (int i = 0; i < kXEarly; i++) {
+    const int64_t u = threadIdx.x + (int64_t)i * W * 64;
+    const int64_t m = u / (K / 8), c = u - m * (K / 8);
+    xe[i] = *reinterpret_cast<const u32x4_t *>(u < nx ? x + m * ldx + c * 8 : x);
+  }
   issue(cw0, sw0, wave);
-  for (int64_t u = threadIdx.x; u < M * K / 8; u += W * 64) {
+#pragma unroll
+  for (int i = 0; i < kXEarly; i++) {
+    const int64_t u = threadIdx.x + (int64_t)i * W * 64;
+    const int64_t m = u / (K / 8), c = u - m * (K / 8);
+    if (u < nx) *reinterpret_cast<u32x4_t *>(xs + m * K + c * 8) = xe[i];
+  }
+  for (int64_t u = threadIdx.x + (int64_t)kXEarly * W * 64; u < nx; u += W * 64) {
     const int64_t m = u / (K / 8), c = u - m * (K / 8);
     *reinterpret_cast<u32x4_t *>(xs + m * K + c * 8) = *reinterpret_cast<const u32x4_t *>(x + m * ldx + c * 8);
   }
