@@ -136,7 +136,9 @@ nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep
                                    float alpha, const float *alpha_dev, void *d, int out_dtype, int64_t ldd,
                                    void *stream);
 
-/* W4A16 GEMM: y = alpha_eff * x (W.SFW)^T, x and y BF16, FP32 accumulation.
+/* W4A16 GEMM: y = alpha_eff * x (W.SFW)^T, x and y BF16, FP32 accumulation
+ * (TileLang PR #3290, "Summary": BF16 activations against NVFP4 weights with
+ * E4M3 block scales, for M = 1 .. 1024 rows).
  *  x  [M][ldx] BF16 (uint16 bit patterns), device, 16-byte aligned, ldx % 8 == 0, ldx >= K.
  *  y  [M][ldy] BF16, device, 2-byte aligned, ldy >= N.
  *  M >= 0, N % 32 == 0, K % 64 == 0.
@@ -147,10 +149,12 @@ nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_p
                               int64_t N, int64_t K, float alpha, const float *alpha_dev, uint16_t *y,
                               int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
-/* BF16 -> NVFP4 quantizer (the recipe: per-tensor g = 2688 / max|x| (1 if the
- * tensor is zero); per 16-block scale = E4M3_RNE_sat((amax_b / 6) * g); codes =
- * E2M1_RNE_sat(x * (g / scale)) with x's sign, all in IEEE FP32; zero-scale
- * blocks get zero codes).
+/* BF16 -> NVFP4 quantizer for activations fed to W4A4 (the format as the pages
+ * use it: packed E2M1 codes, E4M3 block scales, a per-tensor global scale;
+ * TileLang PR #3290, "Summary". The pages do not print the recipe; this library
+ * uses: per-tensor g = 2688 / max|x| (1 if the tensor is zero); per 16-block
+ * scale = E4M3_RNE_sat((amax_b / 6) * g); codes = E2M1_RNE_sat(x * (g / scale))
+ * with x's sign, all in IEEE FP32; zero-scale blocks get zero codes).
  *  x       [rows][K] BF16, device, 16-byte aligned, K % 16 == 0 and K % 8 == 0.
  *  codes   [rows][K/2] bytes out, 8-byte aligned.  scales [rows][K/16] UE4M3 bytes out.
  *  g_dev   device float out: g.  inv_g_dev  device float out (may be NULL): 1/g in FP32.
