@@ -1,7 +1,12 @@
 """Shared helpers for the GPU parity tests (the tolerance of the NVFP4 GEMM
-outputs, host <-> device moves, and quantize-then-verify of inputs)."""
+outputs, host <-> device moves, quantize-then-verify of inputs, and the oracle run over
+row or tile blocks on the host's cores for full-size checks)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 from oracle import formats, gemm, quantize
 
@@ -29,23 +34,48 @@ def bound(ref, sum_abs, bf16):
     return tol
 
 
+def _close_block(got, ref, sum_abs, bf16):
+    """Per-block pieces of assert_close: None if the NaN patterns differ, else
+    (n_bad, worst excess, its err, tol, ref, got, squared error sum, squared ref sum)."""
+    nan_ref = np.isnan(ref)
+    if not np.array_equal(np.isnan(got), nan_ref):
+        return None
+    if nan_ref.any():
+        ok = ~nan_ref
+        got, ref, sum_abs = got[ok], ref[ok], sum_abs[ok]
+    if ref.size == 0:
+        return 0, -np.inf, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0
+    diff = got - ref
+    err = np.abs(diff)
+    tol = bound(ref, sum_abs, bf16)
+    excess = err - tol
+    i = int(np.argmax(excess))
+    return (int(np.count_nonzero(excess > 0)), excess.flat[i], err.flat[i], tol.flat[i], ref.flat[i],
+            got.flat[i], float(np.dot(diff.ravel(), diff.ravel())), float(np.dot(ref.ravel(), ref.ravel())))
+
+
 def assert_close(got, ref, sum_abs, bf16, what=""):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    sum_abs = np.asarray(sum_abs, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
-    nan_ref = np.isnan(ref)
-    assert np.array_equal(np.isnan(got), nan_ref), f"{what}: NaN pattern differs"
-    ok = ~nan_ref
-    err = np.abs(got[ok] - ref[ok])
-    tol = bound(ref[ok], sum_abs[ok], bf16)
-    bad = err > tol
-    if bad.any():
-        i = np.argmax(err - tol)
-        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside the bound; worst err {err[i]:.3e} "
-                             f"tol {tol[i]:.3e} ref {ref[ok][i]:.6e} got {got[ok][i]:.6e}")
+    if ref.ndim == 2 and ref.size > (1 << 22):
+        step = max(1, (1 << 20) // ref.shape[1])
+        parts = _on_host_cores(lambda r: _close_block(got[r:r + step], ref[r:r + step], sum_abs[r:r + step], bf16),
+                               range(0, ref.shape[0], step))
+    else:
+        parts = [_close_block(got, ref, sum_abs, bf16)]
+    assert all(p is not None for p in parts), f"{what}: NaN pattern differs"
+    n_bad = sum(p[0] for p in parts)
+    if n_bad:
+        w = max(parts, key=lambda p: p[1])
+        n_ok = int(np.count_nonzero(~np.isnan(ref)))
+        raise AssertionError(f"{what}: {n_bad} of {n_ok} outside the bound; worst err {w[2]:.3e} "
+                             f"tol {w[3]:.3e} ref {w[4]:.6e} got {w[5]:.6e}")
     # the pages' own, looser checks (TileLang PR #3290, 'Tests'): relative Frobenius error
-    if ref[ok].size and np.linalg.norm(ref[ok]) > 0:
-        rel = np.linalg.norm(got[ok] - ref[ok]) / np.linalg.norm(ref[ok])
+    num, den = sum(p[6] for p in parts), sum(p[7] for p in parts)
+    if den > 0:
+        rel = np.sqrt(num / den)
         assert rel <= 2.5e-3, f"{what}: relative Frobenius error {rel}"
 
 
@@ -72,3 +102,54 @@ def e4m3_scales_from_targets(t):
 def alpha_ab(gA, gB):
     """alpha = fl(1 / fl(gA * gB)) in FP32."""
     return np.float32(np.float32(1.0) / np.float32(np.float32(gA) * np.float32(gB)))
+
+
+def _workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _on_host_cores(fn, items):
+    """fn over items in host threads, one BLAS thread each (the blocks are independent)."""
+    with threadpool_limits(1), ThreadPoolExecutor(_workers()) as ex:
+        return list(ex.map(fn, items))
+
+
+def oracle_quantize_full(x_bits, rows_per_block=256):
+    """The oracle's quantization of a whole tensor: its global scale, then
+    quantize_rows_with_g on blocks of rows (given g, each row is quantized on its own).
+
+    Returns (codes, scales, g)."""
+    g = quantize.global_scale(x_bits)
+    parts = _on_host_cores(lambda r: quantize.quantize_rows_with_g(x_bits[r:r + rows_per_block], g),
+                           range(0, x_bits.shape[0], rows_per_block))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]), g
+
+
+def oracle_w4a4_exact_blocked(a, sa, b, sb, alpha, tile=2048):
+    """gemm.w4a4_exact on tile x tile blocks of D (an output element depends only on its
+    row of A and its row of B); returns (D, sum_abs) like the unblocked call."""
+    M, N = a.shape[0], b.shape[0]
+    D = np.empty((M, N))
+    S = np.empty((M, N))
+
+    def run(rc):
+        r, c = rc
+        d, t = gemm.w4a4_exact(a[r:r + tile], sa[r:r + tile], b[c:c + tile], sb[c:c + tile], alpha)
+        D[r:r + tile, c:c + tile] = d
+        S[r:r + tile, c:c + tile] = t
+    _on_host_cores(run, [(r, c) for r in range(0, M, tile) for c in range(0, N, tile)])
+    return D, S
+
+
+def oracle_w4a16_blocked(x, w_codes, w_scales, alpha, cols=2048):
+    """gemm.w4a16 on blocks of weight rows (output columns); returns (y, sum_abs)."""
+    M, N = x.shape[0], w_codes.shape[0]
+    y = np.empty((M, N))
+    S = np.empty((M, N))
+
+    def run(c):
+        yy, t = gemm.w4a16(x, w_codes[c:c + cols], w_scales[c:c + cols], alpha)
+        y[:, c:c + cols] = yy
+        S[:, c:c + cols] = t
+    _on_host_cores(run, range(0, N, cols))
+    return y, S

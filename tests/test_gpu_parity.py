@@ -11,7 +11,8 @@ import torch
 import nvfp4_block_scaled_amd as nv
 import synth
 from oracle import formats, gemm, prepared, quantize
-from gpu_helpers import alpha_ab, assert_close, dev, gpu_quantize_checked, host
+from gpu_helpers import (alpha_ab, assert_close, dev, gpu_quantize_checked, host, oracle_quantize_full,
+                         oracle_w4a4_exact_blocked, oracle_w4a16_blocked)
 
 pytestmark = pytest.mark.gpu
 
@@ -286,8 +287,35 @@ def _square_sampled(S, gen, n_rows=96, n_cols=96, extra_rows=()):
     return out
 
 
-def test_w4a4_normal_8192_sampled():
-    _square_sampled(8192, synth.square_normal)
+def test_w4a4_normal_8192_full():
+    """8192^3 in the benchmark's launch configuration (A quantized into the tile layout,
+    B quantized and prepared, nvfp4_gemm_w4a4_tiled into BF16), every output checked.
+    The row-major quantizer's bytes are checked in full against the oracle's, and the
+    row-major GEMM entry must give the same bits as the tiled one."""
+    S = 8192
+    xa, xb = synth.square_normal(S, "A"), synth.square_normal(S, "B")
+    xad = dev(xa).view(torch.bfloat16)
+    at, gA_t, _ = nv.nvfp4_quantize_tiled(xad)
+    ca, sa, gA_d, _ = nv.nvfp4_quantize(xad)
+    cb, sb, gB_d, _ = nv.nvfp4_quantize(dev(xb).view(torch.bfloat16))
+    wp, bad = nv.nvfp4_prepare_weight(cb, sb, "ue4m3")
+    a_ref, sa_ref, gA = oracle_quantize_full(xa)
+    b_ref, sb_ref, gB = oracle_quantize_full(xb)
+    assert np.float32(gA_t.item()) == gA and np.float32(gA_d.item()) == gA and np.float32(gB_d.item()) == gB
+    np.testing.assert_array_equal(host(ca), a_ref)
+    np.testing.assert_array_equal(host(sa), sa_ref)
+    np.testing.assert_array_equal(host(cb), b_ref)
+    np.testing.assert_array_equal(host(sb), sb_ref)
+    del xad, cb, sb
+    alpha = alpha_ab(gA, gB)
+    out = nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, float(alpha), None, "bf16")
+    std = nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, float(alpha), None, "bf16")
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    assert torch.equal(out, std), "tiled and row-major entries differ"
+    del std, ca, sa, at, wp
+    D, Sabs = oracle_w4a4_exact_blocked(a_ref, sa_ref, b_ref, sb_ref, alpha)
+    assert_close(host(out), D, Sabs, bf16=True, what="8192^3 full")
 
 
 @pytest.mark.slow
@@ -368,29 +396,39 @@ def test_w4a16_big_ragged(M, N, K):
     assert_close(host(out), y, S, bf16=True, what=f"w4a16 big {M}x{N}x{K}")
 
 
+_DECODE_Q = {}
+
+
+def _decode_weight_oracle(j):
+    """The oracle's quantization of decode weight j: (codes, scales, g), computed once."""
+    if j not in _DECODE_Q:
+        _DECODE_Q[j] = oracle_quantize_full(_decode_weight(j))
+    return _DECODE_Q[j]
+
+
 @pytest.mark.parametrize("j", range(4))
 @pytest.mark.parametrize("mi", range(5))
 def test_w4a16_decode_shapes(j, mi):
-    """27B-class layer shapes with W ~ N(0, 0.02) quantized on the GPU (sampled rows
-    checked bit-exact), x ~ N(0, 1); outputs checked on sampled weight rows."""
+    """27B-class layer shapes with W ~ N(0, 0.02) quantized on the GPU (bytes checked
+    bit-exact against the oracle's), x ~ N(0, 1); every output checked."""
     M = synth.DECODE_MS[mi]
     N, K = synth.DECODE_SHAPES[j]
     w = _decode_weight(j)
     x = synth.decode_activation(M, j, mi)
-    r = np.random.default_rng(j * 10 + mi)
-    cols = np.unique(np.concatenate([r.choice(N, 128, replace=False), [0, N - 1]]))
-    cw, sw, _, _, gW = gpu_quantize_checked(nv, w, cols)
+    cw, sw, gW_d, _ = nv.nvfp4_quantize(dev(w).view(torch.bfloat16))
+    c_ref, s_ref, gW = _decode_weight_oracle(j)
+    assert np.float32(gW_d.item()) == gW
+    np.testing.assert_array_equal(host(cw), c_ref)
+    np.testing.assert_array_equal(host(sw), s_ref)
     wp, bad = nv.nvfp4_prepare_weight(cw, sw, "ue4m3")
     alpha = np.float32(np.float32(1.0) / gW)
     out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, float(alpha))
     out2 = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, float(alpha))
     torch.cuda.synchronize()
+    assert int(bad.item()) == 0
     assert torch.equal(out, out2), "repeat calls must be bit-identical"
-    rows = np.arange(M) if M <= 32 else np.unique(np.concatenate([r.choice(M, 16, replace=False), [M - 1]]))
-    got = host(out[torch.as_tensor(rows).cuda()][:, torch.as_tensor(cols).cuda()])
-    c_ref, s_ref = quantize.quantize_rows_with_g(w[cols], gW)
-    y, S = gemm.w4a16(x[rows], c_ref, s_ref, alpha)
-    assert_close(got, y, S, bf16=True, what=f"decode {N}x{K} M={M}")
+    y, S = oracle_w4a16_blocked(x, c_ref, s_ref, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"decode {N}x{K} M={M}")
 
 
 def test_w4a16_zero_negative_scales_and_strided_out():
@@ -436,23 +474,33 @@ def test_w4a16_graph_capture_replay_matches_eager():
 
 # ------------------------------------------------------------------ prefill W4A4 with on-device quantize
 
-def test_prefill_quantize_then_w4a4_sampled():
+def test_prefill_quantize_then_w4a4_full():
+    """The prefill workload as the benchmark runs it: W quantized and prepared, then the timed
+    pair nvfp4_quantize_tiled(x) -> nvfp4_gemm_w4a4_tiled with alpha = 1/gW on the host and
+    inv_gA from the device. Quantized bytes of x and W bit-exact, every output checked."""
     x, _ = synth.prefill_activation()
     w = synth.prefill_weight()
     M, K = x.shape
     N = w.shape[0]
-    r = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([r.choice(M, 64, replace=False), [M - 1]]))
-    cols = np.unique(np.concatenate([r.choice(N, 64, replace=False), [N - 1]]))
-    cw, sw, _, _, gW = gpu_quantize_checked(nv, w, cols)
-    wp, _ = nv.nvfp4_prepare_weight(cw, sw, "ue4m3")
-    ca, sa, gA_dev, inv_gA, gA = gpu_quantize_checked(nv, x, rows)
+    cw, sw, gW_d, _ = nv.nvfp4_quantize(dev(w).view(torch.bfloat16))
+    wp, bad = nv.nvfp4_prepare_weight(cw, sw, "ue4m3")
+    xd = dev(x).view(torch.bfloat16)
+    at, gA_t, inv_gA = nv.nvfp4_quantize_tiled(xd)
+    ca, sa, _, _ = nv.nvfp4_quantize(xd)
+    w_ref, sw_ref, gW = oracle_quantize_full(w)
+    a_ref, sa_ref, gA = oracle_quantize_full(x)
+    assert np.float32(gW_d.item()) == gW and np.float32(gA_t.item()) == gA
+    assert np.float32(inv_gA.item()) == np.float32(np.float32(1.0) / gA)
+    np.testing.assert_array_equal(host(cw), w_ref)
+    np.testing.assert_array_equal(host(sw), sw_ref)
+    np.testing.assert_array_equal(host(ca), a_ref)
+    np.testing.assert_array_equal(host(sa), sa_ref)
+    del cw, sw, ca, sa, xd
     alpha_w = np.float32(np.float32(1.0) / gW)
-    out = nv.nvfp4_gemm_w4a4(ca, sa, wp, N, K, float(alpha_w), inv_gA, "bf16")
+    out = nv.nvfp4_gemm_w4a4_tiled(at, M, wp, N, K, float(alpha_w), inv_gA, "bf16")
     torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    del at, wp
     alpha_eff = gemm.alpha_product(alpha_w, np.float32(np.float32(1.0) / gA))
-    a_ref, sa_ref = quantize.quantize_rows_with_g(x[rows], gA)
-    b_ref, sb_ref = quantize.quantize_rows_with_g(w[cols], gW)
-    D, S = gemm.w4a4_exact(a_ref, sa_ref, b_ref, sb_ref, alpha_eff)
-    got = host(out[torch.as_tensor(rows).cuda()][:, torch.as_tensor(cols).cuda()])
-    assert_close(got, D, S, bf16=True, what="prefill")
+    D, S = oracle_w4a4_exact_blocked(a_ref, sa_ref, w_ref, sw_ref, alpha_eff)
+    assert_close(host(out), D, S, bf16=True, what="prefill full")
