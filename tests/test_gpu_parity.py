@@ -263,30 +263,6 @@ def test_w4a4_normal_2048_bf16_full():
     assert_close(host(out), D, Sabs, bf16=True, what="2048^3 bf16")
 
 
-def _square_sampled(S, gen, n_rows=96, n_cols=96, extra_rows=()):
-    """The product path at full size (GPU quantize of A and B, prepare, GEMM in
-    the benchmark's launch configuration) checked on sampled outputs."""
-    xa, xb = gen(S, "A"), gen(S, "B")
-    if isinstance(xa, tuple):
-        xa, xb = xa[0], xb[0]
-    r = np.random.default_rng(S)
-    rows = np.unique(np.concatenate([r.choice(S, n_rows, replace=False), np.asarray(extra_rows, int), [0, S - 1]]))
-    cols = np.unique(np.concatenate([r.choice(S, n_cols, replace=False), [0, S - 1]]))
-    ca, sa, _, _, gA = gpu_quantize_checked(nv, xa, rows)
-    cb, sb, _, _, gB = gpu_quantize_checked(nv, xb, cols)
-    wp, bad = nv.nvfp4_prepare_weight(cb, sb, "ue4m3")
-    alpha = alpha_ab(gA, gB)
-    out = nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, float(alpha), None, "bf16")
-    torch.cuda.synchronize()
-    assert int(bad.item()) == 0
-    got = host(out[torch.as_tensor(rows).cuda()][:, torch.as_tensor(cols).cuda()])
-    a_ref, sa_ref = quantize.quantize_rows_with_g(xa[rows], gA)
-    b_ref, sb_ref = quantize.quantize_rows_with_g(xb[cols], gB)
-    D, Sabs = gemm.w4a4_exact(a_ref, sa_ref, b_ref, sb_ref, alpha)
-    assert_close(got, D, Sabs, bf16=True, what=f"{S}^3 sampled")
-    return out
-
-
 def test_w4a4_normal_8192_full():
     """8192^3 in the benchmark's launch configuration (A quantized into the tile layout,
     B quantized and prepared, nvfp4_gemm_w4a4_tiled into BF16), every output checked.
@@ -319,10 +295,36 @@ def test_w4a4_normal_8192_full():
 
 
 @pytest.mark.slow
-def test_w4a4_large_16384_sampled():
+def test_w4a4_large_16384_rows():
+    """16384^3 with 1 % outlier rows (x8) and 1 % zeroed blocks in both operands, in the
+    square benchmark's launch configuration. D is 512 MiB, so the check covers 256 random rows
+    and 64 outlier rows of D across all 16384 columns (every column of B, its zero blocks and
+    outlier rows included); B's quantized bytes are checked in full, A's on those rows."""
     S = 16384
-    _, outl, _ = synth.square_large(S, "A")
-    _square_sampled(S, synth.square_large, extra_rows=outl[:32])
+    xa, outl, _ = synth.square_large(S, "A")
+    xb, _, _ = synth.square_large(S, "B")
+    r = np.random.default_rng(S)
+    rows = np.unique(np.concatenate([r.choice(S, 256, replace=False), outl[:64], [0, S - 1]]))
+    at, gA_t, _ = nv.nvfp4_quantize_tiled(dev(xa).view(torch.bfloat16))
+    ca, sa, _, _, gA = gpu_quantize_checked(nv, xa, rows)
+    cb, sb, gB_d, _ = nv.nvfp4_quantize(dev(xb).view(torch.bfloat16))
+    b_ref, sb_ref, gB = oracle_quantize_full(xb)
+    assert np.float32(gA_t.item()) == gA and np.float32(gB_d.item()) == gB
+    np.testing.assert_array_equal(host(cb), b_ref)
+    np.testing.assert_array_equal(host(sb), sb_ref)
+    wp, bad = nv.nvfp4_prepare_weight(cb, sb, "ue4m3")
+    del cb, sb
+    alpha = alpha_ab(gA, gB)
+    out = nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, float(alpha), None, "bf16")
+    std = nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, float(alpha), None, "bf16")
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    assert torch.equal(out, std), "tiled and row-major entries differ"
+    del std, ca, sa, at, wp
+    got = host(out[torch.as_tensor(rows).cuda()])
+    a_ref, sa_ref = quantize.quantize_rows_with_g(xa[rows], gA)
+    D, Sabs = oracle_w4a4_exact_blocked(a_ref, sa_ref, b_ref, sb_ref, alpha, tile=1024)
+    assert_close(got, D, Sabs, bf16=True, what="16384^3 rows")
 
 
 # ------------------------------------------------------------------ W4A16
