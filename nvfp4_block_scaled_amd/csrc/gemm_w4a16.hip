@@ -66,8 +66,14 @@ static int num_cus_or_default() {
   return 256;
 }
 
-// Output tiles of the big kernel: 256 x 256 when those fill the CUs, else 128 x 128.
-static int big_tile_t(int64_t M, int64_t N, int cus) { return ((M + 255) / 256) * ((N + 255) / 256) >= cus ? 4 : 2; }
+// Output tiles of the big kernel: 256 x 256 when those fill the CUs, or when
+// they are fewer but K is long enough that splitting them over all CUs gives
+// each at least kBigSplitMinChunks 64-deep chunks; else 128 x 128.
+constexpr int64_t kBigSplitMinChunks = 48;
+static int big_tile_t(int64_t M, int64_t N, int64_t K, int cus) {
+  const int64_t t4 = ((M + 255) / 256) * ((N + 255) / 256);
+  return t4 >= cus || t4 * (K / 64) >= kBigSplitMinChunks * cus ? 4 : 2;
+}
 
 // One 32-row group per workgroup. Eight waves once there are two groups per
 // CU; with fewer groups, twelve waves keep more loads in flight per CU (more
@@ -98,7 +104,11 @@ static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 
 // Schedule of the big kernel.
 //  * 256 x 256 tiles (one workgroup per CU): G = CUs persistent workgroups
 //    each run full / G whole tiles; the rem = total - full tiles left over are
-//    split along K over all G workgroups.
+//    split along K over all G workgroups. With fewer tiles than CUs, full = 0
+//    and every tile is split that way (on 5120 x 17408 at M = 1024 this took
+//    311 us with 128 x 128 tiles down to 262 us; at 30 chunks per workgroup,
+//    6144 x 5120 at M = 1024, it was slower than 128 x 128 tiles: 122 against
+//    105 us).
 //  * 128 x 128 tiles (two workgroups per CU), at least as many as CUs: one
 //    workgroup per tile up to two per CU, then whole rounds; a CU running two
 //    workgroups loses little against one that runs one, and splitting these
@@ -120,15 +130,15 @@ struct BigSched {
 
 static BigSched big_sched(int64_t M, int64_t N, int64_t K, int cus) {
   BigSched b{};
-  b.T = big_tile_t(M, N, cus);
+  b.T = big_tile_t(M, N, K, cus);
   const int64_t bt = 64 * b.T;
   b.tiles_m = (M + bt - 1) / bt;
   b.tiles_n = (N + bt - 1) / bt;
   b.total = b.tiles_m * b.tiles_n;
   const int64_t slots = (int64_t)cus * (b.T == 4 ? 1 : 2);
   if (b.T == 4) {
-    b.G = b.total < slots ? b.total : slots;
-    b.full = b.total / b.G * b.G;
+    b.G = slots;
+    b.full = b.total / b.G * b.G;             // 0 when the tiles are fewer than the CUs
   } else if (b.total >= cus) {
     b.G = b.total < slots ? b.total : slots;
     b.full = b.total;
