@@ -2,7 +2,9 @@
 //
 // Kernels, chosen by M (and, for decode, by the number of 32-row groups):
 //  * M <= 4 (decode): a weight-streaming kernel on the vector ALUs. A workgroup
-//    owns one 32-row prepared tile group over the whole K; its waves (12, or 8
+//    owns one 32-row prepared tile group over the whole K (at M = 1, groups
+//    left over after whole rounds of resident workgroups are cut into 8- or
+//    16-row workgroups); its waves (12, or 8
 //    once there are two groups per CU) take interleaved 64-wide K tiles, one
 //    contiguous 1 KB tile per wave load. Each lane streams 16 packed bytes (32
 //    codes of one row) per tile, converts code pairs to exact unscaled BF16
@@ -46,6 +48,8 @@ struct Plan {
   int kind;          // 0 = vector decode kernel, 3 = skinny MFMA kernel, 4 = big MFMA kernel
   int dec;           // launch shape of the decode kernel (kDecodeShapes)
   int64_t grid_x;    // workgroups along the output
+  int64_t nfull;     // decode: workgroups of R rows before the tail
+  int tr;            // decode: rows per tail workgroup (0: no tail cut)
 };
 
 // Launch shapes of the vector decode kernel: R weight rows per workgroup, W
@@ -54,6 +58,7 @@ struct DecodeShape {
   int R, W, U;
 };
 constexpr DecodeShape kDecodeShapes[] = {{32, 8, 2}, {32, 12, 2}};
+constexpr int kDecodeWavesPerCu = 32;   // resident waves per CU at M = 1 (at most 64 registers)
 
 constexpr int kDecodeMaxM = 4;
 constexpr int kSkinnyMaxM = 64;
@@ -87,7 +92,22 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K) {
   if (M <= kDecodeMaxM && M * K * 2 <= kDecodeLdsBytes) {
     p.kind = 0;
     p.dec = decode_shape(N, cus);
-    p.grid_x = N / kDecodeShapes[p.dec].R;
+    const DecodeShape &sh = kDecodeShapes[p.dec];
+    p.grid_x = p.nfull = N / sh.R;
+    // Past at least one whole round of resident workgroups, the groups left
+    // over are cut into 8- or 16-row workgroups when those still get a CU
+    // each (M = 1 only: more rows take more registers and fewer workgroups
+    // stay resident). Larger leftovers run faster uncut.
+    if (p.dec == 0 && M == 1) {
+      const int64_t round = (int64_t)cus * (kDecodeWavesPerCu / sh.W);
+      const int64_t full = p.nfull / round * round, rem = p.nfull - full;
+      const int tr = rem * 4 <= cus ? 8 : rem * 2 <= cus ? 16 : 0;
+      if (full > 0 && rem > 0 && tr > 0) {
+        p.tr = tr;
+        p.grid_x = full + rem * (32 / tr);
+        p.nfull = full;
+      }
+    }
   } else if (M <= kSkinnyMaxM) {
     p.kind = 3;
     p.grid_x = N / 32;
@@ -181,18 +201,16 @@ static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
 // once; the row's lanes are added by a butterfly (the same bits in every lane)
 // and the waves in wave order through LDS.
 template <int M, int R, int W, int U>
-__global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restrict__ x, int64_t ldx,
-                                                        const uint8_t *__restrict__ wp, int64_t N, int64_t K,
-                                                        float alpha, const float *alpha_dev,
-                                                        uint16_t *__restrict__ y, int64_t ldy) {
+__device__ __forceinline__ void decode_rows(int64_t b, uint16_t *xs, const uint16_t *__restrict__ x, int64_t ldx,
+                                            const uint8_t *__restrict__ wp, int64_t N, int64_t K, float alpha,
+                                            const float *alpha_dev, uint16_t *__restrict__ y, int64_t ldy) {
   constexpr int TPL = 32 / R;                       // tiles per wave load
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];     // [M][K]
   __shared__ float red[W][M][R];
   const int64_t T = K / 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int tl = lane / (2 * R), h = (lane / R) & 1, r = lane % R;
-  const int64_t g = blockIdx.x / TPL;
-  const int row0 = (int)(blockIdx.x % TPL) * R;      // first row of the workgroup inside the group
+  const int64_t g = b / TPL;
+  const int row0 = (int)(b % TPL) * R;               // first row of the workgroup inside the group
   // Every load is unconditional: the resource of tile group j0 + i W starts at
   // its first tile and ends at the last tile of the row group, so the lanes
   // past it read zeros, and the waits before a compute step can leave the
@@ -295,6 +313,30 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
     for (int w = 1; w < W; w++) v += red[w][m][rr];
     const float al = load_alpha(alpha, alpha_dev);
     y[m * ldy + g * 32 + row0 + rr] = f32_to_bf16_rne(al * v);
+  }
+}
+
+// The decode launch: workgroups below nfull own R rows each (decode_rows
+// above). With TR > 0 the row groups past nfull are cut into TR-row
+// workgroups: nfull covers whole rounds of resident workgroups, and the groups
+// left over would otherwise run alone at the end, one workgroup each on a
+// fraction of the CUs, at the rate one workgroup's loads in flight allow.
+// Cut finer, they spread over more CUs and finish sooner (34816 x 5120 at
+// M = 1, 1088 groups for 1024 resident workgroups: 19.5 against 18.5 us).
+template <int M, int R, int W, int U, int TR>
+__global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                        const uint8_t *__restrict__ wp, int64_t N, int64_t K,
+                                                        float alpha, const float *alpha_dev,
+                                                        uint16_t *__restrict__ y, int64_t ldy, int64_t nfull) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];     // [M][K]
+  const int64_t b = blockIdx.x;
+  if constexpr (TR == 0) {
+    decode_rows<M, R, W, U>(b, xs, x, ldx, wp, N, K, alpha, alpha_dev, y, ldy);
+  } else {
+    if (b < nfull)
+      decode_rows<M, R, W, U>(b, xs, x, ldx, wp, N, K, alpha, alpha_dev, y, ldy);
+    else
+      decode_rows<M, TR, W, U>(nfull * (R / TR) + (b - nfull), xs, x, ldx, wp, N, K, alpha, alpha_dev, y, ldy);
   }
 }
 
@@ -853,17 +895,25 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
 #define NVFP4_DECODE_CASE(D, MM)                                                                               \
   case D * 8 + MM: {                                                                                           \
     constexpr w4a16::DecodeShape sh = w4a16::kDecodeShapes[D];                                                 \
-    hipLaunchKernelGGL((w4a16::decode_kernel<MM, sh.R, sh.W, sh.U>), dim3((unsigned)plan.grid_x),            \
-                       dim3(sh.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy);               \
+    hipLaunchKernelGGL((w4a16::decode_kernel<MM, sh.R, sh.W, sh.U, 0>), dim3((unsigned)plan.grid_x),        \
+                       dim3(sh.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy, plan.nfull);   \
     break;                                                                                                     \
   }
 #define NVFP4_DECODE_SHAPE(D) \
   NVFP4_DECODE_CASE(D, 1) NVFP4_DECODE_CASE(D, 2) NVFP4_DECODE_CASE(D, 3) NVFP4_DECODE_CASE(D, 4)
-    switch (key) {
-      NVFP4_DECODE_SHAPE(0)
-      NVFP4_DECODE_SHAPE(1)
-      default: return NVFP4_ERR_SHAPE;
-    }
+    constexpr w4a16::DecodeShape s0 = w4a16::kDecodeShapes[0];
+    if (plan.tr == 8)
+      hipLaunchKernelGGL((w4a16::decode_kernel<1, s0.R, s0.W, s0.U, 8>), dim3((unsigned)plan.grid_x),
+                         dim3(s0.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy, plan.nfull);
+    else if (plan.tr == 16)
+      hipLaunchKernelGGL((w4a16::decode_kernel<1, s0.R, s0.W, s0.U, 16>), dim3((unsigned)plan.grid_x),
+                         dim3(s0.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy, plan.nfull);
+    else
+      switch (key) {
+        NVFP4_DECODE_SHAPE(0)
+        NVFP4_DECODE_SHAPE(1)
+        default: return NVFP4_ERR_SHAPE;
+      }
 #undef NVFP4_DECODE_SHAPE
 #undef NVFP4_DECODE_CASE
   } else if (plan.kind == 4) {

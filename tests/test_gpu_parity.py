@@ -369,10 +369,14 @@ def test_w4a16_skinny_long_k(M, N, K):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
-@pytest.mark.parametrize("N,K", [(16384, 256), (16416, 1088)])
+@pytest.mark.parametrize("N,K", [(16384, 256), (16416, 1088), (34048, 320), (35968, 192), (36896, 128),
+                                 (65536, 128)])
 def test_w4a16_wide_decode(M, N, K):
     """Many 32-row groups (>= 2 per CU): the one-group-per-workgroup decode path,
-    including a K that leaves the last tile batch partly empty; full check."""
+    including a K that leaves the last tile batch partly empty; full check. With
+    256 CUs and M = 1, one whole round of 1024 workgroups runs first and the groups
+    left over are cut: 34048 rows (40 left) into 8-row workgroups, 35968 (100 left)
+    into 16-row ones; 36896 (129 left) and 65536 (two whole rounds) are not cut."""
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 7 + N)
     out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
     torch.cuda.synchronize()
