@@ -495,10 +495,15 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
 //    (E2M1 -> FP32, times the E4M3 scale, -> BF16) one MFMA step ahead.
 //  * x: the tile's 64T rows x 64 k BF16 (8T KB) are loaded one chunk ahead with
 //    coalesced 16-byte loads (rows past M read as zero through the buffer range
-//    check), written into one of two LDS buffers with 16-byte units XOR-swizzled
-//    by row, and read back as MFMA fragments without bank conflicts. One LDS-only
-//    barrier per chunk; the x loads are issued before the W loads so waiting for
-//    them does not wait for the W prefetch.
+//    check), written into one of two LDS buffers and read back as MFMA
+//    fragments. The 16-byte units of a row are XOR-swizzled by row / 2: an LDS
+//    cycle serves 16 lanes of a 16-byte read (16 consecutive rows of one unit),
+//    and with 128-byte rows on 64 four-byte banks a swizzle by row alone put
+//    rows r and r + 8 on the same banks (the bank-conflict counter read as many
+//    cycles as the LDS instructions took; now zero). One LDS-only barrier per
+//    chunk; the x loads are issued before the W loads (kept in that order by a
+//    scheduling barrier: loads complete in order, so waiting for x before its
+//    LDS store leaves the W prefetch in flight).
 //  * One scheduling region per MFMA step, as in the W4A4 kernel.
 namespace big {
 
@@ -585,7 +590,7 @@ __device__ __forceinline__ void store_x(uint8_t *buf, const XRegs<T> &xr) {
   for (int i = 0; i < 2 * T; i++) {
     const int q = (int)threadIdx.x + kThreads * i;
     const int row = q >> 3, u = q & 7;
-    *reinterpret_cast<u32x4_t *>(buf + row * 128 + ((u ^ (row & 7)) << 4)) = xr.v[i];
+    *reinterpret_cast<u32x4_t *>(buf + row * 128 + ((u ^ ((row >> 1) & 7)) << 4)) = xr.v[i];
   }
 }
 
@@ -603,7 +608,7 @@ __device__ __forceinline__ void read_x(const uint8_t *buf, int s, int wm, bf16x8
 #pragma unroll
   for (int i = 0; i < T; i++) {
     const int row = wm * 32 * T + 32 * i + r;
-    a[i] = *reinterpret_cast<const bf16x8_t *>(buf + row * 128 + ((u ^ (row & 7)) << 4));
+    a[i] = *reinterpret_cast<const bf16x8_t *>(buf + row * 128 + ((u ^ ((row >> 1) & 7)) << 4));
   }
 }
 
@@ -632,6 +637,7 @@ __device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uin
   constexpr int kValu = 16 / T + 1;                 // dequant instructions per MFMA, rounded up
   XRegs<T> xr;
   load_x<T>(tb, ldx, c + 1, nch, xr);
+  __builtin_amdgcn_sched_barrier(0);   // x first (see above)
   load_w<T>(tb, ow, ows, c + 2, nch, f[(P + 2) % 3]);
   uint8_t *cur = smem + (c & 1) * (64 * T * 128);
   uint8_t *nxt = smem + ((c + 1) & 1) * (64 * T * 128);
@@ -654,7 +660,7 @@ __device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uin
       if (s < 3) a[i] = an[i];
       b[i] = bn[i];
     }
-    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 4 * T, 0);
+    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * T, 0);
 #pragma unroll
     for (int k = 0; k < T * T; k++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
