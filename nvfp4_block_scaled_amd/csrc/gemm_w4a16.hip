@@ -177,11 +177,20 @@ static BigSched big_sched(int64_t M, int64_t N, int64_t K, int cus) {
 
 static size_t big_partial_bytes(int T) { return (size_t)T * T * 16384; }   // 4 waves x T x T x 64 lanes x 16 FP32
 
+// The big kernel's workspace: the split ranges' partial tiles (2 per
+// workgroup, when tiles are split), then, for 256 x 256 tiles, x in fragment
+// order over whole output tiles of rows (xmt 32-row tiles).
+static size_t big_partials_span(const BigSched &b) {
+  return b.rem > 0 ? ((size_t)b.G * 2 * big_partial_bytes(b.T) + 255) / 256 * 256 : 0;
+}
+static int64_t big_xmt(const BigSched &b) { return b.T == 4 ? b.tiles_m * 2 * b.T : 0; }
+static size_t big_xf_bytes(const BigSched &b, int64_t K) { return (size_t)big_xmt(b) * 32 * (size_t)K * 2; }
+
 static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
   if (p.kind == 3) return M > kSkinnyDirectMaxM ? skinny_x_bytes(M, K) : 0;
   if (p.kind == 4) {
     const BigSched b = big_sched(M, N, K, num_cus_or_default());
-    return b.rem > 0 ? (size_t)b.G * 2 * big_partial_bytes(b.T) : 0;
+    return big_partials_span(b) + big_xf_bytes(b, K);
   }
   return 0;
 }
@@ -372,21 +381,19 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
 
 // x [M][ldx] BF16 -> fragment order: unit u = ((t * 4 + s) * MT + mt) * 64 + lane
 // holds x[32 mt + (lane & 31)][64 t + 32 (lane >> 5) + 8 s .. +8] (zero past M).
+// Workgroup (t, mt) moves the 32 rows x 64 k block: thread q reads 16 bytes
+// of row q / 8 (eight threads per 128-byte row piece) and writes them to
+// their unit.
 __global__ __launch_bounds__(256) void tile_x_kernel(const uint16_t *__restrict__ x, int64_t ldx, int64_t M,
                                                      int64_t K, int MT, u32x4_t *__restrict__ xf) {
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t units = K / 64 * 4 * MT * 64;
-  if (u >= units) return;
-  const int lane = (int)(u & 63);
-  const int64_t rest = u >> 6;
-  const int mt = (int)(rest % MT);
-  const int64_t ts = rest / MT;
-  const int s = (int)(ts & 3);
-  const int64_t t = ts >> 2;
-  const int64_t row = 32 * mt + (lane & 31);
+  const int64_t t = blockIdx.x / MT;
+  const int mt = (int)(blockIdx.x - t * MT);
+  const int q = threadIdx.x, r = q >> 3, piece = q & 7;    // piece = 4 h + s
+  const int64_t row = 32 * (int64_t)mt + r;
   u32x4_t v = {0u, 0u, 0u, 0u};
-  if (row < M) v = *reinterpret_cast<const u32x4_t *>(x + row * ldx + t * 64 + 32 * (lane >> 5) + 8 * s);
-  xf[u] = v;
+  if (row < M) v = *reinterpret_cast<const u32x4_t *>(x + row * ldx + t * 64 + piece * 8);
+  const int h = piece >> 2, s = piece & 3;
+  xf[((t * 4 + s) * MT + mt) * 64 + 32 * h + r] = v;
 }
 
 template <int MT, bool XF, int W>
@@ -522,6 +529,8 @@ struct Params {
   int full;          // tiles [0, full) run whole, persistent over gridDim.x workgroups
   int rem;           // tiles [full, full + rem) are split along K over all workgroups
   float *partials;   // 2 slots per workgroup of partial tiles (rem > 0)
+  const uint8_t *xf; // x in MFMA fragment order (tile_x_kernel with xmt row tiles)
+  int xmt;           // 32-row tiles of xf: M rounded up to whole output tiles
 };
 
 // One partial tile: 4 waves x T x T MFMA tiles x 64 lanes x 16 FP32, in the
@@ -731,6 +740,119 @@ __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t
   }
 }
 
+// The main loop with x read straight into registers from its fragment-order
+// copy (xf), like the A operand of the W4A4 kernel: chunk c, step s of row tile
+// rt is the 1 KB at ((c * 4 + s) * xmt + rt) * 1024, one 16-byte unit per lane.
+// x fragments go through a six-slot register ring indexed by the global step
+// (the loop body is three chunks, twelve steps), each loaded five steps before
+// its MFMAs into the slot the previous step freed; W keeps its three-chunk ring.
+// No LDS and no barriers.
+template <int T>
+struct XRing {
+  u32x4_t v[6][T];
+};
+
+template <int T>
+__device__ __forceinline__ void load_xf(__amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[T], int64_t c, int s, int xmt,
+                                        u32x4_t (&v)[T]) {
+  const int so = (int)((c * 4 + s) * xmt * 1024);
+#pragma unroll
+  for (int i = 0; i < T; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], so, 0);
+}
+
+template <int P, int T>
+__device__ __forceinline__ void chunk_d(const TileBase &tb, __amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[T],
+                                        int xmt, const uint32_t (&ow)[T], const uint32_t (&ows)[T], int64_t c,
+                                        int64_t nch, WFrags<T> (&f)[3], f32x2_t (&sc)[T], XRing<T> &xr,
+                                        bf16x8_t (&b)[T], f32x16_t (&acc)[T][T]) {
+  constexpr int kValu = 16 / T + 1;
+  const bool in2 = c + 2 < nch;
+  WFrags<T> &f2 = f[(P + 2) % 3];
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const int g = 4 * P + s;                      // step in the three-chunk body
+    // x of step g + 5 into the slot step g - 1 used
+    load_xf<T>(rx, ox, c + (s + 5) / 4, (s + 5) % 4, xmt, xr.v[(g + 5) % 6]);
+    if (s == 0) {
+      const __amdgpu_buffer_rsrc_t rw = rsrc(tb.w, in2 ? tb.w_bytes : 0);
+#pragma unroll
+      for (int j = 0; j < T; j++) f2.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, ow[j], (int)((c + 2) * 1024), 0);
+    } else if (s == 1) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc(tb.ws, in2 ? tb.ws_bytes : 0);
+#pragma unroll
+      for (int j = 0; j < T; j++) f2.ws[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ows[j], (int)((c + 2) * 128), 0);
+    }
+    bf16x8_t bn[T];
+    if (s < 3) {
+      deq_w<T>(f[P], sc, s + 1, bn);
+    } else {
+      scales_of<T>(f[(P + 1) % 3], sc);
+      deq_w<T>(f[(P + 1) % 3], sc, 0, bn);
+    }
+#pragma unroll
+    for (int i = 0; i < T; i++)
+#pragma unroll
+      for (int j = 0; j < T; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xr.v[g % 6][i]), b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < T; j++) b[j] = bn[j];
+    if (s < 2)   // this step's loads first
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 * T, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(0x020, T, 0);
+#pragma unroll
+    for (int k = 0; k < T * T; k++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void tile_mainloop_d(const Params &p, int tile, int64_t c0, int64_t n,
+                                                const uint32_t (&ow)[T], const uint32_t (&ows)[T], int wm,
+                                                f32x16_t (&acc)[T][T], int64_t &m0, int64_t &n0) {
+  constexpr int BT = 64 * T;
+  const int64_t kt = p.K / 64;
+  int tm, tn;
+  tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
+  m0 = (int64_t)tm * BT;
+  n0 = (int64_t)tn * BT;
+  TileBase tb;
+  tb.w = p.wp + ((n0 >> 5) * kt + c0) * 1024;
+  tb.w_bytes = (p.N - n0) / 32 * kt * 1024 - c0 * 1024;
+  tb.ws = p.wp + p.N * p.K / 2 + ((n0 >> 5) * kt + c0) * 128;
+  tb.ws_bytes = (p.N - n0) / 32 * kt * 128 - c0 * 128;
+  // x: chunks [c0, c0 + n) of the tile's row tiles; loads past the range read zero
+  const int64_t xchunk = (int64_t)4 * p.xmt * 1024;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xf + c0 * xchunk, n * xchunk);
+  const int lane = threadIdx.x & 63;
+  uint32_t ox[T];
+#pragma unroll
+  for (int i = 0; i < T; i++) ox[i] = (uint32_t)(((m0 >> 5) + wm * T + i) * 1024 + lane * 16);
+
+#pragma unroll
+  for (int i = 0; i < T; i++)
+#pragma unroll
+    for (int j = 0; j < T; j++) acc[i][j] = f32x16_t{};
+  WFrags<T> f[3];
+  f32x2_t sc[T];
+  bf16x8_t b[T];
+  XRing<T> xr;
+#pragma unroll
+  for (int s = 0; s < 5; s++) load_xf<T>(rx, ox, s / 4, s % 4, p.xmt, xr.v[s]);
+  load_w<T>(tb, ow, ows, 0, n, f[0]);
+  load_w<T>(tb, ow, ows, 1, n, f[1]);
+  scales_of<T>(f[0], sc);
+  deq_w<T>(f[0], sc, 0, b);
+  for (int64_t c = 0; c < n; c += 3) {
+    chunk_d<0, T>(tb, rx, ox, p.xmt, ow, ows, c, n, f, sc, xr, b, acc);
+    chunk_d<1, T>(tb, rx, ox, p.xmt, ow, ows, c + 1, n, f, sc, xr, b, acc);
+    chunk_d<2, T>(tb, rx, ox, p.xmt, ow, ows, c + 2, n, f, sc, xr, b, acc);
+  }
+}
+
 // Epilogue of a whole tile: per wave 32 x 32T staging of BF16 in LDS (after
 // every wave is done with x), then 16-byte row pieces.
 template <int T>
@@ -776,7 +898,8 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
 template <int T>
 __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p) {
   constexpr int BT = 64 * T;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BT * 128];   // two x chunks; reused by the epilogue
+  // T = 2: two x chunks (the LDS main loop); T = 4: the epilogue's BF16 staging
+  __shared__ __attribute__((aligned(16))) uint8_t smem[T == 4 ? 4 * 32 * 32 * T * 2 : 2 * BT * 128];
   const int t = threadIdx.x, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
   const int lane = t & 63, r = lane & 31;
   const int G = gridDim.x;
@@ -793,7 +916,10 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p)
   f32x16_t acc[T][T];
   int64_t m0, n0;
   for (int tile = pid; tile < p.full; tile += G) {
-    tile_mainloop<T>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
+    if constexpr (T == 4)
+      tile_mainloop_d<T>(p, tile, 0, nch, ow, ows, wm, acc, m0, n0);
+    else
+      tile_mainloop<T>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
     tile_epilogue<T>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
   }
   if (p.rem > 0) {
@@ -801,7 +927,10 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p)
     split_range(pid, G, (int64_t)p.rem * nch, s, e);
     for (int seg = 0; s < e; seg++) {
       const int64_t rho = s / nch, c0 = s - rho * nch, c1 = min(nch, c0 + (e - s));
-      tile_mainloop<T>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm, acc, m0, n0);
+      if constexpr (T == 4)
+        tile_mainloop_d<T>(p, p.full + (int)rho, c0, c1 - c0, ow, ows, wm, acc, m0, n0);
+      else
+        tile_mainloop<T>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm, acc, m0, n0);
       float *dst = p.partials + ((int64_t)pid * 2 + seg) * partial_floats<T>() + (int64_t)wave * T * T * 1024 +
                    lane * 16;
 #pragma unroll
@@ -923,12 +1052,20 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
 #undef NVFP4_DECODE_SHAPE
 #undef NVFP4_DECODE_CASE
   } else if (plan.kind == 4) {
-    if ((int64_t)256 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
     const w4a16::BigSched b = w4a16::big_sched(M, N, K, di.num_cus);
-    if (b.total > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
+    // fragment-order x: 32-bit offsets inside it
+    if (b.total > 0x7FFFFFFF || w4a16::big_xf_bytes(b, K) > 0x7FFFFFFFull) return NVFP4_ERR_SHAPE;
+    if (b.T == 2 && (int64_t)128 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;   // LDS path: 32-bit x offsets
+    const int64_t xmt = w4a16::big_xmt(b);
+    uint8_t *xf = xmt > 0 ? static_cast<uint8_t *>(ws) + w4a16::big_partials_span(b) : nullptr;
+    if (xmt > 0) {
+      hipLaunchKernelGGL(w4a16::tile_x_kernel, dim3((unsigned)(K / 64 * xmt)), dim3(256), 0, s, x, ldx, M, K,
+                         (int)xmt, reinterpret_cast<u32x4_t *>(xf));
+      NVFP4_LAUNCH_CHECK();
+    }
     w4a16::big::Params bp{x,     ldx,           w_prep,        y,           ldy,          M,
                           N,     K,             alpha,         alpha_dev,   (int)b.tiles_m, (int)b.tiles_n,
-                          (int)b.full, (int)b.rem, static_cast<float *>(ws)};
+                          (int)b.full, (int)b.rem, static_cast<float *>(ws), xf, (int)xmt};
     const unsigned grid = (unsigned)b.G;
     if (b.T == 4)
       hipLaunchKernelGGL(w4a16::big::big_kernel<4>, dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);
@@ -949,9 +1086,8 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     const bool xf_path = M > w4a16::kSkinnyDirectMaxM;
     uint8_t *xf = static_cast<uint8_t *>(ws);
     if (xf_path) {
-      const int64_t units = K / 64 * 4 * MT * 64;
-      hipLaunchKernelGGL(w4a16::tile_x_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, x, ldx, M, K,
-                         MT, reinterpret_cast<u32x4_t *>(xf));
+      hipLaunchKernelGGL(w4a16::tile_x_kernel, dim3((unsigned)(K / 64 * MT)), dim3(256), 0, s, x, ldx, M, K, MT,
+                         reinterpret_cast<u32x4_t *>(xf));
       NVFP4_LAUNCH_CHECK();
     }
     const unsigned grid = (unsigned)plan.grid_x;
