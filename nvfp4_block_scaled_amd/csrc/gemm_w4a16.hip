@@ -73,11 +73,13 @@ static int num_cus_or_default() {
 
 // Output tiles of the big kernel: 256 x 256 when those fill the CUs, or when
 // they are fewer but K is long enough that splitting them over all CUs gives
-// each at least kBigSplitMinChunks 64-deep chunks; else 128 x 128.
-constexpr int64_t kBigSplitMinChunks = 48;
+// each at least kBigSplitMinChunks 64-deep chunks and x's rows fill at least
+// 7/8 of the tile rows; else 128 x 128.
+constexpr int64_t kBigSplitMinChunks = 32;
 static int big_tile_t(int64_t M, int64_t N, int64_t K, int cus) {
-  const int64_t t4 = ((M + 255) / 256) * ((N + 255) / 256);
-  return t4 >= cus || t4 * (K / 64) >= kBigSplitMinChunks * cus ? 4 : 2;
+  const int64_t tm4 = (M + 255) / 256, t4 = tm4 * ((N + 255) / 256);
+  if (t4 >= cus) return 4;
+  return t4 * (K / 64) >= kBigSplitMinChunks * cus && 8 * M >= 7 * 256 * tm4 ? 4 : 2;
 }
 
 // One 32-row group per workgroup. Eight waves once there are two groups per
@@ -125,10 +127,12 @@ static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 
 //  * 256 x 256 tiles (one workgroup per CU): G = CUs persistent workgroups
 //    each run full / G whole tiles; the rem = total - full tiles left over are
 //    split along K over all G workgroups. With fewer tiles than CUs, full = 0
-//    and every tile is split that way (on 5120 x 17408 at M = 1024 this took
-//    311 us with 128 x 128 tiles down to 262 us; at 30 chunks per workgroup,
-//    6144 x 5120 at M = 1024, it was slower than 128 x 128 tiles: 122 against
-//    105 us).
+//    and every tile is split that way (with x staged through LDS, this took
+//    5120 x 17408 at M = 1024 from 311 us with 128 x 128 tiles to 262 us; with
+//    x read straight into registers, a threshold of 32 rather than 48 chunks
+//    per workgroup took 5120 x 17408 at M = 512 from 155 to 131 us, while 24
+//    made 6144 x 5120 at M = 1024, 30 chunks each, slower: 113 against 100 us;
+//    at M = 384, a quarter of the 256-row tiles empty, it was slower too).
 //  * 128 x 128 tiles (two workgroups per CU), at least as many as CUs: one
 //    workgroup per tile up to two per CU, then whole rounds; a CU running two
 //    workgroups loses little against one that runs one, and splitting these
