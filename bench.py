@@ -270,6 +270,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the W4A16 M = 1 decode shapes (one JSON line; for profiling the decode kernels)")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="only the W4A16 M > 1 layer sweep (one JSON line; for profiling the MFMA kernels)")
     ap.add_argument("--large", action="store_true", help="also time the 32768^3 square (about 4 GiB of device memory)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
@@ -292,6 +294,11 @@ def main():
     if args.decode_only:
         import synth
         print(json.dumps({"w4a16_m1": [w4a16_m1(nv, j) for j in range(len(synth.DECODE_SHAPES))]}), flush=True)
+        return
+    if args.sweep_only:
+        import synth
+        print(json.dumps({"w4a16_m_sweep": [r for j in range(len(synth.DECODE_SHAPES))
+                                            for r in w4a16_m_sweep(nv, j, args.steps, args.warmup)]}), flush=True)
         return
     S = args.size
     log(f"[bench] W4A4 {S}^3 bf16: {args.warmup} warmup + {args.steps} timed steps")
@@ -333,7 +340,8 @@ def main():
         pf = prefill(nv, max(5, args.steps // 2), args.warmup)
         log(f"[bench] prefill: {pf}")
         extras["prefill_w4a4"] = pf
-        extras["w4a16_m_sweep"] = w4a16_m_sweep(nv, 2, args.steps, args.warmup)
+        extras["w4a16_m_sweep"] = [r for j in range(len(synth.DECODE_SHAPES))
+                                   for r in w4a16_m_sweep(nv, j, args.steps, args.warmup)]
         sweep = {}
         for s2 in (2048, 4096):
             m2, t2 = w4a4_square(nv, s2, args.steps, args.warmup)

@@ -975,15 +975,37 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
     if (e > lo || first == G - 1) break;
     first++;
   }
+  // the contributing workgroups are first .. last (ranges are contiguous)
+  int64_t last = first;
+  for (;;) {
+    int64_t s, e;
+    if (last + 1 >= G) break;
+    split_range(last + 1, G, units, s, e);
+    if (s >= hi) break;
+    last++;
+  }
+  // Their partials are loaded four at a time, all four in flight together;
+  // a slot with no partial (past last, or an empty range) reads zero through
+  // the buffer range check, and adding +0 to a sum that started at +0 changes
+  // nothing, so the sum is the same as one over the contributors in order.
+  const int64_t pbytes = (int64_t)G * 2 * partial_floats<T>() * 4;
+  const __amdgpu_buffer_rsrc_t rp = rsrc(p.partials, pbytes);
   const int64_t off = (int64_t)part * 1024 + lane * 16 + 4 * q;
   f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t w = first; w < G; w++) {
-    int64_t s, e;
-    split_range(w, G, units, s, e);
-    if (s >= hi) break;
-    if (e <= lo || s == e) continue;
-    const int seg = s >= lo ? 0 : 1;
-    v += *reinterpret_cast<const f32x4_t *>(p.partials + (w * 2 + seg) * partial_floats<T>() + off);
+  for (int64_t w0 = first; w0 <= last; w0 += 4) {
+    f32x4_t t[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int64_t w = w0 + k;
+      int64_t s, e;
+      split_range(w, G, units, s, e);
+      const bool ok = w <= last && e > lo && s < e;
+      const int seg = s >= lo ? 0 : 1;
+      const uint32_t o = ok ? (uint32_t)(((w * 2 + seg) * partial_floats<T>() + off) * 4) : (uint32_t)pbytes;
+      t[k] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, o, 0, 0));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) v += t[k];
   }
   const float alpha = load_alpha(p.alpha, p.alpha_dev);
   const int64_t col = n0 + wn * 32 * T + 32 * j + r;
