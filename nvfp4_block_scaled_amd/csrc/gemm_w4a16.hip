@@ -22,7 +22,7 @@
 //    kernel, the decode structure with v_mfma_f32_32x32x16_bf16 on one or two
 //    32-row x tiles (below).
 //  * M > 64: the big MFMA kernel, built like the W4A4 kernel (below), on
-//    persistent workgroups. Output tiles that do not fill whole rounds of the
+//    persistent workgroups over 256 x 256, 128 x 256 or 128 x 128 tiles. Output tiles that do not fill whole rounds of the
 //    CUs, or are fewer than the CUs, are split along K: each split range writes
 //    an FP32 partial tile to the workspace and a fix-up kernel adds the partials
 //    in workgroup order and applies the epilogue, so the result does not depend
@@ -71,15 +71,29 @@ static int num_cus_or_default() {
   return 256;
 }
 
-// Output tiles of the big kernel: 256 x 256 when those fill the CUs, or when
-// they are fewer but K is long enough that splitting them over all CUs gives
-// each at least kBigSplitMinChunks 64-deep chunks and x's rows fill at least
-// 7/8 of the tile rows; else 128 x 128.
+// Output tiles of the big kernel, as MFMA tiles per wave (TM x TN; the
+// workgroup tile is 64 TM x 64 TN):
+//  * 4 x 4 (256 x 256) when those fill the CUs, or when they are fewer but K
+//    is long enough that splitting them over all CUs gives each at least
+//    kBigSplitMinChunks 64-deep chunks and x's rows fill at least 7/8 of the
+//    tile rows;
+//  * else 2 x 4 (128 x 256) when those fill the CUs or split that way;
+//  * else 2 x 2 (128 x 128).
 constexpr int64_t kBigSplitMinChunks = 32;
-static int big_tile_t(int64_t M, int64_t N, int64_t K, int cus) {
-  const int64_t tm4 = (M + 255) / 256, t4 = tm4 * ((N + 255) / 256);
-  if (t4 >= cus) return 4;
-  return t4 * (K / 64) >= kBigSplitMinChunks * cus && 8 * M >= 7 * 256 * tm4 ? 4 : 2;
+static void big_tile_shape(int64_t M, int64_t N, int64_t K, int cus, int &TM, int &TN) {
+  const int64_t nch = K / 64;
+  const int64_t tm4 = (M + 255) / 256, t44 = tm4 * ((N + 255) / 256);
+  if (t44 >= cus || (t44 * nch >= kBigSplitMinChunks * cus && 8 * M >= 7 * 256 * tm4)) {
+    TM = TN = 4;
+    return;
+  }
+  const int64_t t24 = ((M + 127) / 128) * ((N + 255) / 256);
+  if (t24 >= cus || t24 * nch >= kBigSplitMinChunks * cus) {
+    TM = 2;
+    TN = 4;
+    return;
+  }
+  TM = TN = 2;
 }
 
 // One 32-row group per workgroup. Eight waves once there are two groups per
@@ -123,7 +137,7 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K) {
 // roundup32(M) rows x K BF16.
 static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 32 * 32) * (size_t)K * 2; }
 
-// Schedule of the big kernel.
+// Schedule of the big kernel (tile shapes: big_tile_shape).
 //  * 256 x 256 tiles (one workgroup per CU): G = CUs persistent workgroups
 //    each run full / G whole tiles; the rem = total - full tiles left over are
 //    split along K over all G workgroups. With fewer tiles than CUs, full = 0
@@ -133,6 +147,11 @@ static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 
 //    per workgroup took 5120 x 17408 at M = 512 from 155 to 131 us, while 24
 //    made 6144 x 5120 at M = 1024, 30 chunks each, slower: 113 against 100 us;
 //    at M = 384, a quarter of the 256-row tiles empty, it was slower too).
+//  * 128 x 256 tiles (one workgroup per CU, x read directly) follow the same
+//    rules: 34816 x 5120 at M = 128 took 84.5 us against 92.6 with 128 x 128
+//    tiles, 5120 x 17408 at M = 192 80.8 against 86.8. A wave's two MFMA rows
+//    share each dequantized W fragment, so these tiles spend about nine vector
+//    instructions per MFMA against five for 256 x 256.
 //  * 128 x 128 tiles (two workgroups per CU), at least as many as CUs: one
 //    workgroup per tile up to two per CU, then whole rounds; a CU running two
 //    workgroups loses little against one that runs one, and splitting these
@@ -148,19 +167,19 @@ static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 
 constexpr int kMaxKSplit = 8;
 
 struct BigSched {
-  int T;
+  int TM, TN;
   int64_t tiles_m, tiles_n, total, G, full, rem;
 };
 
 static BigSched big_sched(int64_t M, int64_t N, int64_t K, int cus) {
   BigSched b{};
-  b.T = big_tile_t(M, N, K, cus);
-  const int64_t bt = 64 * b.T;
-  b.tiles_m = (M + bt - 1) / bt;
-  b.tiles_n = (N + bt - 1) / bt;
+  big_tile_shape(M, N, K, cus, b.TM, b.TN);
+  b.tiles_m = (M + 64 * b.TM - 1) / (64 * b.TM);
+  b.tiles_n = (N + 64 * b.TN - 1) / (64 * b.TN);
   b.total = b.tiles_m * b.tiles_n;
-  const int64_t slots = (int64_t)cus * (b.T == 4 ? 1 : 2);
-  if (b.T == 4) {
+  const bool direct = b.TM * b.TN >= 8;       // one workgroup per CU
+  const int64_t slots = (int64_t)cus * (direct ? 1 : 2);
+  if (direct) {
     b.G = slots;
     b.full = b.total / b.G * b.G;             // 0 when the tiles are fewer than the CUs
   } else if (b.total >= cus) {
@@ -179,15 +198,16 @@ static BigSched big_sched(int64_t M, int64_t N, int64_t K, int cus) {
   return b;
 }
 
-static size_t big_partial_bytes(int T) { return (size_t)T * T * 16384; }   // 4 waves x T x T x 64 lanes x 16 FP32
+// 4 waves x TM x TN MFMA tiles x 64 lanes x 16 FP32
+static size_t big_partial_bytes(const BigSched &b) { return (size_t)b.TM * b.TN * 16384; }
 
 // The big kernel's workspace: the split ranges' partial tiles (2 per
-// workgroup, when tiles are split), then, for 256 x 256 tiles, x in fragment
-// order over whole output tiles of rows (xmt 32-row tiles).
+// workgroup, when tiles are split), then, for the tiles that read x directly,
+// x in fragment order over whole output tiles of rows (xmt 32-row tiles).
 static size_t big_partials_span(const BigSched &b) {
-  return b.rem > 0 ? ((size_t)b.G * 2 * big_partial_bytes(b.T) + 255) / 256 * 256 : 0;
+  return b.rem > 0 ? ((size_t)b.G * 2 * big_partial_bytes(b) + 255) / 256 * 256 : 0;
 }
-static int64_t big_xmt(const BigSched &b) { return b.T == 4 ? b.tiles_m * 2 * b.T : 0; }
+static int64_t big_xmt(const BigSched &b) { return b.TM * b.TN >= 8 ? b.tiles_m * 2 * b.TM : 0; }
 static size_t big_xf_bytes(const BigSched &b, int64_t K) { return (size_t)big_xmt(b) * 32 * (size_t)K * 2; }
 
 static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
@@ -498,13 +518,16 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
 // ---------------------------------------------------------------- big MFMA kernel (M > 64)
 
 // The W4A4 kernel's structure with x in BF16. Persistent workgroups of 4 waves
-// (2 x 2) over 64T x 64T output tiles (T = 4: 256 x 256, one workgroup per CU;
-// T = 2: 128 x 128), each wave owning T x T v_mfma_f32_32x32x16_bf16 tiles.
-//  * W: each wave loads its T column groups' fragments of a 64-wide K chunk
+// (2 x 2) over 64TM x 64TN output tiles, each wave owning TM x TN
+// v_mfma_f32_32x32x16_bf16 tiles: 4 x 4 (256 x 256) and 2 x 4 (128 x 256), one
+// workgroup per CU, read x in fragment order straight into registers
+// (tile_mainloop_d); 2 x 2 (128 x 128, two workgroups per CU) stages x
+// through LDS (tile_mainloop).
+//  * W: each wave loads its TN column groups' fragments of a 64-wide K chunk
 //    straight into registers (one contiguous 1 KB each plus a scale word), two
 //    chunks ahead in a three-deep ring, and dequantizes them exactly to BF16
 //    (E2M1 -> FP32, times the E4M3 scale, -> BF16) one MFMA step ahead.
-//  * x: the tile's 64T rows x 64 k BF16 (8T KB) are loaded one chunk ahead with
+//  * x through LDS: the tile's 128 rows x 64 k BF16 (16 KB) are loaded one chunk ahead with
 //    coalesced 16-byte loads (rows past M read as zero through the buffer range
 //    check), written into one of two LDS buffers and read back as MFMA
 //    fragments. The 16-byte units of a row are XOR-swizzled by row / 2: an LDS
@@ -537,11 +560,11 @@ struct Params {
   int xmt;           // 32-row tiles of xf: M rounded up to whole output tiles
 };
 
-// One partial tile: 4 waves x T x T MFMA tiles x 64 lanes x 16 FP32, in the
+// One partial tile: 4 waves x TM x TN MFMA tiles x 64 lanes x 16 FP32, in the
 // accumulator layout.
-template <int T>
+template <int TM, int TN>
 constexpr int64_t partial_floats() {
-  return (int64_t)4 * T * T * 64 * 16;
+  return (int64_t)4 * TM * TN * 64 * 16;
 }
 
 // Chunk range [s, e) of workgroup `pid` in the split part: the rem x nch
@@ -764,48 +787,48 @@ __device__ __forceinline__ void load_xf(__amdgpu_buffer_rsrc_t rx, const uint32_
   for (int i = 0; i < T; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], so, 0);
 }
 
-template <int P, int T>
-__device__ __forceinline__ void chunk_d(const TileBase &tb, __amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[T],
-                                        int xmt, const uint32_t (&ow)[T], const uint32_t (&ows)[T], int64_t c,
-                                        int64_t nch, WFrags<T> (&f)[3], f32x2_t (&sc)[T], XRing<T> &xr,
-                                        bf16x8_t (&b)[T], f32x16_t (&acc)[T][T]) {
-  constexpr int kValu = 16 / T + 1;
+template <int P, int TM, int TN>
+__device__ __forceinline__ void chunk_d(const TileBase &tb, __amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[TM],
+                                        int xmt, const uint32_t (&ow)[TN], const uint32_t (&ows)[TN], int64_t c,
+                                        int64_t nch, WFrags<TN> (&f)[3], f32x2_t (&sc)[TN], XRing<TM> &xr,
+                                        bf16x8_t (&b)[TN], f32x16_t (&acc)[TM][TN]) {
+  constexpr int kValu = 16 / TM + 1;              // dequant instructions per MFMA, rounded up
   const bool in2 = c + 2 < nch;
-  WFrags<T> &f2 = f[(P + 2) % 3];
+  WFrags<TN> &f2 = f[(P + 2) % 3];
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     const int g = 4 * P + s;                      // step in the three-chunk body
     // x of step g + 5 into the slot step g - 1 used
-    load_xf<T>(rx, ox, c + (s + 5) / 4, (s + 5) % 4, xmt, xr.v[(g + 5) % 6]);
+    load_xf<TM>(rx, ox, c + (s + 5) / 4, (s + 5) % 4, xmt, xr.v[(g + 5) % 6]);
     if (s == 0) {
       const __amdgpu_buffer_rsrc_t rw = rsrc(tb.w, in2 ? tb.w_bytes : 0);
 #pragma unroll
-      for (int j = 0; j < T; j++) f2.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, ow[j], (int)((c + 2) * 1024), 0);
+      for (int j = 0; j < TN; j++) f2.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, ow[j], (int)((c + 2) * 1024), 0);
     } else if (s == 1) {
       const __amdgpu_buffer_rsrc_t rs = rsrc(tb.ws, in2 ? tb.ws_bytes : 0);
 #pragma unroll
-      for (int j = 0; j < T; j++) f2.ws[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ows[j], (int)((c + 2) * 128), 0);
+      for (int j = 0; j < TN; j++) f2.ws[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ows[j], (int)((c + 2) * 128), 0);
     }
-    bf16x8_t bn[T];
+    bf16x8_t bn[TN];
     if (s < 3) {
-      deq_w<T>(f[P], sc, s + 1, bn);
+      deq_w<TN>(f[P], sc, s + 1, bn);
     } else {
-      scales_of<T>(f[(P + 1) % 3], sc);
-      deq_w<T>(f[(P + 1) % 3], sc, 0, bn);
+      scales_of<TN>(f[(P + 1) % 3], sc);
+      deq_w<TN>(f[(P + 1) % 3], sc, 0, bn);
     }
 #pragma unroll
-    for (int i = 0; i < T; i++)
+    for (int i = 0; i < TM; i++)
 #pragma unroll
-      for (int j = 0; j < T; j++)
+      for (int j = 0; j < TN; j++)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xr.v[g % 6][i]), b[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < T; j++) b[j] = bn[j];
+    for (int j = 0; j < TN; j++) b[j] = bn[j];
     if (s < 2)   // this step's loads first
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 * T, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, TM + TN, 0);
     else
-      __builtin_amdgcn_sched_group_barrier(0x020, T, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, TM, 0);
 #pragma unroll
-    for (int k = 0; k < T * T; k++) {
+    for (int k = 0; k < TM * TN; k++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
     }
@@ -813,16 +836,15 @@ __device__ __forceinline__ void chunk_d(const TileBase &tb, __amdgpu_buffer_rsrc
   }
 }
 
-template <int T>
+template <int TM, int TN>
 __device__ __forceinline__ void tile_mainloop_d(const Params &p, int tile, int64_t c0, int64_t n,
-                                                const uint32_t (&ow)[T], const uint32_t (&ows)[T], int wm,
-                                                f32x16_t (&acc)[T][T], int64_t &m0, int64_t &n0) {
-  constexpr int BT = 64 * T;
+                                                const uint32_t (&ow)[TN], const uint32_t (&ows)[TN], int wm,
+                                                f32x16_t (&acc)[TM][TN], int64_t &m0, int64_t &n0) {
   const int64_t kt = p.K / 64;
   int tm, tn;
   tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
-  m0 = (int64_t)tm * BT;
-  n0 = (int64_t)tn * BT;
+  m0 = (int64_t)tm * 64 * TM;
+  n0 = (int64_t)tn * 64 * TN;
   TileBase tb;
   tb.w = p.wp + ((n0 >> 5) * kt + c0) * 1024;
   tb.w_bytes = (p.N - n0) / 32 * kt * 1024 - c0 * 1024;
@@ -832,47 +854,47 @@ __device__ __forceinline__ void tile_mainloop_d(const Params &p, int tile, int64
   const int64_t xchunk = (int64_t)4 * p.xmt * 1024;
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.xf + c0 * xchunk, n * xchunk);
   const int lane = threadIdx.x & 63;
-  uint32_t ox[T];
+  uint32_t ox[TM];
 #pragma unroll
-  for (int i = 0; i < T; i++) ox[i] = (uint32_t)(((m0 >> 5) + wm * T + i) * 1024 + lane * 16);
+  for (int i = 0; i < TM; i++) ox[i] = (uint32_t)(((m0 >> 5) + wm * TM + i) * 1024 + lane * 16);
 
 #pragma unroll
-  for (int i = 0; i < T; i++)
+  for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int j = 0; j < T; j++) acc[i][j] = f32x16_t{};
-  WFrags<T> f[3];
-  f32x2_t sc[T];
-  bf16x8_t b[T];
-  XRing<T> xr;
+    for (int j = 0; j < TN; j++) acc[i][j] = f32x16_t{};
+  WFrags<TN> f[3];
+  f32x2_t sc[TN];
+  bf16x8_t b[TN];
+  XRing<TM> xr;
 #pragma unroll
-  for (int s = 0; s < 5; s++) load_xf<T>(rx, ox, s / 4, s % 4, p.xmt, xr.v[s]);
-  load_w<T>(tb, ow, ows, 0, n, f[0]);
-  load_w<T>(tb, ow, ows, 1, n, f[1]);
-  scales_of<T>(f[0], sc);
-  deq_w<T>(f[0], sc, 0, b);
+  for (int s = 0; s < 5; s++) load_xf<TM>(rx, ox, s / 4, s % 4, p.xmt, xr.v[s]);
+  load_w<TN>(tb, ow, ows, 0, n, f[0]);
+  load_w<TN>(tb, ow, ows, 1, n, f[1]);
+  scales_of<TN>(f[0], sc);
+  deq_w<TN>(f[0], sc, 0, b);
   for (int64_t c = 0; c < n; c += 3) {
-    chunk_d<0, T>(tb, rx, ox, p.xmt, ow, ows, c, n, f, sc, xr, b, acc);
-    chunk_d<1, T>(tb, rx, ox, p.xmt, ow, ows, c + 1, n, f, sc, xr, b, acc);
-    chunk_d<2, T>(tb, rx, ox, p.xmt, ow, ows, c + 2, n, f, sc, xr, b, acc);
+    chunk_d<0, TM, TN>(tb, rx, ox, p.xmt, ow, ows, c, n, f, sc, xr, b, acc);
+    chunk_d<1, TM, TN>(tb, rx, ox, p.xmt, ow, ows, c + 1, n, f, sc, xr, b, acc);
+    chunk_d<2, TM, TN>(tb, rx, ox, p.xmt, ow, ows, c + 2, n, f, sc, xr, b, acc);
   }
 }
 
-// Epilogue of a whole tile: per wave 32 x 32T staging of BF16 in LDS (after
+// Epilogue of a whole tile: per wave 32 x 32TN staging of BF16 in LDS (after
 // every wave is done with x), then 16-byte row pieces.
-template <int T>
+template <int TM, int TN>
 __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, float alpha, int64_t m0, int64_t n0,
-                                              int wave, int wm, int wn, f32x16_t (&acc)[T][T]) {
+                                              int wave, int wm, int wn, f32x16_t (&acc)[TM][TN]) {
   const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
   __syncthreads();
-  constexpr int ROW_BYTES = 32 * T * 2;
+  constexpr int ROW_BYTES = 32 * TN * 2;
   uint8_t *reg = smem + wave * (32 * ROW_BYTES);
-  const int64_t col0 = n0 + wn * 32 * T;
+  const int64_t col0 = n0 + wn * 32 * TN;
   const int64_t ncols = p.N - col0;
   const bool vec_ok = (p.ldy * 2) % 16 == 0 && ((uintptr_t)p.y & 15) == 0;
 #pragma unroll
-  for (int i = 0; i < T; i++) {
+  for (int i = 0; i < TM; i++) {
 #pragma unroll
-    for (int j = 0; j < T; j++)
+    for (int j = 0; j < TN; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int row = 8 * (e >> 2) + 4 * h + (e & 3);
@@ -882,7 +904,7 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
     constexpr int PIECES = ROW_BYTES / 16;
     for (int q = lane; q < 32 * PIECES; q += 64) {
       const int row = q / PIECES, pc = q % PIECES;
-      const int64_t m = m0 + wm * 32 * T + i * 32 + row;
+      const int64_t m = m0 + wm * 32 * TM + i * 32 + row;
       const int64_t cc = (int64_t)pc * 8;
       if (m < p.M && cc < ncols) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t *>(reg + row * ROW_BYTES + pc * 16);
@@ -899,11 +921,13 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
   }
 }
 
-template <int T>
-__global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p) {
-  constexpr int BT = 64 * T;
-  // T = 2: two x chunks (the LDS main loop); T = 4: the epilogue's BF16 staging
-  __shared__ __attribute__((aligned(16))) uint8_t smem[T == 4 ? 4 * 32 * 32 * T * 2 : 2 * BT * 128];
+// TM x TN MFMA tiles per wave: (2, 2) stages x through LDS; (4, 4) and (2, 4)
+// read x straight into registers (tile_mainloop_d).
+template <int TM, int TN>
+__global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Params p) {
+  constexpr bool kLds = TM == 2 && TN == 2;
+  // LDS path: two x chunks; direct paths: the epilogue's BF16 staging
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds ? 2 * 128 * 128 : 4 * 32 * 32 * TN * 2];
   const int t = threadIdx.x, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
   const int lane = t & 63, r = lane & 31;
   const int G = gridDim.x;
@@ -911,39 +935,39 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p)
   if ((G & 7) == 0) pid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const float alpha = load_alpha(p.alpha, p.alpha_dev);
   const int64_t nch = p.K / 64, kt = p.K / 64;
-  uint32_t ow[T], ows[T];
+  uint32_t ow[TN], ows[TN];
 #pragma unroll
-  for (int j = 0; j < T; j++) {
-    ow[j] = (uint32_t)(((wn * T + j) * kt) * 1024 + lane * 16);
-    ows[j] = (uint32_t)(((wn * T + j) * kt) * 128 + r * 4);
+  for (int j = 0; j < TN; j++) {
+    ow[j] = (uint32_t)(((wn * TN + j) * kt) * 1024 + lane * 16);
+    ows[j] = (uint32_t)(((wn * TN + j) * kt) * 128 + r * 4);
   }
-  f32x16_t acc[T][T];
+  f32x16_t acc[TM][TN];
   int64_t m0, n0;
   for (int tile = pid; tile < p.full; tile += G) {
-    if constexpr (T == 4)
-      tile_mainloop_d<T>(p, tile, 0, nch, ow, ows, wm, acc, m0, n0);
+    if constexpr (kLds)
+      tile_mainloop<2>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
     else
-      tile_mainloop<T>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
-    tile_epilogue<T>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
+      tile_mainloop_d<TM, TN>(p, tile, 0, nch, ow, ows, wm, acc, m0, n0);
+    tile_epilogue<TM, TN>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
   }
   if (p.rem > 0) {
     int64_t s, e;
     split_range(pid, G, (int64_t)p.rem * nch, s, e);
     for (int seg = 0; s < e; seg++) {
       const int64_t rho = s / nch, c0 = s - rho * nch, c1 = min(nch, c0 + (e - s));
-      if constexpr (T == 4)
-        tile_mainloop_d<T>(p, p.full + (int)rho, c0, c1 - c0, ow, ows, wm, acc, m0, n0);
+      if constexpr (kLds)
+        tile_mainloop<2>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm, acc, m0, n0);
       else
-        tile_mainloop<T>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm, acc, m0, n0);
-      float *dst = p.partials + ((int64_t)pid * 2 + seg) * partial_floats<T>() + (int64_t)wave * T * T * 1024 +
-                   lane * 16;
+        tile_mainloop_d<TM, TN>(p, p.full + (int)rho, c0, c1 - c0, ow, ows, wm, acc, m0, n0);
+      float *dst = p.partials + ((int64_t)pid * 2 + seg) * partial_floats<TM, TN>() +
+                   (int64_t)wave * TM * TN * 1024 + lane * 16;
 #pragma unroll
-      for (int i = 0; i < T; i++)
+      for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < T; j++)
+        for (int j = 0; j < TN; j++)
 #pragma unroll
           for (int q = 0; q < 4; q++)
-            *reinterpret_cast<f32x4_t *>(dst + (i * T + j) * 1024 + 4 * q) =
+            *reinterpret_cast<f32x4_t *>(dst + (i * TN + j) * 1024 + 4 * q) =
                 f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
       s += c1 - c0;
     }
@@ -954,18 +978,18 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void big_kernel(Params p)
 // accumulator elements (thread t: lane t % 64, elements 4 (t / 64) .. + 3 of
 // that lane in wave-tile `part`), adds them over every workgroup whose range
 // touches the tile, in workgroup order, then applies alpha and the BF16
-// conversion. 4 T^2 workgroups per tile.
-template <int T>
+// conversion. 4 TM TN workgroups per tile.
+template <int TM, int TN>
 __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
-  const int rho = blockIdx.x / (4 * T * T), part = blockIdx.x % (4 * T * T);   // part = (wave, i, j)
-  const int wave = part / (T * T), i = (part / T) % T, j = part % T;
+  const int rho = blockIdx.x / (4 * TM * TN), part = blockIdx.x % (4 * TM * TN);   // part = (wave, i, j)
+  const int wave = part / (TM * TN), i = (part / TN) % TM, j = part % TN;
   const int wm = wave >> 1, wn = wave & 1;
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6, h = lane >> 5, r = lane & 31;
   const int64_t nch = p.K / 64, units = (int64_t)p.rem * nch;
   const int64_t lo = (int64_t)rho * nch, hi = lo + nch;   // the tile's units
   int tm, tn;
   tile_coords(p.full + rho, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * 64 * T, n0 = (int64_t)tn * 64 * T;
+  const int64_t m0 = (int64_t)tm * 64 * TM, n0 = (int64_t)tn * 64 * TN;
   // first workgroup whose range ends past lo
   int64_t first = lo * G / units;
   if (first > 0) first--;
@@ -988,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
   // a slot with no partial (past last, or an empty range) reads zero through
   // the buffer range check, and adding +0 to a sum that started at +0 changes
   // nothing, so the sum is the same as one over the contributors in order.
-  const int64_t pbytes = (int64_t)G * 2 * partial_floats<T>() * 4;
+  const int64_t pbytes = (int64_t)G * 2 * partial_floats<TM, TN>() * 4;
   const __amdgpu_buffer_rsrc_t rp = rsrc(p.partials, pbytes);
   const int64_t off = (int64_t)part * 1024 + lane * 16 + 4 * q;
   f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1001,18 +1025,18 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
       split_range(w, G, units, s, e);
       const bool ok = w <= last && e > lo && s < e;
       const int seg = s >= lo ? 0 : 1;
-      const uint32_t o = ok ? (uint32_t)(((w * 2 + seg) * partial_floats<T>() + off) * 4) : (uint32_t)pbytes;
+      const uint32_t o = ok ? (uint32_t)(((w * 2 + seg) * partial_floats<TM, TN>() + off) * 4) : (uint32_t)pbytes;
       t[k] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, o, 0, 0));
     }
 #pragma unroll
     for (int k = 0; k < 4; k++) v += t[k];
   }
   const float alpha = load_alpha(p.alpha, p.alpha_dev);
-  const int64_t col = n0 + wn * 32 * T + 32 * j + r;
+  const int64_t col = n0 + wn * 32 * TN + 32 * j + r;
 #pragma unroll
   for (int k = 0; k < 4; k++) {
     const int e = 4 * q + k;
-    const int64_t m = m0 + wm * 32 * T + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+    const int64_t m = m0 + wm * 32 * TM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
     if (m < p.M && col < p.N) p.y[m * p.ldy + col] = f32_to_bf16_rne(alpha * v[k]);
   }
 }
@@ -1081,7 +1105,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     const w4a16::BigSched b = w4a16::big_sched(M, N, K, di.num_cus);
     // fragment-order x: 32-bit offsets inside it
     if (b.total > 0x7FFFFFFF || w4a16::big_xf_bytes(b, K) > 0x7FFFFFFFull) return NVFP4_ERR_SHAPE;
-    if (b.T == 2 && (int64_t)128 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;   // LDS path: 32-bit x offsets
+    if (b.TM * b.TN < 8 && (int64_t)128 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;   // LDS path: 32-bit x offsets
     const int64_t xmt = w4a16::big_xmt(b);
     uint8_t *xf = xmt > 0 ? static_cast<uint8_t *>(ws) + w4a16::big_partials_span(b) : nullptr;
     if (xmt > 0) {
@@ -1092,20 +1116,22 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     w4a16::big::Params bp{x,     ldx,           w_prep,        y,           ldy,          M,
                           N,     K,             alpha,         alpha_dev,   (int)b.tiles_m, (int)b.tiles_n,
                           (int)b.full, (int)b.rem, static_cast<float *>(ws), xf, (int)xmt};
-    const unsigned grid = (unsigned)b.G;
-    if (b.T == 4)
-      hipLaunchKernelGGL(w4a16::big::big_kernel<4>, dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);
-    else
-      hipLaunchKernelGGL(w4a16::big::big_kernel<2>, dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);
-    if (b.rem > 0) {
-      NVFP4_LAUNCH_CHECK();
-      if (b.T == 4)
-        hipLaunchKernelGGL(w4a16::big::big_fixup_kernel<4>, dim3((unsigned)(b.rem * 64)), dim3(w4a16::big::kThreads),
-                           0, s, bp, (int)b.G);
-      else
-        hipLaunchKernelGGL(w4a16::big::big_fixup_kernel<2>, dim3((unsigned)(b.rem * 16)), dim3(w4a16::big::kThreads),
-                           0, s, bp, (int)b.G);
+    const unsigned grid = (unsigned)b.G, fix_grid = (unsigned)(b.rem * 4 * b.TM * b.TN);
+#define NVFP4_BIG(TMV, TNV)                                                                                      \
+  hipLaunchKernelGGL((w4a16::big::big_kernel<TMV, TNV>), dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);     \
+  if (b.rem > 0) {                                                                                               \
+    NVFP4_LAUNCH_CHECK();                                                                                        \
+    hipLaunchKernelGGL((w4a16::big::big_fixup_kernel<TMV, TNV>), dim3(fix_grid), dim3(w4a16::big::kThreads), 0, \
+                       s, bp, (int)b.G);                                                                         \
+  }
+    if (b.TM == 4) {
+      NVFP4_BIG(4, 4)
+    } else if (b.TN == 4) {
+      NVFP4_BIG(2, 4)
+    } else {
+      NVFP4_BIG(2, 2)
     }
+#undef NVFP4_BIG
   } else if (plan.kind == 3) {
     if (plan.grid_x > 0x7FFFFFFF || M * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
     const int MT = M <= 32 ? 1 : 2;

@@ -386,19 +386,22 @@ def test_w4a16_wide_decode(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(1000, 2080, 320), (100, 512, 1024), (65, 4096, 4160), (200, 34816, 192),
                                    (2600, 8224, 128), (256, 65792, 64), (300, 56320, 192),
-                                   (700, 3008, 33792), (1024, 2048, 49152)])
+                                   (700, 3008, 33792), (1024, 2048, 49152), (100, 8224, 16064)])
 def test_w4a16_big_ragged(M, N, K):
     """Larger M with ragged rows and columns on the persistent MFMA path; full check.
     Fewer 128 x 128 tiles than CUs, each split along K with a fix-up: 1000 x 2080 x 320
     (136 tiles in 3 ranges of 5 chunks, so ranges straddle tiles), 100 x 512 x 1024 (4
     tiles in 8 aligned ranges), 65 x 4096 x 4160 (65 chunks in 8 unaligned ranges).
-    200 x 34816: 544 ragged 128 x 128 tiles for 512 slots (an uneven last round). 256 x 256
-    tiles, the ones past the last full round split along K over all workgroups: 2600 x
-    8224 (107 of 363 tiles); 256 x 65792 x 64 (one tile of one chunk, so every other
-    workgroup's range is empty); 300 x 56320 (184 ragged tiles, about two chunks each).
+    256 x 256 tiles, the ones past the last full round split along K over all
+    workgroups: 2600 x 8224 (107 of 363 tiles); 256 x 65792 x 64 (one tile of one
+    chunk, so every other workgroup's range is empty); 300 x 56320 (184 ragged tiles,
+    about two chunks each).
     Fewer 256 x 256 tiles than CUs with a long K, every tile split over all workgroups:
     700 x 3008 x 33792 (36 ragged tiles of 528 chunks, 74-75 per workgroup, so ranges
-    straddle tiles) and 1024 x 2048 x 49152 (32 tiles, exactly 8 ranges of 96 per tile)."""
+    straddle tiles) and 1024 x 2048 x 49152 (32 tiles, exactly 8 ranges of 96 per tile).
+    128 x 256 tiles: 200 x 34816 x 192 (544 tiles of 128 x 128 would do; 272 of 128 x 256
+    fill one round and leave 16 split three chunks over 256 workgroups, most of them empty)
+    and 100 x 8224 x 16064 (33 ragged tiles, all split, about 32 chunks per workgroup)."""
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M + N + K)
     out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
     torch.cuda.synchronize()
