@@ -77,23 +77,28 @@ static int num_cus_or_default() {
 //    is long enough that splitting them over all CUs gives each at least
 //    kBigSplitMinChunks 64-deep chunks and x's rows fill at least 7/8 of the
 //    tile rows;
-//  * else 2 x 4 (128 x 256) when those fill the CUs or split that way;
+//  * else 128 x 256 when those fill the CUs or split that way, as 4 x 2 MFMA
+//    tiles per wave with the 4 waves side by side along N (each wave
+//    dequantizes W fragments for all four of its row tiles);
 //  * else 2 x 2 (128 x 128).
+// WGM is the number of waves along M (2 x 2 waves, or 1 x 4).
 constexpr int64_t kBigSplitMinChunks = 32;
-static void big_tile_shape(int64_t M, int64_t N, int64_t K, int cus, int &TM, int &TN) {
+static void big_tile_shape(int64_t M, int64_t N, int64_t K, int cus, int &TM, int &TN, int &WGM) {
   const int64_t nch = K / 64;
   const int64_t tm4 = (M + 255) / 256, t44 = tm4 * ((N + 255) / 256);
   if (t44 >= cus || (t44 * nch >= kBigSplitMinChunks * cus && 8 * M >= 7 * 256 * tm4)) {
     TM = TN = 4;
+    WGM = 2;
     return;
   }
   const int64_t t24 = ((M + 127) / 128) * ((N + 255) / 256);
   if (t24 >= cus || t24 * nch >= kBigSplitMinChunks * cus) {
-    TM = 2;
-    TN = 4;
+    TM = 4;
+    TN = 2;
+    WGM = 1;
     return;
   }
-  TM = TN = 2;
+  TM = TN = WGM = 2;
 }
 
 // One 32-row group per workgroup. Eight waves once there are two groups per
@@ -148,10 +153,10 @@ static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 
 //    made 6144 x 5120 at M = 1024, 30 chunks each, slower: 113 against 100 us;
 //    at M = 384, a quarter of the 256-row tiles empty, it was slower too).
 //  * 128 x 256 tiles (one workgroup per CU, x read directly) follow the same
-//    rules: 34816 x 5120 at M = 128 took 84.5 us against 92.6 with 128 x 128
-//    tiles, 5120 x 17408 at M = 192 80.8 against 86.8. A wave's two MFMA rows
-//    share each dequantized W fragment, so these tiles spend about nine vector
-//    instructions per MFMA against five for 256 x 256.
+//    rules. With 2 x 2 waves of 2 x 4 MFMA tiles, 34816 x 5120 at M = 128 took
+//    84.5 us against 92.6 with 128 x 128 tiles, but both waves of a column
+//    dequantized the same W fragments: nine vector instructions per MFMA, and
+//    the counters showed the MFMA and vector work barely overlapping.
 //  * 128 x 128 tiles (two workgroups per CU), at least as many as CUs: one
 //    workgroup per tile up to two per CU, then whole rounds; a CU running two
 //    workgroups loses little against one that runs one, and splitting these
@@ -167,15 +172,17 @@ static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 
 constexpr int kMaxKSplit = 8;
 
 struct BigSched {
-  int TM, TN;
+  int TM, TN, WGM;   // MFMA tiles per wave; waves along M
   int64_t tiles_m, tiles_n, total, G, full, rem;
+  int64_t tile_rows() const { return 32 * TM * WGM; }
+  int64_t tile_cols() const { return 32 * TN * (4 / WGM); }
 };
 
 static BigSched big_sched(int64_t M, int64_t N, int64_t K, int cus) {
   BigSched b{};
-  big_tile_shape(M, N, K, cus, b.TM, b.TN);
-  b.tiles_m = (M + 64 * b.TM - 1) / (64 * b.TM);
-  b.tiles_n = (N + 64 * b.TN - 1) / (64 * b.TN);
+  big_tile_shape(M, N, K, cus, b.TM, b.TN, b.WGM);
+  b.tiles_m = (M + b.tile_rows() - 1) / b.tile_rows();
+  b.tiles_n = (N + b.tile_cols() - 1) / b.tile_cols();
   b.total = b.tiles_m * b.tiles_n;
   const bool direct = b.TM * b.TN >= 8;       // one workgroup per CU
   const int64_t slots = (int64_t)cus * (direct ? 1 : 2);
@@ -207,7 +214,7 @@ static size_t big_partial_bytes(const BigSched &b) { return (size_t)b.TM * b.TN 
 static size_t big_partials_span(const BigSched &b) {
   return b.rem > 0 ? ((size_t)b.G * 2 * big_partial_bytes(b) + 255) / 256 * 256 : 0;
 }
-static int64_t big_xmt(const BigSched &b) { return b.TM * b.TN >= 8 ? b.tiles_m * 2 * b.TM : 0; }
+static int64_t big_xmt(const BigSched &b) { return b.TM * b.TN >= 8 ? b.tiles_m * b.tile_rows() / 32 : 0; }
 static size_t big_xf_bytes(const BigSched &b, int64_t K) { return (size_t)big_xmt(b) * 32 * (size_t)K * 2; }
 
 static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
@@ -836,15 +843,15 @@ __device__ __forceinline__ void chunk_d(const TileBase &tb, __amdgpu_buffer_rsrc
   }
 }
 
-template <int TM, int TN>
+template <int TM, int TN, int WGM>
 __device__ __forceinline__ void tile_mainloop_d(const Params &p, int tile, int64_t c0, int64_t n,
                                                 const uint32_t (&ow)[TN], const uint32_t (&ows)[TN], int wm,
                                                 f32x16_t (&acc)[TM][TN], int64_t &m0, int64_t &n0) {
   const int64_t kt = p.K / 64;
   int tm, tn;
   tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
-  m0 = (int64_t)tm * 64 * TM;
-  n0 = (int64_t)tn * 64 * TN;
+  m0 = (int64_t)tm * 32 * TM * WGM;
+  n0 = (int64_t)tn * 32 * TN * (4 / WGM);
   TileBase tb;
   tb.w = p.wp + ((n0 >> 5) * kt + c0) * 1024;
   tb.w_bytes = (p.N - n0) / 32 * kt * 1024 - c0 * 1024;
@@ -921,14 +928,16 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
   }
 }
 
-// TM x TN MFMA tiles per wave: (2, 2) stages x through LDS; (4, 4) and (2, 4)
-// read x straight into registers (tile_mainloop_d).
-template <int TM, int TN>
+// TM x TN MFMA tiles per wave, the 4 waves WGM x (4 / WGM) over the tile:
+// (2, 2, 2) stages x through LDS; (4, 4, 2) and (4, 2, 1) read x straight into
+// registers (tile_mainloop_d).
+template <int TM, int TN, int WGM>
 __global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Params p) {
   constexpr bool kLds = TM == 2 && TN == 2;
+  constexpr int WGN = 4 / WGM;
   // LDS path: two x chunks; direct paths: the epilogue's BF16 staging
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds ? 2 * 128 * 128 : 4 * 32 * 32 * TN * 2];
-  const int t = threadIdx.x, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+  const int t = threadIdx.x, wave = t >> 6, wm = wave / WGN, wn = wave % WGN;
   const int lane = t & 63, r = lane & 31;
   const int G = gridDim.x;
   int pid = blockIdx.x;
@@ -947,7 +956,7 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Par
     if constexpr (kLds)
       tile_mainloop<2>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
     else
-      tile_mainloop_d<TM, TN>(p, tile, 0, nch, ow, ows, wm, acc, m0, n0);
+      tile_mainloop_d<TM, TN, WGM>(p, tile, 0, nch, ow, ows, wm, acc, m0, n0);
     tile_epilogue<TM, TN>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
   }
   if (p.rem > 0) {
@@ -958,7 +967,7 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Par
       if constexpr (kLds)
         tile_mainloop<2>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm, acc, m0, n0);
       else
-        tile_mainloop_d<TM, TN>(p, p.full + (int)rho, c0, c1 - c0, ow, ows, wm, acc, m0, n0);
+        tile_mainloop_d<TM, TN, WGM>(p, p.full + (int)rho, c0, c1 - c0, ow, ows, wm, acc, m0, n0);
       float *dst = p.partials + ((int64_t)pid * 2 + seg) * partial_floats<TM, TN>() +
                    (int64_t)wave * TM * TN * 1024 + lane * 16;
 #pragma unroll
@@ -974,22 +983,24 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Par
   }
 }
 
-// Split tiles: workgroup (rho, part) takes 1024 of tile full + rho's
-// accumulator elements (thread t: lane t % 64, elements 4 (t / 64) .. + 3 of
-// that lane in wave-tile `part`), adds them over every workgroup whose range
-// touches the tile, in workgroup order, then applies alpha and the BF16
-// conversion. 4 TM TN workgroups per tile.
-template <int TM, int TN>
+// Split tiles: workgroup (rho, g) takes 4 x 1024 of tile full + rho's
+// accumulator elements, the four wave-tiles `part` = 4 g .. 4 g + 3 (thread t:
+// lane t % 64, elements 4 (t / 64) .. + 3 of that lane in each), adds them over
+// every workgroup whose range touches the tile, in workgroup order, then
+// applies alpha and the BF16 conversion. TM TN workgroups per tile; with four
+// parts per thread, sixteen loads are in flight together (a workgroup per
+// part left the kernel bound by load latency: 17.6 us after the 128 x 256 tile
+// kernel at M = 128 on 34816 x 5120).
+template <int TM, int TN, int WGM>
 __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
-  const int rho = blockIdx.x / (4 * TM * TN), part = blockIdx.x % (4 * TM * TN);   // part = (wave, i, j)
-  const int wave = part / (TM * TN), i = (part / TN) % TM, j = part % TN;
-  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int WGN = 4 / WGM;
+  const int rho = blockIdx.x / (TM * TN), pg = blockIdx.x % (TM * TN);
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6, h = lane >> 5, r = lane & 31;
   const int64_t nch = p.K / 64, units = (int64_t)p.rem * nch;
   const int64_t lo = (int64_t)rho * nch, hi = lo + nch;   // the tile's units
   int tm, tn;
   tile_coords(p.full + rho, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * 64 * TM, n0 = (int64_t)tn * 64 * TN;
+  const int64_t m0 = (int64_t)tm * 32 * TM * WGM, n0 = (int64_t)tn * 32 * TN * WGN;
   // first workgroup whose range ends past lo
   int64_t first = lo * G / units;
   if (first > 0) first--;
@@ -1008,16 +1019,18 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
     if (s >= hi) break;
     last++;
   }
-  // Their partials are loaded four at a time, all four in flight together;
-  // a slot with no partial (past last, or an empty range) reads zero through
-  // the buffer range check, and adding +0 to a sum that started at +0 changes
-  // nothing, so the sum is the same as one over the contributors in order.
+  // Their partials are loaded four workgroups at a time; a slot with no
+  // partial (past last, or an empty range) reads zero through the buffer range
+  // check, and adding +0 to a sum that started at +0 changes nothing, so each
+  // sum is the same as one over the contributors in order.
   const int64_t pbytes = (int64_t)G * 2 * partial_floats<TM, TN>() * 4;
   const __amdgpu_buffer_rsrc_t rp = rsrc(p.partials, pbytes);
-  const int64_t off = (int64_t)part * 1024 + lane * 16 + 4 * q;
-  f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t off = (int64_t)(4 * pg) * 1024 + lane * 16 + 4 * q;
+  f32x4_t v[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++) v[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t w0 = first; w0 <= last; w0 += 4) {
-    f32x4_t t[4];
+    f32x4_t t[4][4];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       const int64_t w = w0 + k;
@@ -1025,19 +1038,31 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
       split_range(w, G, units, s, e);
       const bool ok = w <= last && e > lo && s < e;
       const int seg = s >= lo ? 0 : 1;
-      const uint32_t o = ok ? (uint32_t)(((w * 2 + seg) * partial_floats<TM, TN>() + off) * 4) : (uint32_t)pbytes;
-      t[k] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, o, 0, 0));
+      const int64_t base = ((w * 2 + seg) * partial_floats<TM, TN>() + off) * 4;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const uint32_t o = ok ? (uint32_t)(base + u * 4096) : (uint32_t)pbytes;
+        t[k][u] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, o, 0, 0));
+      }
     }
 #pragma unroll
-    for (int k = 0; k < 4; k++) v += t[k];
+    for (int k = 0; k < 4; k++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) v[u] += t[k][u];
   }
   const float alpha = load_alpha(p.alpha, p.alpha_dev);
-  const int64_t col = n0 + wn * 32 * TN + 32 * j + r;
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
-    const int e = 4 * q + k;
-    const int64_t m = m0 + wm * 32 * TM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-    if (m < p.M && col < p.N) p.y[m * p.ldy + col] = f32_to_bf16_rne(alpha * v[k]);
+  for (int u = 0; u < 4; u++) {
+    const int part = 4 * pg + u;   // (wave, i, j)
+    const int wave = part / (TM * TN), i = (part / TN) % TM, j = part % TN;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int64_t col = n0 + wn * 32 * TN + 32 * j + r;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int e = 4 * q + k;
+      const int64_t m = m0 + wm * 32 * TM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (m < p.M && col < p.N) p.y[m * p.ldy + col] = f32_to_bf16_rne(alpha * v[u][k]);
+    }
   }
 }
 
@@ -1116,20 +1141,20 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     w4a16::big::Params bp{x,     ldx,           w_prep,        y,           ldy,          M,
                           N,     K,             alpha,         alpha_dev,   (int)b.tiles_m, (int)b.tiles_n,
                           (int)b.full, (int)b.rem, static_cast<float *>(ws), xf, (int)xmt};
-    const unsigned grid = (unsigned)b.G, fix_grid = (unsigned)(b.rem * 4 * b.TM * b.TN);
-#define NVFP4_BIG(TMV, TNV)                                                                                      \
-  hipLaunchKernelGGL((w4a16::big::big_kernel<TMV, TNV>), dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp);     \
+    const unsigned grid = (unsigned)b.G, fix_grid = (unsigned)(b.rem * b.TM * b.TN);
+#define NVFP4_BIG(TMV, TNV, WGMV)                                                                                \
+  hipLaunchKernelGGL((w4a16::big::big_kernel<TMV, TNV, WGMV>), dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp); \
   if (b.rem > 0) {                                                                                               \
     NVFP4_LAUNCH_CHECK();                                                                                        \
-    hipLaunchKernelGGL((w4a16::big::big_fixup_kernel<TMV, TNV>), dim3(fix_grid), dim3(w4a16::big::kThreads), 0, \
-                       s, bp, (int)b.G);                                                                         \
+    hipLaunchKernelGGL((w4a16::big::big_fixup_kernel<TMV, TNV, WGMV>), dim3(fix_grid), dim3(w4a16::big::kThreads), \
+                       0, s, bp, (int)b.G);                                                                      \
   }
-    if (b.TM == 4) {
-      NVFP4_BIG(4, 4)
-    } else if (b.TN == 4) {
-      NVFP4_BIG(2, 4)
+    if (b.TN == 4) {
+      NVFP4_BIG(4, 4, 2)
+    } else if (b.TM == 4) {
+      NVFP4_BIG(4, 2, 1)
     } else {
-      NVFP4_BIG(2, 2)
+      NVFP4_BIG(2, 2, 2)
     }
 #undef NVFP4_BIG
   } else if (plan.kind == 3) {
