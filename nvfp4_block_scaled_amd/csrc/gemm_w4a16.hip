@@ -404,6 +404,10 @@ constexpr int kSkAhead = 1;   // tiles per wave and ring batch
 
 static int skinny_waves(int64_t N, int cus) { return N / 32 < cus ? 16 : 8; }
 
+// Row groups per workgroup with 8 waves and one x tile: each x fragment a wave
+// loads then feeds NG MFMAs, so x is read from L2 by groups / NG workgroups.
+constexpr int kSkinnyNG = 2;
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   bf16x8_t b;
   __builtin_memcpy(&b, &v, 16);
@@ -427,20 +431,20 @@ __global__ __launch_bounds__(256) void tile_x_kernel(const uint16_t *__restrict_
   xf[((t * 4 + s) * MT + mt) * 64 + 32 * h + r] = v;
 }
 
-template <int MT, bool XF, int W>
+template <int MT, bool XF, int W, int NG>
 __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restrict__ x, int64_t ldx,
                                                              const uint8_t *__restrict__ wp, int64_t M, int64_t N,
                                                              int64_t K, float alpha, const float *alpha_dev,
                                                              uint16_t *__restrict__ y, int64_t ldy,
                                                              const uint8_t *__restrict__ xf) {
   constexpr int U = kSkAhead;                          // tiles per wave per batch
-  __shared__ f32x16_t red[W / 2][MT][64];
+  __shared__ f32x16_t red[W / 2][NG][MT][64];
   const int64_t T = K / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, r = lane & 31;
-  const int64_t g = blockIdx.x;
-  const uint8_t *cb = wp + ((g * T) << 10) + lane * 16;
-  const uint8_t *sb = wp + N * K / 2 + ((g * T) << 7) + r * 4;
+  const int64_t g0 = (int64_t)blockIdx.x * NG;         // the workgroup's first row group
+  const uint8_t *cb = wp + ((g0 * T) << 10) + lane * 16;
+  const uint8_t *sb = wp + N * K / 2 + ((g0 * T) << 7) + r * 4;
   const uint8_t *xl = XF ? xf + lane * 16 : nullptr;   // this lane's unit of every x fragment
   const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, XF ? 0 : M * ldx * 2);
   uint32_t xo[MT];                                 // direct reads: byte offset of this lane's x row, k = 32h
@@ -448,8 +452,8 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
   for (int mt = 0; mt < MT; mt++) xo[mt] = (uint32_t)(((int64_t)(32 * mt + r) * ldx + 32 * h) * 2);
 
   struct Batch {
-    u32x4_t cw[U];
-    uint32_t sw[U];
+    u32x4_t cw[U][NG];
+    uint32_t sw[U][NG];
     u32x4_t xv[U][MT][4];
   };
   auto issue = [&](Batch &b, int64_t t0) {
@@ -458,9 +462,13 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
       const int64_t t = t0 + (int64_t)i * W;
       const bool in = t < T;
       const int64_t tc = in ? t : 0;
-      b.cw[i] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cb + (tc << 10)))
-                   : u32x4_t{0u, 0u, 0u, 0u};
-      b.sw[i] = in ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + (tc << 7))) : 0u;
+#pragma unroll
+      for (int q = 0; q < NG; q++) {
+        b.cw[i][q] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cb + ((q * T + tc) << 10)))
+                        : u32x4_t{0u, 0u, 0u, 0u};
+        b.sw[i][q] =
+            in ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + ((q * T + tc) << 7))) : 0u;
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -469,20 +477,25 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
                               : __builtin_amdgcn_raw_buffer_load_b128(rx, xo[mt] + (uint32_t)(tc * 128 + 16 * s), 0, 0);
     }
   };
-  f32x16_t acc[MT];
+  f32x16_t acc[NG][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; mt++) acc[mt] = f32x16_t{};
+  for (int q = 0; q < NG; q++)
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[q][mt] = f32x16_t{};
   auto compute = [&](const Batch &b, int64_t t0) {
 #pragma unroll
     for (int i = 0; i < U; i++) {
       if (t0 + (int64_t)i * W < T) {
-        const f32x2_t sc = e4m3x2_to_f32(b.sw[i] >> (16 * h));
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-          const bf16x8_t bv = dequant8_bf16(b.cw[i][s], sc[s >> 1]);
+        for (int q = 0; q < NG; q++) {
+          const f32x2_t sc = e4m3x2_to_f32(b.sw[i][q] >> (16 * h));
 #pragma unroll
-          for (int mt = 0; mt < MT; mt++)
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b.xv[i][mt][s]), bv, acc[mt], 0, 0, 0);
+          for (int s = 0; s < 4; s++) {
+            const bf16x8_t bv = dequant8_bf16(b.cw[i][q][s], sc[s >> 1]);
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+              acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b.xv[i][mt][s]), bv, acc[q][mt], 0, 0, 0);
+          }
         }
       }
     }
@@ -502,23 +515,30 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
   for (int half = W / 2; half >= 1; half >>= 1) {
     if (wave >= half && wave < 2 * half)
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++) red[wave - half][mt][lane] = acc[mt];
+      for (int q = 0; q < NG; q++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) red[wave - half][q][mt][lane] = acc[q][mt];
     __syncthreads();
     if (wave < half)
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++) acc[mt] += red[wave][mt][lane];
+      for (int q = 0; q < NG; q++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) acc[q][mt] += red[wave][q][mt][lane];
     __syncthreads();
   }
   if (wave == 0) {
     const float al = load_alpha(alpha, alpha_dev);
-    const int64_t n = g * 32 + r;
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++)
+    for (int q = 0; q < NG; q++) {
+      const int64_t n = (g0 + q) * 32 + r;
 #pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const int64_t m = 32 * mt + 8 * (j >> 2) + 4 * h + (j & 3);
-        if (m < M) y[m * ldy + n] = f32_to_bf16_rne(al * acc[mt][j]);
-      }
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int64_t m = 32 * mt + 8 * (j >> 2) + 4 * h + (j & 3);
+          if (m < M) y[m * ldy + n] = f32_to_bf16_rne(al * acc[q][mt][j]);
+        }
+    }
   }
 }
 
@@ -1169,17 +1189,21 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     }
     const unsigned grid = (unsigned)plan.grid_x;
     const int W = w4a16::skinny_waves(N, di.num_cus);
-#define NVFP4_SKINNY(MTV, XFV, WV)                                                                              \
-  hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV, WV>), dim3(grid), dim3(WV * 64), 0, s, x, ldx, w_prep, M, N, \
-                     K, alpha, alpha_dev, y, ldy, xf)
+#define NVFP4_SKINNY(MTV, XFV, WV, NGV)                                                                         \
+  hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV, WV, NGV>), dim3(grid / NGV), dim3(WV * 64), 0, s, x, ldx,     \
+                     w_prep, M, N, K, alpha, alpha_dev, y, ldy, xf)
+    const bool ng = MT == 1 && W == 8 && plan.grid_x % w4a16::kSkinnyNG == 0;
     if (W == 16) {
-      if (!xf_path) NVFP4_SKINNY(1, false, 16);
-      else if (MT == 1) NVFP4_SKINNY(1, true, 16);
-      else NVFP4_SKINNY(2, true, 16);
+      if (!xf_path) NVFP4_SKINNY(1, false, 16, 1);
+      else if (MT == 1) NVFP4_SKINNY(1, true, 16, 1);
+      else NVFP4_SKINNY(2, true, 16, 1);
+    } else if (ng) {
+      if (!xf_path) NVFP4_SKINNY(1, false, 8, w4a16::kSkinnyNG);
+      else NVFP4_SKINNY(1, true, 8, w4a16::kSkinnyNG);
     } else {
-      if (!xf_path) NVFP4_SKINNY(1, false, 8);
-      else if (MT == 1) NVFP4_SKINNY(1, true, 8);
-      else NVFP4_SKINNY(2, true, 8);
+      if (!xf_path) NVFP4_SKINNY(1, false, 8, 1);
+      else if (MT == 1) NVFP4_SKINNY(1, true, 8, 1);
+      else NVFP4_SKINNY(2, true, 8, 1);
     }
 #undef NVFP4_SKINNY
   }
