@@ -404,8 +404,10 @@ constexpr int kSkAhead = 1;   // tiles per wave and ring batch
 
 static int skinny_waves(int64_t N, int cus) { return N / 32 < cus ? 16 : 8; }
 
-// Row groups per workgroup with 8 waves and one x tile: each x fragment a wave
-// loads then feeds NG MFMAs, so x is read from L2 by groups / NG workgroups.
+// Row groups per workgroup with 8 waves: each x fragment a wave loads then
+// feeds NG MFMAs, so x is read from L2 by groups / NG workgroups (34816 x 5120:
+// M = 16 from 43.2 to 35.5 us, M = 64 from 61.6 to 58.1 us; four groups per
+// workgroup, at 116+ registers, left too few workgroups resident).
 constexpr int kSkinnyNG = 2;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
@@ -1192,14 +1194,15 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
 #define NVFP4_SKINNY(MTV, XFV, WV, NGV)                                                                         \
   hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV, WV, NGV>), dim3(grid / NGV), dim3(WV * 64), 0, s, x, ldx,     \
                      w_prep, M, N, K, alpha, alpha_dev, y, ldy, xf)
-    const bool ng = MT == 1 && W == 8 && plan.grid_x % w4a16::kSkinnyNG == 0;
+    const bool ng = W == 8 && plan.grid_x % w4a16::kSkinnyNG == 0;
     if (W == 16) {
       if (!xf_path) NVFP4_SKINNY(1, false, 16, 1);
       else if (MT == 1) NVFP4_SKINNY(1, true, 16, 1);
       else NVFP4_SKINNY(2, true, 16, 1);
     } else if (ng) {
       if (!xf_path) NVFP4_SKINNY(1, false, 8, w4a16::kSkinnyNG);
-      else NVFP4_SKINNY(1, true, 8, w4a16::kSkinnyNG);
+      else if (MT == 1) NVFP4_SKINNY(1, true, 8, w4a16::kSkinnyNG);
+      else NVFP4_SKINNY(2, true, 8, w4a16::kSkinnyNG);
     } else {
       if (!xf_path) NVFP4_SKINNY(1, false, 8, 1);
       else if (MT == 1) NVFP4_SKINNY(1, true, 8, 1);

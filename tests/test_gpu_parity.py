@@ -355,12 +355,13 @@ def test_w4a16_small_shapes(M, N, K):
     assert_close(host(out), y, S, bf16=True, what=f"w4a16 M={M} {N}x{K}")
 
 
-@pytest.mark.parametrize("M", [6, 16])
-@pytest.mark.parametrize("N,K", [(17408, 4160), (2048, 8192)])
+@pytest.mark.parametrize("M", [6, 16, 24, 40, 64])
+@pytest.mark.parametrize("N,K", [(17408, 4160), (17440, 1088), (2048, 8192)])
 def test_w4a16_skinny_long_k(M, N, K):
-    """M <= 16 (x rows read directly, rows >= M zero) with many tiles per wave: 544 row
-    groups (8 waves per workgroup, 65 tiles over them) and 64 row groups (16 waves, 8
-    tiles each); full check."""
+    """4 < M <= 64 with many tiles per wave; full check. M <= 16 reads x rows directly
+    (rows >= M zero), 24 and 40 / 64 read the fragment-order copy with one or two x
+    tiles. 544 row groups: 8 waves per workgroup, two groups each, 65 tiles over the
+    waves. 545 groups (odd): 8 waves, one group each. 64 groups: 16 waves, 8 tiles each."""
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 7 + N + K)
     out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
     torch.cuda.synchronize()
