@@ -66,11 +66,13 @@ size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
 
 /* Workspace bytes an op needs for (M, N, K); 0 means no workspace is used.
  * The workspace holds A in the prepared tile layout (W4A4: (M rounded up to
- * 32) * K * 9/16 bytes), x in MFMA fragment order (W4A16, 16 < M <= 64),
- * FP32 partial tiles of output tiles split along K (W4A16, M > 64 when the
- * tiles do not fill whole rounds of the CUs; the size depends on the device's
- * CU count), or per-workgroup maxima (quantize); every call overwrites what it
- * reads. */
+ * 32) * K * 9/16 bytes); for W4A16, x in MFMA fragment order (16 < M <= 64:
+ * (M rounded up to 32) * K * 2 bytes; M > 64 on 256 x 256 or 128 x 256
+ * output tiles: M rounded up to the tile rows, * K * 2 bytes) after the FP32
+ * partial tiles of output tiles split along K (M > 64 when the tiles do not
+ * fill whole rounds of the CUs; the tile shape and this size depend on the
+ * device's CU count); or per-workgroup maxima (quantize). Every call
+ * overwrites what it reads. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* Zeroes a workspace on `stream` with a fill kernel (no hipMemset, so it may be
