@@ -148,6 +148,20 @@ def test_workspace_sizes():
     assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 33, 64, 128) == 64 * 128 * 9 // 16
     assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 0, 64, 128) == 0
     assert L.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 0, 5120) >= 4
+    # W4A16 (no device here: the plan assumes 256 CUs). Decode (M <= 4) needs none; the
+    # skinny kernel's x copy for 16 < M <= 64 is 32 rows x K BF16.
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1, 34816, 5120) == 0
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 4, 34816, 5120) == 0
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 16, 34816, 5120) == 0
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 24, 17408, 4160) == 32 * 4160 * 2
+    # M = 128 on 34816 x 5120: 136 tiles of 128 x 256, all split over 256 workgroups (two
+    # 128 KiB partial slots each), then x for one 128-row tile in fragment order
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 128, 34816, 5120) == 256 * 2 * 128 * 1024 + 128 * 5120 * 2
+    # M = 1024: 544 tiles of 256 x 256, 512 in two whole rounds and 32 split (two 256 KiB
+    # slots per workgroup), then x for four 256-row tiles
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1024, 34816, 5120) == 256 * 2 * 256 * 1024 + 1024 * 5120 * 2
+    # 8192 rows on 256 x 256 tiles fill 32 x 32 = 1024 tiles, 4 whole rounds: x copy only
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 8192, 8192, 1024) == 8192 * 1024 * 2
     assert L.nvfp4_workspace_bytes(7, 1, 1, 1) == 0
     assert L.nvfp4_workspace_init(None, 0, None) == nv.OK
     assert L.nvfp4_workspace_init(None, 64, None) == nv.ERR_NULL
