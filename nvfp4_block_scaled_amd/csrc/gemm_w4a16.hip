@@ -20,7 +20,7 @@
 //    an L2 write-back on this part, which measured several times slower.)
 //  * 4 < M <= 64 (and M <= 4 when x does not fit in LDS): the skinny MFMA
 //    kernel, the decode structure with v_mfma_f32_32x32x16_bf16 on one or two
-//    32-row x tiles (below).
+//    32-row x tiles and one or two row groups per workgroup (below).
 //  * M > 64: the big MFMA kernel, built like the W4A4 kernel (below), on
 //    persistent workgroups over 256 x 256, 128 x 256 or 128 x 128 tiles. Output tiles that do not fill whole rounds of the
 //    CUs, or are fewer than the CUs, are split along K: each split range writes
@@ -382,10 +382,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
 
 // ---------------------------------------------------------------- skinny MFMA kernel (4 < M <= 64)
 
-// Workgroup g covers the 32-row prepared tile group g over the whole K with W
-// waves; wave w takes the tiles w, w + W, ... as in the decode kernel. Per
-// tile and MFMA step s (k = 32h + 8s + i, the same K order as the prepared
-// weight units), lane l dequantizes its 8 codes of weight row 32g + (l & 31)
+// Workgroup b covers the NG 32-row prepared tile groups NG b .. NG b + NG - 1
+// over the whole K with W waves; wave w takes the tiles w, w + W, ... as in the
+// decode kernel. Per tile, group g and MFMA step s (k = 32h + 8s + i, the same
+// K order as the prepared weight units), lane l dequantizes its 8 codes of
+// weight row 32g + (l & 31)
 // exactly to BF16 (E2M1 -> FP32, times the E4M3 scale, -> BF16) as the B
 // operand and loads the matching 8 BF16 of x rows 32 mt + (l & 31) as the A
 // operand of v_mfma_f32_32x32x16_bf16 (MT 32-row x tiles). For M > 16 (XF) x is
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
 // check). Weights and x fragments are loaded one tile per wave ahead (a
 // two-tile register ring): the x fragments cost 16 MT registers per tile, and
 // deeper rings lowered the occupancy enough to measure slower. Each wave ends
-// with a full 32 x 32 MT partial tile; the waves are added in a fixed tree
+// with NG full 32 x 32 MT partial tiles; the waves are added in a fixed tree
 // (W/2 + W/2, ..., 1 + 1) through LDS. W = 8 waves, or 16 when there are
 // fewer row groups than CUs (more loads in flight on each busy CU; measured
 // 17 % faster at M = 8 on 5120 x 17408, slower on 34816 x 5120).
