@@ -85,7 +85,10 @@ struct Params {
   int64_t M, N, K, ldd;
   float alpha;
   const float *alpha_dev;
-  int tiles_m, tiles_n;
+  int tiles_m, tiles_n;     // tile grid of D (in workgroup tiles; in 256 x 256 tiles when quad)
+  int count;                // tiles this launch computes
+  int first;                // quad: first 256 x 256 tile (raster index) whose quadrants it computes
+  int quad;                 // 1: 128 x 128 workgroups on the quadrants of 256 x 256 tiles first ..
 };
 
 // Raw buffer resource over [base, base + bytes); loads at offsets >= bytes
@@ -306,9 +309,28 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
   tn = w / rows;
 }
 
+// Origin of launch tile `tile`. Plain launches walk their own BT x BT tiles in
+// raster order; a quad launch (BT = 128) computes the four quadrants of the
+// 256 x 256 tiles first, first + 1, ... (consecutive indices: one tile's
+// quadrants, which then share A rows and W columns in one XCD's L2).
+template <int BT>
+__device__ __forceinline__ void tile_origin(const Params &p, int tile, int64_t &m0, int64_t &n0) {
+  int tm, tn;
+  if (BT == 128 && p.quad) {
+    tile_coords(p.first + (tile >> 2), p.tiles_m, p.tiles_n, tm, tn);
+    m0 = (int64_t)tm * 256 + ((tile >> 1) & 1) * 128;
+    n0 = (int64_t)tn * 256 + (tile & 1) * 128;
+  } else {
+    tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
+    m0 = (int64_t)tm * BT;
+    n0 = (int64_t)tn * BT;
+  }
+}
+
 // T = 4: 256 x 256 workgroup tiles, one workgroup per CU (all 512 registers of
-// a lane in use). T = 2: 128 x 128 tiles for problems with fewer 256 x 256
-// tiles than CUs, two workgroups per CU.
+// a lane in use). T = 2: 128 x 128 tiles, two workgroups per CU: for problems
+// with fewer 256 x 256 tiles than CUs, and for the quadrants of the 256 x 256
+// tiles of a last round that would leave at least half the CUs idle.
 template <bool OUT_BF16, int T>
 __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p) {
   constexpr int BT = 64 * T;                      // workgroup tile edge
@@ -316,7 +338,6 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
   const int t = threadIdx.x;
   const int wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int total = p.tiles_m * p.tiles_n;
   const int G = gridDim.x;
   // XCD-aware logical id: hardware ids b, b+8, b+16, ... run on one XCD; give
   // them consecutive logical ids so they take neighbouring tiles.
@@ -336,10 +357,10 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
     o.ws[i] = (uint32_t)(((wn * T + i) * kt) * 128 + r * 4);
   }
 
-  for (int tile = pid; tile < total; tile += G) {
-    int tm, tn;
-    tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * BT, n0 = (int64_t)tn * BT;
+  for (int tile = pid; tile < p.count; tile += G) {
+    int64_t m0, n0;
+    tile_origin<BT>(p, tile, m0, n0);
+    if (m0 >= p.M || n0 >= p.N) continue;   // a quadrant past the edge of D (uniform per workgroup)
     TileRsrc tr;
     const int64_t Mp = padded_rows(p.M);
     tr.a = p.a_tiled + (m0 >> 5) * kt * 1024;
@@ -400,32 +421,48 @@ nvfp4_status check_gemm_args(const uint8_t *w_prep, int64_t M, int64_t N, int64_
   return NVFP4_OK;
 }
 
+template <int T>
+void launch_tiles(const w4a4::Params &p, int grid, int out_dtype, hipStream_t s) {
+  if (out_dtype == NVFP4_OUT_BF16)
+    hipLaunchKernelGGL((w4a4::gemm_kernel<true, T>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((w4a4::gemm_kernel<false, T>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+}
+
 // The GEMM kernel proper on A already in the tile layout (arguments checked).
+//  * At least as many 256 x 256 tiles as CUs: the T = 4 kernel, one persistent
+//    workgroup per CU. When the tiles do not make whole rounds and the last
+//    round would use at most half the CUs, that round's tiles are left to a
+//    second launch of the T = 2 kernel on their 128 x 128 quadrants (two
+//    workgroups per CU, so the round takes about half as long). Each output
+//    element sees the same sequence of MFMAs either way: the results are the
+//    same bits as with T = 4 alone.
+//  * Fewer: the T = 2 kernel on 128 x 128 tiles.
 nvfp4_status launch_gemm(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N, int64_t K, float alpha,
                          const float *alpha_dev, void *d, int out_dtype, int64_t ldd, hipStream_t s) {
   DeviceInfo di;
   nvfp4_status st = device_info(&di);
   if (st != NVFP4_OK) return st;
-  // 256 x 256 tiles unless they cannot fill the CUs; then 128 x 128 tiles
-  const int T = ((M + 255) / 256) * ((N + 255) / 256) >= di.num_cus ? 4 : 2;
-  const int64_t bt = 64 * T;
-  const int64_t tiles_m = (M + bt - 1) / bt;
-  const int64_t tiles_n = (N + bt - 1) / bt;
-  w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tiles_m, (int)tiles_n};
-  const int64_t total = tiles_m * tiles_n;
-  const int64_t slots = (int64_t)di.num_cus * (T == 4 ? 1 : 2);
-  const int grid = (int)(total < slots ? total : slots);
-  if (T == 4) {
-    if (out_dtype == NVFP4_OUT_BF16)
-      hipLaunchKernelGGL((w4a4::gemm_kernel<true, 4>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((w4a4::gemm_kernel<false, 4>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
-  } else {
-    if (out_dtype == NVFP4_OUT_BF16)
-      hipLaunchKernelGGL((w4a4::gemm_kernel<true, 2>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((w4a4::gemm_kernel<false, 2>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+  const int64_t cus = di.num_cus;
+  const int64_t tm4 = (M + 255) / 256, tn4 = (N + 255) / 256, t4 = tm4 * tn4;
+  if (t4 >= cus) {
+    const int64_t rem = t4 % cus;
+    const int64_t full = rem > 0 && 2 * rem <= cus ? t4 - rem : t4;
+    w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tm4, (int)tn4, (int)full, 0, 0};
+    launch_tiles<4>(p, (int)cus, out_dtype, s);
+    NVFP4_LAUNCH_CHECK();
+    if (full < t4) {
+      p.count = (int)(4 * (t4 - full));   // <= 2 * cus: one workgroup per quadrant
+      p.first = (int)full;
+      p.quad = 1;
+      launch_tiles<2>(p, p.count, out_dtype, s);
+      NVFP4_LAUNCH_CHECK();
+    }
+    return NVFP4_OK;
   }
+  const int64_t tm2 = (M + 127) / 128, tn2 = (N + 127) / 128, t2 = tm2 * tn2;
+  w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tm2, (int)tn2, (int)t2, 0, 0};
+  launch_tiles<2>(p, (int)(t2 < 2 * cus ? t2 : 2 * cus), out_dtype, s);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }

@@ -192,6 +192,29 @@ def test_w4a4_big_tiles_ragged_strided_out(out_dtype, pad):
     assert_close(host(out), D, S, bf16=out_dtype == "bf16", what=f"strided {out_dtype} {M}x{N}x{K}")
 
 
+def test_w4a4_last_round_quadrants_same_bits():
+    """16 x 17 = 272 tiles of 256 x 256 on 256 CUs: the last 16 (at most half a round) run as
+    128 x 128 quadrants on two workgroups per CU. Ragged both ways: the last tile row holds 160
+    rows (lower quadrants part-filled), the last tile column 96 columns (right quadrants wholly
+    outside D, skipped). Every output checked against the oracle, and the same bits as the
+    columns of a wider W whose 16 x 32 tiles make whole rounds (the T = 4 kernel alone)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if 272 < cus or 2 * (272 % cus) > cus or (16 * 32) % cus != 0:
+        pytest.skip(f"tile counts chosen for 256 CUs, this device has {cus}")
+    M, N, K, Nw = 4000, 4192, 1024, 8192
+    a, sa = _random_nvfp4(71, M, K)
+    b, sb = _random_nvfp4(72, Nw, K)
+    wp, _ = _prep(b[:N], sb[:N])
+    wpw, _ = _prep(b, sb)
+    A, SA = dev(a), dev(sa)
+    out = nv.nvfp4_gemm_w4a4(A, SA, wp, N, K, 0.63, None, "bf16")
+    wide = nv.nvfp4_gemm_w4a4(A, SA, wpw, Nw, K, 0.63, None, "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(out, wide[:, :N]), "quadrant launch must give the T = 4 kernel's bits"
+    D, S = oracle_w4a4_exact_blocked(a, sa, b[:N], sb[:N], 0.63)
+    assert_close(host(out), D, S, bf16=True, what=f"last-round quadrants {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,K", [(64, 128), (77, 320), (1, 64)])
 def test_tile_activation_bytes_match_oracle_layout(M, K):
     """The activation tile layout is the prepared-weight index map (no folds needed:
