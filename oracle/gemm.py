@@ -8,7 +8,9 @@ Definitions followed:
   SFB N x K/16); the product accumulates in FP32 and the epilogue multiplies by
   alpha in FP32 before converting to the output type ("Version 3").
 * TileLang PR #3290, "Summary": W4A16 keeps the activations x [M, K] in BF16
-  and multiplies by the dequantized NVFP4 weight W [N, K] with a global scale.
+  and multiplies by the dequantized NVFP4 weight W [N, K] with a global or a
+  per-column scale. Here alpha is either one FP32 value or an FP32 vector [N],
+  one value per output column (column_alpha forms it), for both GEMMs.
 
 Exact evaluation of W4A4. With v = E2M1 value and s = E4M3 value, 2v is an
 integer in {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12} and 2**9 s is an integer in
@@ -64,9 +66,9 @@ def w4a4_exact(a_codes, a_scales, b_codes, b_scales, alpha, a_kind="e4m3", b_kin
         b = bi[:, k0:k0 + _CHUNK]
         S += (a @ b.T).astype(np.int64)
         T += (np.abs(a) @ np.abs(b).T).astype(np.int64)
-    scale = float(np.float32(alpha)) * 2.0 ** -20
-    D = S.astype(np.float64) * scale
-    sum_abs = T.astype(np.float64) * abs(scale)
+    al = _alpha64(alpha, N)
+    D = S.astype(np.float64) * 2.0 ** -20 * al
+    sum_abs = T.astype(np.float64) * 2.0 ** -20 * np.abs(al)
     D[a_nan, :] = np.nan
     D[:, b_nan] = np.nan
     return D, sum_abs
@@ -76,18 +78,32 @@ def w4a4_float64(a_codes, a_scales, b_codes, b_scales, alpha, a_kind="e4m3", b_k
     """Second, independent evaluation: decode to float64 and multiply directly."""
     a = decode_nvfp4(a_codes, a_scales, a_kind)
     b = decode_nvfp4(b_codes, b_scales, b_kind)
-    return float(np.float32(alpha)) * (a @ b.T)
+    return (a @ b.T) * _alpha64(alpha, b.shape[0])
 
 
 def w4a16(x_bf16_bits, w_codes, w_scales, alpha, w_kind="e4m3"):
     """y = alpha * x W~^T in float64 (products exact; float64 summation) and sum_k |alpha x w|."""
     x = formats.bf16_bits_to_f32(x_bf16_bits).astype(np.float64)
     w = decode_nvfp4(w_codes, w_scales, w_kind)
-    al = float(np.float32(alpha))
-    y = al * (x @ w.T)
+    al = _alpha64(alpha, w.shape[0])
+    y = (x @ w.T) * al
     with np.errstate(invalid="ignore"):
-        sum_abs = abs(al) * (np.abs(x) @ np.abs(w).T)
+        sum_abs = (np.abs(x) @ np.abs(w).T) * np.abs(al)
     return y, sum_abs
+
+
+def _alpha64(alpha, N):
+    """alpha as float64: a scalar (rounded to FP32 first), or an FP32 vector of the N columns."""
+    al = np.asarray(alpha)
+    if al.ndim == 0:
+        return float(np.float32(al))
+    assert al.shape == (N,) and al.dtype == np.float32, "per-column alpha: float32 [N]"
+    return al.astype(np.float64)
+
+
+def column_alpha(alpha_eff, alpha_col):
+    """Per-column alpha: fl32(alpha_eff * alpha_col[n]) for every output column n."""
+    return (np.float32(alpha_eff) * np.asarray(alpha_col, np.float32)).astype(np.float32)
 
 
 def alpha_product(alpha_host, alpha_dev=None):

@@ -334,6 +334,59 @@ def test_alpha_product_is_fp32():
     assert a == np.float32(np.float32(1.0 / 3.0) * np.float32(3.0))
 
 
+def test_column_alpha_is_fp32_per_column():
+    c = gemm.column_alpha(np.float32(1.0 / 3.0), [3.0, 0.1, -2.0, 0.0])
+    third = np.float32(1.0 / 3.0)
+    assert c.dtype == np.float32 and c.shape == (4,)
+    assert c[0] == np.float32(third * np.float32(3.0)) and c[0] == 1.0        # 0x3EAAAAAB * 3 rounds to 1
+    assert c[1] == np.float32(third * np.float32(0.1))
+    assert c[2] == -2 * third and c[3] == 0.0
+
+
+def test_per_column_alpha_w4a16_one_hot_zero_negative_scales():
+    """A global or a per-column weight scale (TileLang PR #3290, "Summary"; its tests pair the
+    per-column one with zero and negative block scales). A one-hot x = e_k reads out column
+    by column y[n] = alpha[n] * W~[n, k]; M != N, so a scale applied along rows fails."""
+    r = np.random.default_rng(41)
+    N, K = 64, 128
+    w = formats.pack_nibbles(r.integers(0, 16, (N, K)))
+    sw = r.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)       # E4M3 bytes below NaN, zero included
+    sw[::3] |= 0x80                                                 # negative scales
+    sw[1, :] = 0
+    al = gemm.column_alpha(0.75, 2.0 ** r.integers(-4, 5, N) * r.choice([-1.0, 1.0], N))
+    Wd = gemm.decode_nvfp4(w, sw)
+    x = np.zeros((3, K), np.float32)
+    x[0, 7] = 1.0
+    x[1, 100] = 1.0
+    x[2, :] = 1.0
+    y, S = gemm.w4a16(formats.f32_to_bf16_bits(x), w, sw, al)
+    np.testing.assert_array_equal(y[0], al.astype(np.float64) * Wd[:, 7])
+    np.testing.assert_array_equal(y[1], al.astype(np.float64) * Wd[:, 100])
+    assert not y[:, 1].any() and (Wd < 0).any()
+    np.testing.assert_allclose(y[2], al.astype(np.float64) * Wd.sum(axis=1), rtol=1e-14)
+    np.testing.assert_array_equal(S[0], np.abs(al.astype(np.float64) * Wd[:, 7]))
+
+
+def test_per_column_alpha_w4a4_reduces_to_scalar_per_column():
+    """Column n of the per-column result is the scalar-alpha result of that column alone
+    (alpha[n]), and a vector of equal entries gives the scalar result bit for bit."""
+    r = np.random.default_rng(53)
+    a = formats.pack_nibbles(r.integers(0, 16, (48, 256)))
+    sa = formats.round_e4m3_byte(2.0 ** r.uniform(-4, 4, (48, 16)))
+    b = formats.pack_nibbles(r.integers(0, 16, (64, 256)))
+    sb = formats.round_e4m3_byte(2.0 ** r.uniform(-4, 4, (64, 16)))
+    al = gemm.column_alpha(0.37, r.uniform(-3, 3, 64))
+    D, S = gemm.w4a4_exact(a, sa, b, sb, al)
+    for n in (0, 5, 47, 48, 63):
+        Dn, Sn = gemm.w4a4_exact(a, sa, b[n:n + 1], sb[n:n + 1], al[n])
+        np.testing.assert_array_equal(D[:, n], Dn[:, 0])
+        np.testing.assert_array_equal(S[:, n], Sn[:, 0])
+    D1, _ = gemm.w4a4_exact(a, sa, b, sb, 0.37)
+    Dv, _ = gemm.w4a4_exact(a, sa, b, sb, np.full(64, 0.37, np.float32))
+    np.testing.assert_array_equal(D1, Dv)
+    np.testing.assert_allclose(gemm.w4a4_float64(a, sa, b, sb, al), D, rtol=1e-12, atol=1e-30)
+
+
 # ------------------------------------------------------------------ prepared layout
 
 def test_prepared_size_matches_page_formula():
