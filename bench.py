@@ -94,15 +94,20 @@ def w4a4_square(nv, S, steps, warmup, gen=None, standard_too=False):
     ms = time_calls(lambda: nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, alpha, None, "bf16", out), steps, warmup)
     if not standard_too:
         return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12
+    # the same GEMM with a per-column alpha (a weight with per-column scales)
+    ac = torch.from_numpy(np.random.default_rng(7).uniform(0.5, 2.0, S).astype(np.float32)).cuda()
+    ms_col = time_calls(lambda: nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, alpha, None, "bf16", out, alpha_col=ac),
+                        steps, warmup)
     del at
     ca, sa, _, _ = quantized_square(nv, S, "A", gen)
     ws = torch.empty(nv.workspace_bytes(nv.OP_W4A4, S, S, S), dtype=torch.uint8, device="cuda")
     ms_std = time_calls(lambda: nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, alpha, None, "bf16", out, ws), steps, warmup)
-    return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12, ms_std
+    return ms, 2.0 * S ** 3 / (ms * 1e-3) / 1e12, ms_std, ms_col
 
 
-def w4a16_m1(nv, j, reps=3):
-    """M = 1 decode on shape j, weights rotated over >= 1 GiB, replayed from a CUDA graph."""
+def w4a16_m1(nv, j, reps=3, per_column=False):
+    """M = 1 decode on shape j, weights rotated over >= 1 GiB, replayed from a CUDA graph
+    (per_column: with a per-column alpha as well)."""
     import numpy as np
     import torch
     import synth
@@ -119,15 +124,18 @@ def w4a16_m1(nv, j, reps=3):
     alpha = float(np.float32(1.0) / np.float32(gW.item()))
     out = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
     ws = nv.workspace(nv.OP_W4A16, 1, N, K)
+    ac = None
+    if per_column:
+        ac = torch.from_numpy(np.random.default_rng(7).uniform(0.5, 2.0, N).astype(np.float32)).cuda()
     for c in copies:
-        nv.nvfp4_gemm_w4a16(x, c, N, K, alpha, out=out, ws=ws)
+        nv.nvfp4_gemm_w4a16(x, c, N, K, alpha, out=out, ws=ws, alpha_col=ac)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     st = torch.cuda.Stream()
     with torch.cuda.stream(st):
         with torch.cuda.graph(g, stream=st):
             for c in copies:
-                nv.nvfp4_gemm_w4a16(x, c, N, K, alpha, out=out, ws=ws)
+                nv.nvfp4_gemm_w4a16(x, c, N, K, alpha, out=out, ws=ws, alpha_col=ac)
     torch.cuda.synchronize()
     best = None
     for _ in range(reps):
@@ -302,10 +310,11 @@ def main():
         return
     S = args.size
     log(f"[bench] W4A4 {S}^3 bf16: {args.warmup} warmup + {args.steps} timed steps")
-    ms, tflops, ms_std = w4a4_square(nv, S, args.steps, args.warmup, standard_too=True)
+    ms, tflops, ms_std, ms_col = w4a4_square(nv, S, args.steps, args.warmup, standard_too=True)
     std_tflops = 2.0 * S ** 3 / (ms_std * 1e-3) / 1e12
     log(f"[bench] W4A4 {S}^3: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s (A from nvfp4_quantize_tiled); "
-        f"row-major A through nvfp4_gemm_w4a4 (tile copy + GEMM): {ms_std:.4f} ms, {std_tflops:.1f} TFLOP/s")
+        f"row-major A through nvfp4_gemm_w4a4 (tile copy + GEMM): {ms_std:.4f} ms, {std_tflops:.1f} TFLOP/s; "
+        f"with a per-column alpha: {ms_col:.4f} ms")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -337,6 +346,11 @@ def main():
             log(f"[bench] W4A16 M=1 {r['N']}x{r['K']}: {r['us']} us, {r['GBps']} GB/s")
             dec.append(r)
         extras["w4a16_m1"] = dec
+        r = w4a16_m1(nv, 2, per_column=True)
+        log(f"[bench] W4A16 M=1 {r['N']}x{r['K']} with a per-column alpha: {r['us']} us")
+        extras["per_column_alpha"] = {"w4a4_tiled_ms": round(ms_col, 5),
+                                      "w4a4_tiled_TFLOPs": round(2.0 * S ** 3 / (ms_col * 1e-3) / 1e12, 1),
+                                      "w4a16_m1": r}
         pf = prefill(nv, max(5, args.steps // 2), args.warmup)
         log(f"[bench] prefill: {pf}")
         extras["prefill_w4a4"] = pf

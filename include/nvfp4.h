@@ -101,6 +101,11 @@ nvfp4_status nvfp4_prepare_weight(const uint8_t *w_codes, const uint8_t *w_scale
 
 /* W4A4 GEMM: D = alpha_eff * (A.SFA)(W.SFW)^T with FP32 accumulation, where
  * alpha_eff = alpha * (*alpha_dev) in FP32 (alpha alone when alpha_dev is NULL).
+ *  alpha_col  NULL, or a per-column scale: FP32 [N], device, 4-byte aligned
+ *           (a weight with a global or a per-column scale: TileLang PR #3290,
+ *           "Summary"). Column n of the output is then scaled by
+ *           fl32(alpha_eff * alpha_col[n]) instead of alpha_eff, the product
+ *           formed in FP32 before the accumulator is multiplied by it.
  *  a_codes  [M][K/2] bytes, device, 16-byte aligned (rows are K/2 bytes apart).
  *  a_scales [M][K/16] bytes, device, E4M3 or UE4M3 bytes read as E4M3, 4-byte
  *           aligned. A NaN scale (0x7F/0xFF) propagates NaN into its output row.
@@ -115,8 +120,8 @@ nvfp4_status nvfp4_prepare_weight(const uint8_t *w_codes, const uint8_t *w_scale
  *      must not run concurrently. */
 nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
                              int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
-                             void *d, int out_dtype, int64_t ldd, void *ws, size_t ws_bytes,
-                             void *stream);
+                             const float *alpha_col, void *d, int out_dtype, int64_t ldd, void *ws,
+                             size_t ws_bytes, void *stream);
 
 /* Bytes of an activation in the tile layout: nvfp4_prepared_weight_bytes for M
  * rounded up to 32 rows (0 for M <= 0 or K % 64 != 0). */
@@ -135,12 +140,14 @@ nvfp4_status nvfp4_tile_activation(const uint8_t *a_codes, const uint8_t *a_scal
 /* nvfp4_gemm_w4a4 on an A that nvfp4_tile_activation has already tiled; the
  * other arguments as there. Needs no workspace. */
 nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N, int64_t K,
-                                   float alpha, const float *alpha_dev, void *d, int out_dtype, int64_t ldd,
-                                   void *stream);
+                                   float alpha, const float *alpha_dev, const float *alpha_col, void *d,
+                                   int out_dtype, int64_t ldd, void *stream);
 
 /* W4A16 GEMM: y = alpha_eff * x (W.SFW)^T, x and y BF16, FP32 accumulation
  * (TileLang PR #3290, "Summary": BF16 activations against NVFP4 weights with
- * E4M3 block scales, for M = 1 .. 1024 rows).
+ * E4M3 block scales, for M = 1 .. 1024 rows). alpha, alpha_dev and alpha_col
+ * (NULL or FP32 [N]: column n scaled by fl32(alpha_eff * alpha_col[n])) as for
+ * nvfp4_gemm_w4a4.
  *  x  [M][ldx] BF16 (uint16 bit patterns), device, 16-byte aligned, ldx % 8 == 0, ldx >= K.
  *  y  [M][ldy] BF16, device, 2-byte aligned, ldy >= N.
  *  M >= 0, N % 32 == 0, K % 64 == 0.
@@ -148,8 +155,9 @@ nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep
  *      NULL when that is 0). Calls that share a workspace must not run
  *      concurrently (use one workspace per stream). */
 nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_prep, int64_t M,
-                              int64_t N, int64_t K, float alpha, const float *alpha_dev, uint16_t *y,
-                              int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+                              int64_t N, int64_t K, float alpha, const float *alpha_dev,
+                              const float *alpha_col, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
+                              void *stream);
 
 /* BF16 -> NVFP4 quantizer for activations fed to W4A4 (the format as the pages
  * use it: packed E2M1 codes, E4M3 block scales, a per-tensor global scale;

@@ -7,8 +7,9 @@ library every call raises.
 
 Entry points (same names as the C ABI):
   nvfp4_prepare_weight(w_codes, w_scales, scale_kind="e4m3", out=None, bad_count=None)
-  nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None)
-  nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=None)
+  nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None,
+                  ws=None, alpha_col=None)
+  nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=None, alpha_col=None)
   nvfp4_quantize(x, codes=None, scales=None, g=None, inv_g=None, ws=None)
 """
 import ctypes
@@ -35,13 +36,13 @@ _SIGS = [
     ("nvfp4_workspace_init", ctypes.c_int, [_P, ctypes.c_size_t, _P]),
     ("nvfp4_prepare_weight", ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P]),
     ("nvfp4_gemm_w4a4", ctypes.c_int,
-     [_P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P]),
+     [_P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P]),
     ("nvfp4_tiled_activation_bytes", ctypes.c_size_t, [_I64, _I64]),
     ("nvfp4_tile_activation", ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     ("nvfp4_gemm_w4a4_tiled", ctypes.c_int,
-     [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, ctypes.c_int, _I64, _P]),
+     [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _P]),
     ("nvfp4_gemm_w4a16", ctypes.c_int,
-     [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _I64, _P, ctypes.c_size_t, _P]),
+     [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _I64, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize_tiled", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 ]
@@ -154,7 +155,19 @@ def nvfp4_prepare_weight(w_codes, w_scales, scale_kind="e4m3", out=None, bad_cou
     return out, bad_count
 
 
-def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None, ws=None):
+def _check_alpha_col(alpha_col, N):
+    """A per-column scale: None, or a contiguous float32 device tensor of N values."""
+    if alpha_col is None:
+        return None
+    if not isinstance(alpha_col, torch.Tensor) or alpha_col.dtype != torch.float32 or not alpha_col.is_cuda:
+        raise TypeError("alpha_col must be a float32 device tensor")
+    if alpha_col.dim() != 1 or alpha_col.shape[0] != N or not alpha_col.is_contiguous():
+        raise ValueError("alpha_col must be a contiguous [N] tensor")
+    return alpha_col
+
+
+def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None, ws=None,
+                    alpha_col=None):
     a_codes = _u8(a_codes, "a_codes")
     a_scales = _u8(a_scales, "a_scales")
     w_prep = _u8(w_prep, "w_prep")
@@ -172,11 +185,12 @@ def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, 
         raise ValueError("out must be [M][>=N] rows of out_dtype")
     if alpha_dev is not None and (alpha_dev.dtype != torch.float32 or not alpha_dev.is_cuda):
         raise TypeError("alpha_dev must be a float32 device tensor")
+    alpha_col = _check_alpha_col(alpha_col, N)
     if ws is None and M > 0:
         ws = torch.empty(workspace_bytes(OP_W4A4, M, N, K), dtype=torch.uint8, device=a_codes.device)
     nws = 0 if ws is None else ws.numel()
     _check(lib().nvfp4_gemm_w4a4(_ptr(a_codes), _ptr(a_scales), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
-                                 _ptr(out), od[0], out.stride(0), _ptr(ws), nws, _stream()))
+                                 _ptr(alpha_col), _ptr(out), od[0], out.stride(0), _ptr(ws), nws, _stream()))
     return out
 
 
@@ -196,7 +210,8 @@ def nvfp4_tile_activation(a_codes, a_scales, out=None):
     return out
 
 
-def nvfp4_gemm_w4a4_tiled(a_tiled, M, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None):
+def nvfp4_gemm_w4a4_tiled(a_tiled, M, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None,
+                          alpha_col=None):
     """nvfp4_gemm_w4a4 on an activation already in the tile layout (nvfp4_tile_activation)."""
     a_tiled = _u8(a_tiled, "a_tiled")
     w_prep = _u8(w_prep, "w_prep")
@@ -213,12 +228,13 @@ def nvfp4_gemm_w4a4_tiled(a_tiled, M, w_prep, N, K, alpha=1.0, alpha_dev=None, o
         raise ValueError("out must be [M][>=N] rows of out_dtype")
     if alpha_dev is not None and (alpha_dev.dtype != torch.float32 or not alpha_dev.is_cuda):
         raise TypeError("alpha_dev must be a float32 device tensor")
+    alpha_col = _check_alpha_col(alpha_col, N)
     _check(lib().nvfp4_gemm_w4a4_tiled(_ptr(a_tiled), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
-                                       _ptr(out), od[0], out.stride(0), _stream()))
+                                       _ptr(alpha_col), _ptr(out), od[0], out.stride(0), _stream()))
     return out
 
 
-def nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=None):
+def nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=None, alpha_col=None):
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise TypeError("x must be a CUDA tensor")
     if x.dtype != torch.bfloat16:
@@ -235,11 +251,14 @@ def nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=No
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[0] != M or out.stride(1) != 1:
         raise ValueError("out must be [M][>=N] bfloat16")
+    if alpha_dev is not None and (alpha_dev.dtype != torch.float32 or not alpha_dev.is_cuda):
+        raise TypeError("alpha_dev must be a float32 device tensor")
+    alpha_col = _check_alpha_col(alpha_col, N)
     if ws is None:
         ws = workspace(OP_W4A16, M, N, K, x.device)
     nws = 0 if ws is None else ws.numel()
     _check(lib().nvfp4_gemm_w4a16(_ptr(x), x.stride(0), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
-                                  _ptr(out), out.stride(0), _ptr(ws), nws, _stream()))
+                                  _ptr(alpha_col), _ptr(out), out.stride(0), _ptr(ws), nws, _stream()))
     return out
 
 

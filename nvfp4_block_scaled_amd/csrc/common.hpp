@@ -92,6 +92,12 @@ __device__ __forceinline__ float load_alpha(float alpha, const float *alpha_dev)
   return alpha_dev ? alpha * __builtin_nontemporal_load(alpha_dev) : alpha;
 }
 
+// The alpha of output column n: alpha_eff times the column's own scale
+// alpha_col[n] (one FP32 product), or alpha_eff when there is no per-column scale.
+__device__ __forceinline__ float col_alpha(float al, const float *alpha_col, int64_t n) {
+  return alpha_col ? al * alpha_col[n] : al;
+}
+
 // ---------------------------------------------------------------- host side
 
 struct DeviceInfo {

@@ -243,7 +243,7 @@ static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
 template <int M, int R, int W, int U>
 __device__ __forceinline__ void decode_rows(int64_t b, uint16_t *xs, const uint16_t *__restrict__ x, int64_t ldx,
                                             const uint8_t *__restrict__ wp, int64_t N, int64_t K, float alpha,
-                                            const float *alpha_dev, uint16_t *__restrict__ y, int64_t ldy) {
+                                            const float *alpha_dev, const float *alpha_col, uint16_t *__restrict__ y, int64_t ldy) {
   constexpr int TPL = 32 / R;                       // tiles per wave load
   __shared__ float red[W][M][R];
   const int64_t T = K / 64;
@@ -352,7 +352,8 @@ __device__ __forceinline__ void decode_rows(int64_t b, uint16_t *xs, const uint1
 #pragma unroll
     for (int w = 1; w < W; w++) v += red[w][m][rr];
     const float al = load_alpha(alpha, alpha_dev);
-    y[m * ldy + g * 32 + row0 + rr] = f32_to_bf16_rne(al * v);
+    const int64_t n = g * 32 + row0 + rr;
+    y[m * ldy + n] = f32_to_bf16_rne(col_alpha(al, alpha_col, n) * v);
   }
 }
 
@@ -366,17 +367,17 @@ __device__ __forceinline__ void decode_rows(int64_t b, uint16_t *xs, const uint1
 template <int M, int R, int W, int U, int TR>
 __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restrict__ x, int64_t ldx,
                                                         const uint8_t *__restrict__ wp, int64_t N, int64_t K,
-                                                        float alpha, const float *alpha_dev,
+                                                        float alpha, const float *alpha_dev, const float *alpha_col,
                                                         uint16_t *__restrict__ y, int64_t ldy, int64_t nfull) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];     // [M][K]
   const int64_t b = blockIdx.x;
   if constexpr (TR == 0) {
-    decode_rows<M, R, W, U>(b, xs, x, ldx, wp, N, K, alpha, alpha_dev, y, ldy);
+    decode_rows<M, R, W, U>(b, xs, x, ldx, wp, N, K, alpha, alpha_dev, alpha_col, y, ldy);
   } else {
     if (b < nfull)
-      decode_rows<M, R, W, U>(b, xs, x, ldx, wp, N, K, alpha, alpha_dev, y, ldy);
+      decode_rows<M, R, W, U>(b, xs, x, ldx, wp, N, K, alpha, alpha_dev, alpha_col, y, ldy);
     else
-      decode_rows<M, TR, W, U>(nfull * (R / TR) + (b - nfull), xs, x, ldx, wp, N, K, alpha, alpha_dev, y, ldy);
+      decode_rows<M, TR, W, U>(nfull * (R / TR) + (b - nfull), xs, x, ldx, wp, N, K, alpha, alpha_dev, alpha_col, y, ldy);
   }
 }
 
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(256) void tile_x_kernel(const uint16_t *__restrict_
 template <int MT, bool XF, int W, int NG>
 __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restrict__ x, int64_t ldx,
                                                              const uint8_t *__restrict__ wp, int64_t M, int64_t N,
-                                                             int64_t K, float alpha, const float *alpha_dev,
+                                                             int64_t K, float alpha, const float *alpha_dev, const float *alpha_col,
                                                              uint16_t *__restrict__ y, int64_t ldy,
                                                              const uint8_t *__restrict__ xf) {
   constexpr int U = kSkAhead;                          // tiles per wave per batch
@@ -534,12 +535,13 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
 #pragma unroll
     for (int q = 0; q < NG; q++) {
       const int64_t n = (g0 + q) * 32 + r;
+      const float an = col_alpha(al, alpha_col, n);
 #pragma unroll
       for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int j = 0; j < 16; j++) {
           const int64_t m = 32 * mt + 8 * (j >> 2) + 4 * h + (j & 3);
-          if (m < M) y[m * ldy + n] = f32_to_bf16_rne(al * acc[q][mt][j]);
+          if (m < M) y[m * ldy + n] = f32_to_bf16_rne(an * acc[q][mt][j]);
         }
     }
   }
@@ -582,6 +584,7 @@ struct Params {
   int64_t ldy, M, N, K;
   float alpha;
   const float *alpha_dev;
+  const float *alpha_col;  // per-column scale [N] or null
   int tiles_m, tiles_n;
   int full;          // tiles [0, full) run whole, persistent over gridDim.x workgroups
   int rem;           // tiles [full, full + rem) are split along K over all workgroups
@@ -924,12 +927,15 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
 #pragma unroll
   for (int i = 0; i < TM; i++) {
 #pragma unroll
-    for (int j = 0; j < TN; j++)
+    for (int j = 0; j < TN; j++) {
+      // the alpha of this lane's column (columns past N are not stored)
+      const float aj = j * 32 + r < ncols ? col_alpha(alpha, p.alpha_col, col0 + j * 32 + r) : alpha;
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int row = 8 * (e >> 2) + 4 * h + (e & 3);
-        *reinterpret_cast<uint16_t *>(reg + row * ROW_BYTES + (j * 32 + r) * 2) = f32_to_bf16_rne(alpha * acc[i][j][e]);
+        *reinterpret_cast<uint16_t *>(reg + row * ROW_BYTES + (j * 32 + r) * 2) = f32_to_bf16_rne(aj * acc[i][j][e]);
       }
+    }
     __syncthreads();
     constexpr int PIECES = ROW_BYTES / 16;
     for (int q = lane; q < 32 * PIECES; q += 64) {
@@ -1080,11 +1086,12 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
     const int wave = part / (TM * TN), i = (part / TN) % TM, j = part % TN;
     const int wm = wave / WGN, wn = wave % WGN;
     const int64_t col = n0 + wn * 32 * TN + 32 * j + r;
+    const float ac = col < p.N ? col_alpha(alpha, p.alpha_col, col) : alpha;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       const int e = 4 * q + k;
       const int64_t m = m0 + wm * 32 * TM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-      if (m < p.M && col < p.N) p.y[m * p.ldy + col] = f32_to_bf16_rne(alpha * v[u][k]);
+      if (m < p.M && col < p.N) p.y[m * p.ldy + col] = f32_to_bf16_rne(ac * v[u][k]);
     }
   }
 }
@@ -1104,14 +1111,14 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 using namespace nvfp4;
 
 extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_prep, int64_t M, int64_t N,
-                                         int64_t K, float alpha, const float *alpha_dev, uint16_t *y, int64_t ldy,
+                                         int64_t K, float alpha, const float *alpha_dev, const float *alpha_col, uint16_t *y, int64_t ldy,
                                          void *ws, size_t ws_bytes, void *stream) {
   if (M < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0 || ldx < K || ldy < N) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
   if (!x || !w_prep || !y) return NVFP4_ERR_NULL;
   if (!(alpha == alpha) || alpha - alpha != 0.0f) return NVFP4_ERR_VALUE;
   if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(w_prep, 16) || !aligned(y, 2) ||
-      (alpha_dev && !aligned(alpha_dev, 4)))
+      (alpha_dev && !aligned(alpha_dev, 4)) || (alpha_col && !aligned(alpha_col, 4)))
     return NVFP4_ERR_ALIGN;
   DeviceInfo di;
   nvfp4_status st = device_info(&di);
@@ -1129,7 +1136,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   case D * 8 + MM: {                                                                                           \
     constexpr w4a16::DecodeShape sh = w4a16::kDecodeShapes[D];                                                 \
     hipLaunchKernelGGL((w4a16::decode_kernel<MM, sh.R, sh.W, sh.U, 0>), dim3((unsigned)plan.grid_x),        \
-                       dim3(sh.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy, plan.nfull);   \
+                       dim3(sh.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, alpha_col, y, ldy, plan.nfull);   \
     break;                                                                                                     \
   }
 #define NVFP4_DECODE_SHAPE(D) \
@@ -1137,10 +1144,10 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     constexpr w4a16::DecodeShape s0 = w4a16::kDecodeShapes[0];
     if (plan.tr == 8)
       hipLaunchKernelGGL((w4a16::decode_kernel<1, s0.R, s0.W, s0.U, 8>), dim3((unsigned)plan.grid_x),
-                         dim3(s0.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy, plan.nfull);
+                         dim3(s0.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, alpha_col, y, ldy, plan.nfull);
     else if (plan.tr == 16)
       hipLaunchKernelGGL((w4a16::decode_kernel<1, s0.R, s0.W, s0.U, 16>), dim3((unsigned)plan.grid_x),
-                         dim3(s0.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, y, ldy, plan.nfull);
+                         dim3(s0.W * 64), lds, s, x, ldx, w_prep, N, K, alpha, alpha_dev, alpha_col, y, ldy, plan.nfull);
     else
       switch (key) {
         NVFP4_DECODE_SHAPE(0)
@@ -1162,7 +1169,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
       NVFP4_LAUNCH_CHECK();
     }
     w4a16::big::Params bp{x,     ldx,           w_prep,        y,           ldy,          M,
-                          N,     K,             alpha,         alpha_dev,   (int)b.tiles_m, (int)b.tiles_n,
+                          N,     K,             alpha,         alpha_dev,   alpha_col,   (int)b.tiles_m, (int)b.tiles_n,
                           (int)b.full, (int)b.rem, static_cast<float *>(ws), xf, (int)xmt};
     const unsigned grid = (unsigned)b.G, fix_grid = (unsigned)(b.rem * b.TM * b.TN);
 #define NVFP4_BIG(TMV, TNV, WGMV)                                                                                \
@@ -1194,7 +1201,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     const int W = w4a16::skinny_waves(N, di.num_cus);
 #define NVFP4_SKINNY(MTV, XFV, WV, NGV)                                                                         \
   hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV, WV, NGV>), dim3(grid / NGV), dim3(WV * 64), 0, s, x, ldx,     \
-                     w_prep, M, N, K, alpha, alpha_dev, y, ldy, xf)
+                     w_prep, M, N, K, alpha, alpha_dev, alpha_col, y, ldy, xf)
     const bool ng = W == 8 && plan.grid_x % w4a16::kSkinnyNG == 0;
     if (W == 16) {
       if (!xf_path) NVFP4_SKINNY(1, false, 16, 1);

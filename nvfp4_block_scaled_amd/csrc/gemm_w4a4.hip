@@ -85,6 +85,7 @@ struct Params {
   int64_t M, N, K, ldd;
   float alpha;
   const float *alpha_dev;
+  const float *alpha_col;   // per-column scale [N] or null
   int tiles_m, tiles_n;     // tile grid of D (in workgroup tiles; in 256 x 256 tiles when quad)
   int count;                // tiles this launch computes
   int first;                // quad: first 256 x 256 tile (raster index) whose quadrants it computes
@@ -262,16 +263,19 @@ __device__ __forceinline__ void epilogue(uint8_t *smem, const Params &p, int64_t
 #pragma unroll
   for (int i = 0; i < T; i++) {
 #pragma unroll
-    for (int j = 0; j < T; j++)
+    for (int j = 0; j < T; j++) {
+      // the alpha of this lane's column (columns past N are not stored)
+      const float aj = j * 32 + r < ncols ? col_alpha(alpha, p.alpha_col, col0 + j * 32 + r) : alpha;
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int row = 8 * (e >> 2) + 4 * h + (e & 3);
-        const float v = alpha * acc[i][j][e];
+        const float v = aj * acc[i][j][e];
         if (OUT_BF16)
           *reinterpret_cast<uint16_t *>(reg + row * ROW_BYTES + (j * 32 + r) * 2) = f32_to_bf16_rne(v);
         else
           *reinterpret_cast<float *>(reg + row * ROW_BYTES + (j * 32 + r) * 4) = v;
       }
+    }
     __syncthreads();
     constexpr int PIECES = ROW_BYTES / 16;        // 16-byte pieces per row
 #pragma unroll
@@ -407,14 +411,16 @@ size_t nvfp4::w4a4_workspace_bytes(int64_t M, int64_t K) {
 namespace {
 
 nvfp4_status check_gemm_args(const uint8_t *w_prep, int64_t M, int64_t N, int64_t K, float alpha,
-                             const float *alpha_dev, void *d, int out_dtype, int64_t ldd) {
+                             const float *alpha_dev, const float *alpha_col, void *d, int out_dtype, int64_t ldd) {
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0 || ldd < N) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
   if (!w_prep || !d) return NVFP4_ERR_NULL;
   if (!(alpha == alpha) || alpha - alpha != 0.0f) return NVFP4_ERR_VALUE;
   const size_t esz = out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
-  if (!aligned(w_prep, 16) || !aligned(d, esz) || (alpha_dev && !aligned(alpha_dev, 4))) return NVFP4_ERR_ALIGN;
+  if (!aligned(w_prep, 16) || !aligned(d, esz) || (alpha_dev && !aligned(alpha_dev, 4)) ||
+      (alpha_col && !aligned(alpha_col, 4)))
+    return NVFP4_ERR_ALIGN;
   // 32-bit buffer offsets inside the code tiles of one 256-row (256-column) tile
   if ((int64_t)8 * (K / 64) * 1024 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
   if ((M + 127) / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return NVFP4_ERR_SHAPE;
@@ -439,7 +445,7 @@ void launch_tiles(const w4a4::Params &p, int grid, int out_dtype, hipStream_t s)
 //    same bits as with T = 4 alone.
 //  * Fewer: the T = 2 kernel on 128 x 128 tiles.
 nvfp4_status launch_gemm(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N, int64_t K, float alpha,
-                         const float *alpha_dev, void *d, int out_dtype, int64_t ldd, hipStream_t s) {
+                         const float *alpha_dev, const float *alpha_col, void *d, int out_dtype, int64_t ldd, hipStream_t s) {
   DeviceInfo di;
   nvfp4_status st = device_info(&di);
   if (st != NVFP4_OK) return st;
@@ -448,7 +454,7 @@ nvfp4_status launch_gemm(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t 
   if (t4 >= cus) {
     const int64_t rem = t4 % cus;
     const int64_t full = rem > 0 && 2 * rem <= cus ? t4 - rem : t4;
-    w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tm4, (int)tn4, (int)full, 0, 0};
+    w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, alpha_col, (int)tm4, (int)tn4, (int)full, 0, 0};
     launch_tiles<4>(p, (int)cus, out_dtype, s);
     NVFP4_LAUNCH_CHECK();
     if (full < t4) {
@@ -461,7 +467,7 @@ nvfp4_status launch_gemm(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t 
     return NVFP4_OK;
   }
   const int64_t tm2 = (M + 127) / 128, tn2 = (N + 127) / 128, t2 = tm2 * tn2;
-  w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, (int)tm2, (int)tn2, (int)t2, 0, 0};
+  w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, alpha_col, (int)tm2, (int)tn2, (int)t2, 0, 0};
   launch_tiles<2>(p, (int)(t2 < 2 * cus ? t2 : 2 * cus), out_dtype, s);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
@@ -494,20 +500,21 @@ extern "C" nvfp4_status nvfp4_tile_activation(const uint8_t *a_codes, const uint
 }
 
 extern "C" nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N,
-                                              int64_t K, float alpha, const float *alpha_dev, void *d,
-                                              int out_dtype, int64_t ldd, void *stream) {
-  nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, d, out_dtype, ldd);
+                                              int64_t K, float alpha, const float *alpha_dev,
+                                              const float *alpha_col, void *d, int out_dtype, int64_t ldd,
+                                              void *stream) {
+  nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd);
   if (st != NVFP4_OK || M == 0) return st;
   if (!a_tiled) return NVFP4_ERR_NULL;
   if (!aligned(a_tiled, 16)) return NVFP4_ERR_ALIGN;
-  return launch_gemm(a_tiled, w_prep, M, N, K, alpha, alpha_dev, d, out_dtype, ldd, (hipStream_t)stream);
+  return launch_gemm(a_tiled, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, (hipStream_t)stream);
 }
 
 extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
                                         int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
-                                        void *d, int out_dtype, int64_t ldd, void *ws, size_t ws_bytes,
-                                        void *stream) {
-  nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, d, out_dtype, ldd);
+                                        const float *alpha_col, void *d, int out_dtype, int64_t ldd, void *ws,
+                                        size_t ws_bytes, void *stream) {
+  nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd);
   if (st != NVFP4_OK || M == 0) return st;
   if (!a_codes || !a_scales) return NVFP4_ERR_NULL;
   if (!aligned(a_codes, 16) || !aligned(a_scales, 4)) return NVFP4_ERR_ALIGN;
@@ -521,5 +528,5 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a
   uint8_t *at = static_cast<uint8_t *>(ws);
   launch_tile_a(a_codes, a_scales, M, K, at, s);
   NVFP4_LAUNCH_CHECK();
-  return launch_gemm(at, w_prep, M, N, K, alpha, alpha_dev, d, out_dtype, ldd, s);
+  return launch_gemm(at, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, s);
 }

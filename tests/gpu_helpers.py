@@ -134,7 +134,8 @@ def oracle_w4a4_exact_blocked(a, sa, b, sb, alpha, tile=2048):
 
     def run(rc):
         r, c = rc
-        d, t = gemm.w4a4_exact(a[r:r + tile], sa[r:r + tile], b[c:c + tile], sb[c:c + tile], alpha)
+        al = alpha[c:c + tile] if np.ndim(alpha) else alpha      # a per-column alpha goes with its columns
+        d, t = gemm.w4a4_exact(a[r:r + tile], sa[r:r + tile], b[c:c + tile], sb[c:c + tile], al)
         D[r:r + tile, c:c + tile] = d
         S[r:r + tile, c:c + tile] = t
     _on_host_cores(run, [(r, c) for r in range(0, M, tile) for c in range(0, N, tile)])
@@ -148,7 +149,8 @@ def oracle_w4a16_blocked(x, w_codes, w_scales, alpha, cols=2048):
     S = np.empty((M, N))
 
     def run(c):
-        yy, t = gemm.w4a16(x, w_codes[c:c + cols], w_scales[c:c + cols], alpha)
+        al = alpha[c:c + cols] if np.ndim(alpha) else alpha
+        yy, t = gemm.w4a16(x, w_codes[c:c + cols], w_scales[c:c + cols], al)
         y[:, c:c + cols] = yy
         S[:, c:c + cols] = t
     _on_host_cores(run, range(0, N, cols))

@@ -49,13 +49,13 @@ ODD = ctypes.c_void_p(0x10001)
 def test_gemm_w4a4_argument_checks():
     f = nv.lib().nvfp4_gemm_w4a4
     need = nv.lib().nvfp4_workspace_bytes(nv.OP_W4A4, 64, 64, 128)
-    ok = dict(a=FAKE, s=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ad=None, d=FAKE, dt=nv.OUT_BF16, ldd=64,
+    ok = dict(a=FAKE, s=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ad=None, ac=None, d=FAKE, dt=nv.OUT_BF16, ldd=64,
               ws=None, nws=0)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["a"], a["s"], a["w"], a["M"], a["N"], a["K"], a["alpha"], a["ad"], a["d"], a["dt"], a["ldd"],
-                 a["ws"], a["nws"], None)
+        return f(a["a"], a["s"], a["w"], a["M"], a["N"], a["K"], a["alpha"], a["ad"], a["ac"], a["d"], a["dt"],
+                 a["ldd"], a["ws"], a["nws"], None)
     assert call(dt=7) == nv.ERR_DTYPE
     assert call(K=96) == nv.ERR_SHAPE
     assert call(N=48) == nv.ERR_SHAPE
@@ -71,6 +71,8 @@ def test_gemm_w4a4_argument_checks():
     assert call() == nv.ERR_WORKSPACE             # A is re-tiled into the workspace
     assert call(ws=FAKE, nws=need - 1) == nv.ERR_WORKSPACE
     assert call(ws=ODD, nws=need) == nv.ERR_ALIGN
+    assert call(ac=ODD, ws=FAKE, nws=need) == nv.ERR_ALIGN   # per-column alpha: FP32 aligned
+    assert call(ad=ODD, ws=FAKE, nws=need) == nv.ERR_ALIGN
 
 
 def test_tile_activation_and_tiled_gemm_argument_checks():
@@ -87,8 +89,8 @@ def test_tile_activation_and_tiled_gemm_argument_checks():
     assert t(FAKE, FAKE, 64, 128, ODD, None) == nv.ERR_ALIGN
     g = L.nvfp4_gemm_w4a4_tiled
 
-    def call(at=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, d=FAKE, dt=nv.OUT_BF16, ldd=64):
-        return g(at, w, M, N, K, alpha, None, d, dt, ldd, None)
+    def call(at=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ac=None, d=FAKE, dt=nv.OUT_BF16, ldd=64):
+        return g(at, w, M, N, K, alpha, None, ac, d, dt, ldd, None)
     assert call(dt=5) == nv.ERR_DTYPE
     assert call(K=96) == nv.ERR_SHAPE
     assert call(N=40) == nv.ERR_SHAPE
@@ -98,6 +100,7 @@ def test_tile_activation_and_tiled_gemm_argument_checks():
     assert call(alpha=float("nan")) == nv.ERR_VALUE
     assert call(at=ODD) == nv.ERR_ALIGN
     assert call(d=ODD) == nv.ERR_ALIGN
+    assert call(ac=ODD) == nv.ERR_ALIGN
 
 
 def test_quantize_tiled_argument_checks():
@@ -113,8 +116,8 @@ def test_quantize_tiled_argument_checks():
 def test_gemm_w4a16_argument_checks():
     f = nv.lib().nvfp4_gemm_w4a16
 
-    def call(x=FAKE, ldx=128, w=FAKE, M=1, N=64, K=128, alpha=1.0, y=FAKE, ldy=64, ws=None, nws=0):
-        return f(x, ldx, w, M, N, K, alpha, None, y, ldy, ws, nws, None)
+    def call(x=FAKE, ldx=128, w=FAKE, M=1, N=64, K=128, alpha=1.0, ac=None, y=FAKE, ldy=64, ws=None, nws=0):
+        return f(x, ldx, w, M, N, K, alpha, None, ac, y, ldy, ws, nws, None)
     assert call(K=100) == nv.ERR_SHAPE
     assert call(ldx=64) == nv.ERR_SHAPE
     assert call(ldy=32) == nv.ERR_SHAPE
@@ -123,6 +126,7 @@ def test_gemm_w4a16_argument_checks():
     assert call(alpha=float("-inf")) == nv.ERR_VALUE
     assert call(ldx=132) == nv.ERR_ALIGN
     assert call(x=ODD) == nv.ERR_ALIGN
+    assert call(ac=ODD) == nv.ERR_ALIGN
 
 
 def test_prepare_and_quantize_argument_checks():

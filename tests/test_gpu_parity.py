@@ -433,6 +433,62 @@ def test_w4a16_big_ragged(M, N, K):
     assert_close(host(out), y, S, bf16=True, what=f"w4a16 big {M}x{N}x{K}")
 
 
+# ------------------------------------------------------------------ per-column alpha
+
+def _alpha_col(seed, N):
+    """Per-column scales of both signs over 2^-6 .. 2^6, every 17th zero."""
+    r = np.random.default_rng(seed)
+    c = (2.0 ** r.uniform(-6, 6, N) * r.choice([-1.0, 1.0], N)).astype(np.float32)
+    c[::17] = 0.0
+    return c
+
+
+@pytest.mark.parametrize("M,N,K,entry", [(300, 320, 192, "std"), (4000, 4192, 256, "std"),
+                                         (4000, 4192, 256, "tiled"), (4100, 4128, 128, "tiled")])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_w4a4_per_column_alpha(M, N, K, entry, out_dtype):
+    """A global or a per-column weight scale (TileLang PR #3290, "Summary"): column n is scaled
+    by fl32(alpha_eff * alpha_col[n]), alpha_eff = alpha * *alpha_dev. 128 x 128 tiles (300 x 320);
+    256 x 256 tiles with the last round as quadrants and ragged edges; full check."""
+    a, sa = _random_nvfp4(M + 3, M, K)
+    b, sb = _random_nvfp4(N + 4, N, K)
+    wp, _ = _prep(b, sb)
+    ac = _alpha_col(M + N, N)
+    ad = torch.tensor([1.5], dtype=torch.float32, device="cuda")
+    if entry == "std":
+        out = nv.nvfp4_gemm_w4a4(dev(a), dev(sa), wp, N, K, 0.3, ad, out_dtype, alpha_col=dev(ac))
+    else:
+        at = nv.nvfp4_tile_activation(dev(a), dev(sa))
+        out = nv.nvfp4_gemm_w4a4_tiled(at, M, wp, N, K, 0.3, ad, out_dtype, alpha_col=dev(ac))
+    torch.cuda.synchronize()
+    al = gemm.column_alpha(gemm.alpha_product(0.3, np.float32(1.5)), ac)
+    D, S = oracle_w4a4_exact_blocked(a, sa, b, sb, al)
+    assert_close(host(out), D, S, bf16=out_dtype == "bf16", what=f"per-column alpha {entry} {M}x{N}x{K}")
+    assert not host(out)[:, ::17].any(), "zero column scales give zero columns"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 34816, 256), (3, 320, 640), (16, 17408, 1088), (40, 2048, 1024),
+                                   (100, 512, 1024), (300, 56320, 192), (1000, 2080, 320)])
+def test_w4a16_per_column_alpha_zero_negative_scales(M, N, K):
+    """Per-column alpha with zero and negative block scales (the combination the pages' tests
+    name) on every W4A16 path: decode with the cut tail (1 x 34816), decode M = 3, skinny on x
+    rows (16) and on the fragment-order copy (40), the 128 x 128 split with a fix-up
+    (100 x 512, 1000 x 2080), 256 x 256 tiles with split leftovers (300 x 56320); full check."""
+    x, b, sb, _, alpha = _w4a16_case(M, N, K, M + N + K + 5)
+    sb = sb.copy()
+    sb[::5] |= 0x80
+    sb[1::7] = 0
+    wp, bad = _prep(b, sb)
+    assert bad == 0
+    ac = _alpha_col(N + K, N)
+    ad = torch.tensor([0.75], dtype=torch.float32, device="cuda")
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha, ad, alpha_col=dev(ac))
+    torch.cuda.synchronize()
+    al = gemm.column_alpha(gemm.alpha_product(alpha, np.float32(0.75)), ac)
+    y, S = oracle_w4a16_blocked(x, b, sb, al)
+    assert_close(host(out), y, S, bf16=True, what=f"w4a16 per-column alpha M={M} {N}x{K}")
+
+
 _DECODE_Q = {}
 
 
