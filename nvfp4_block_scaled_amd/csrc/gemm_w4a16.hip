@@ -914,7 +914,7 @@ __device__ __forceinline__ void tile_mainloop_d(const Params &p, int tile, int64
 
 // Epilogue of a whole tile: per wave 32 x 32TN staging of BF16 in LDS (after
 // every wave is done with x), then 16-byte row pieces.
-template <int TM, int TN>
+template <int TM, int TN, bool COLS>
 __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, float alpha, int64_t m0, int64_t n0,
                                               int wave, int wm, int wn, f32x16_t (&acc)[TM][TN]) {
   const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
@@ -929,7 +929,7 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       // the alpha of this lane's column (columns past N are not stored)
-      const float aj = j * 32 + r < ncols ? col_alpha(alpha, p.alpha_col, col0 + j * 32 + r) : alpha;
+      const float aj = COLS && j * 32 + r < ncols ? alpha * p.alpha_col[col0 + j * 32 + r] : alpha;
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int row = 8 * (e >> 2) + 4 * h + (e & 3);
@@ -960,7 +960,9 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
 // TM x TN MFMA tiles per wave, the 4 waves WGM x (4 / WGM) over the tile:
 // (2, 2, 2) stages x through LDS; (4, 4, 2) and (4, 2, 1) read x straight into
 // registers (tile_mainloop_d).
-template <int TM, int TN, int WGM>
+// COLS: p.alpha_col is set (a separate instantiation, so that the kernel
+// without a per-column scale keeps its registers for the main loop).
+template <int TM, int TN, int WGM, bool COLS>
 __global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Params p) {
   constexpr bool kLds = TM == 2 && TN == 2;
   constexpr int WGN = 4 / WGM;
@@ -986,7 +988,7 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Par
       tile_mainloop<2>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
     else
       tile_mainloop_d<TM, TN, WGM>(p, tile, 0, nch, ow, ows, wm, acc, m0, n0);
-    tile_epilogue<TM, TN>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
+    tile_epilogue<TM, TN, COLS>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
   }
   if (p.rem > 0) {
     int64_t s, e;
@@ -1173,7 +1175,12 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
                           (int)b.full, (int)b.rem, static_cast<float *>(ws), xf, (int)xmt};
     const unsigned grid = (unsigned)b.G, fix_grid = (unsigned)(b.rem * b.TM * b.TN);
 #define NVFP4_BIG(TMV, TNV, WGMV)                                                                                \
-  hipLaunchKernelGGL((w4a16::big::big_kernel<TMV, TNV, WGMV>), dim3(grid), dim3(w4a16::big::kThreads), 0, s, bp); \
+  if (alpha_col)                                                                                                 \
+    hipLaunchKernelGGL((w4a16::big::big_kernel<TMV, TNV, WGMV, true>), dim3(grid), dim3(w4a16::big::kThreads), 0, s, \
+                       bp);                                                                                      \
+  else                                                                                                           \
+    hipLaunchKernelGGL((w4a16::big::big_kernel<TMV, TNV, WGMV, false>), dim3(grid), dim3(w4a16::big::kThreads), 0,   \
+                       s, bp);                                                                                   \
   if (b.rem > 0) {                                                                                               \
     NVFP4_LAUNCH_CHECK();                                                                                        \
     hipLaunchKernelGGL((w4a16::big::big_fixup_kernel<TMV, TNV, WGMV>), dim3(fix_grid), dim3(w4a16::big::kThreads), \

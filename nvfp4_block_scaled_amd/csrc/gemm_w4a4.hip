@@ -249,7 +249,7 @@ __device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff<T
 
 // Epilogue through LDS: each wave writes a 32 x 32T block of alpha * acc to its
 // own LDS region in row-major order, then writes it out as 16-byte row pieces.
-template <bool OUT_BF16, int T>
+template <bool OUT_BF16, int T, bool COLS>
 __device__ __forceinline__ void epilogue(uint8_t *smem, const Params &p, int64_t m0, int64_t n0, int wm, int wn,
                                          float alpha, f32x16_t acc[T][T]) {
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
@@ -265,7 +265,7 @@ __device__ __forceinline__ void epilogue(uint8_t *smem, const Params &p, int64_t
 #pragma unroll
     for (int j = 0; j < T; j++) {
       // the alpha of this lane's column (columns past N are not stored)
-      const float aj = j * 32 + r < ncols ? col_alpha(alpha, p.alpha_col, col0 + j * 32 + r) : alpha;
+      const float aj = COLS && j * 32 + r < ncols ? alpha * p.alpha_col[col0 + j * 32 + r] : alpha;
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int row = 8 * (e >> 2) + 4 * h + (e & 3);
@@ -335,7 +335,9 @@ __device__ __forceinline__ void tile_origin(const Params &p, int tile, int64_t &
 // a lane in use). T = 2: 128 x 128 tiles, two workgroups per CU: for problems
 // with fewer 256 x 256 tiles than CUs, and for the quadrants of the 256 x 256
 // tiles of a last round that would leave at least half the CUs idle.
-template <bool OUT_BF16, int T>
+// COLS: p.alpha_col is set (a separate instantiation, so that the kernel
+// without a per-column scale keeps its registers for the main loop).
+template <bool OUT_BF16, int T, bool COLS>
 __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p) {
   constexpr int BT = 64 * T;                      // workgroup tile edge
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * 32 * 32 * T * 4];
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
       chunk_direct<2, T>(tr, o, c + 2, nch, f, sc, a, b, acc);
     }
     __syncthreads();
-    epilogue<OUT_BF16, T>(smem, p, m0, n0, wm, wn, alpha, acc);
+    epilogue<OUT_BF16, T, COLS>(smem, p, m0, n0, wm, wn, alpha, acc);
   }
 }
 
@@ -429,10 +431,14 @@ nvfp4_status check_gemm_args(const uint8_t *w_prep, int64_t M, int64_t N, int64_
 
 template <int T>
 void launch_tiles(const w4a4::Params &p, int grid, int out_dtype, hipStream_t s) {
-  if (out_dtype == NVFP4_OUT_BF16)
-    hipLaunchKernelGGL((w4a4::gemm_kernel<true, T>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((w4a4::gemm_kernel<false, T>), dim3(grid), dim3(w4a4::kThreads), 0, s, p);
+  const dim3 g(grid), b(w4a4::kThreads);
+  if (out_dtype == NVFP4_OUT_BF16) {
+    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, true>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, false>), g, b, 0, s, p);
+  } else {
+    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, true>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, false>), g, b, 0, s, p);
+  }
 }
 
 // The GEMM kernel proper on A already in the tile layout (arguments checked).
