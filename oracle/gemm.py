@@ -112,3 +112,14 @@ def alpha_product(alpha_host, alpha_dev=None):
     if alpha_dev is None:
         return a
     return np.float32(a * np.float32(alpha_dev))
+
+
+def w4a4_two_pass_exact(a1_codes, a1_scales, a2_codes, a2_scales, b_codes, b_scales, alpha, b_kind="e4m3"):
+    """Two-pass W4A4: D = alpha (A1 + A2) W~^T with A1, A2 the value and residual passes of one
+    activation under one global scale. Written as one contraction over 2K, [A1 | A2] against
+    [W | W], so the exact evaluation and its error bound are w4a4_exact's."""
+    a = np.concatenate([a1_codes, a2_codes], axis=1)
+    sa = np.concatenate([a1_scales, a2_scales], axis=1)
+    b = np.concatenate([b_codes, b_codes], axis=1)
+    sb = np.concatenate([b_scales, b_scales], axis=1)
+    return w4a4_exact(a, sa, b, sb, alpha, "e4m3", b_kind)

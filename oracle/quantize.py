@@ -53,7 +53,13 @@ def quantize_rows_with_g(x_bf16_bits, g):
     """Steps 3-5 for a subset of rows, given the tensor's global scale g (for row-sampled checks)."""
     xb = np.asarray(x_bf16_bits, dtype=np.uint16)
     rows, K = xb.shape
-    x = formats.bf16_bits_to_f32(xb).reshape(rows, K)
+    return quantize_f32_rows_with_g(formats.bf16_bits_to_f32(xb).reshape(rows, K), g)
+
+
+def quantize_f32_rows_with_g(x, g):
+    """Steps 3-5 on FP32 values [rows][K] (the residual pass of the two-pass recipe below)."""
+    x = np.asarray(x, dtype=np.float32)
+    rows, K = x.shape
     f32 = np.float32
     g = f32(g)
     with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
@@ -70,3 +76,34 @@ def quantize_rows_with_g(x_bf16_bits, g):
     codes = (sign << 3) | mag
     codes[s == 0] = 0
     return formats.pack_nibbles(codes.reshape(rows, K)), s_byte.astype(np.uint8)
+
+
+def dequantize_with_g(codes_packed, scale_bytes, g):
+    """The FP32 value each code stands for: fl32(code * scale / g). code * scale is exact in FP32
+    (at most 6 significant bits); the division by the global scale is the one rounding."""
+    v = formats.decode_e2m1(formats.unpack_nibbles(codes_packed)).astype(np.float64)
+    rows, K = v.shape
+    s = formats.decode_e4m3(np.asarray(scale_bytes, dtype=np.uint8)).astype(np.float64)
+    prod = (v.reshape(rows, K // 16, 16) * s[:, :, None]).reshape(rows, K).astype(np.float32)
+    return (prod / np.float32(g)).astype(np.float32)
+
+
+def two_pass_rows_with_g(x_bf16_bits, g):
+    """Two NVFP4 passes over the activations, value then residual (TileLang PR #3290, "Follow-ups":
+    the W4A4 prefill that quantizes activations in two passes). Pass 1 is the quantizer above;
+    the residual r = fl32(x - dequantize(pass 1)) is quantized by the same steps under the same
+    global scale g, so both passes share one alpha. Returns (codes1, scales1, codes2, scales2)."""
+    xb = np.asarray(x_bf16_bits, dtype=np.uint16)
+    rows, K = xb.shape
+    x = formats.bf16_bits_to_f32(xb).reshape(rows, K)
+    c1, s1 = quantize_f32_rows_with_g(x, g)
+    r = (x - dequantize_with_g(c1, s1, g)).astype(np.float32)
+    c2, s2 = quantize_f32_rows_with_g(r, g)
+    return c1, s1, c2, s2
+
+
+def two_pass(x_bf16_bits):
+    """two_pass_rows_with_g over a whole tensor with its global scale: (c1, s1, c2, s2, g, 1/g)."""
+    g = global_scale(x_bf16_bits)
+    c1, s1, c2, s2 = two_pass_rows_with_g(x_bf16_bits, g)
+    return c1, s1, c2, s2, g, np.float32(np.float32(1.0) / g)

@@ -465,3 +465,59 @@ def test_weight_bandwidth_formula():
     for c in fig["cells"]:
         bw = prepared.prepared_bytes(c["N"], c["K"]) / (c["us"] * 1e-6) / 1e12
         assert abs(bw - c["TBps"]) < 0.01
+
+
+# ------------------------------------------------------------------ two-pass prefill
+
+def test_two_pass_on_grid_input_has_zero_residual():
+    """Values on the E2M1 grid with block maximum 6 and tensor maximum 6: g = 448, every block
+    scale is 448 (0x7E), the first pass is exact, so the residual pass is all zero."""
+    r = np.random.default_rng(61)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    x = grid[r.integers(0, 8, (4, 64))] * r.choice([-1.0, 1.0], (4, 64))
+    x[:, ::16] = 6.0
+    c1, s1, c2, s2, g, _ = quantize.two_pass(formats.f32_to_bf16_bits(x.astype(np.float32)))
+    assert g == np.float32(448.0) and np.all(s1 == 0x7E)
+    np.testing.assert_array_equal(quantize.dequantize_with_g(c1, s1, g), x.astype(np.float32))
+    assert not c2.any() and not s2.any()
+
+
+def test_two_pass_reconstruction_bound_and_gain():
+    """|x - deq1 - deq2| is at most the second pass's half grid step: (amax of the block's
+    residual) / 6 times the E4M3 rounding slack, plus the FP32 rounding of the residual; over
+    normal data the two passes cut the RMS error about tenfold."""
+    x = synth.normal_bf16(62, 32, 512)
+    c1, s1, c2, s2, g, _ = quantize.two_pass(x)
+    xf = formats.bf16_bits_to_f32(x).astype(np.float64)
+    d1 = quantize.dequantize_with_g(c1, s1, g).astype(np.float64)
+    d2 = quantize.dequantize_with_g(c2, s2, g).astype(np.float64)
+    res = (xf - d1).reshape(32, 32, 16)
+    amax_r = np.abs(res).max(axis=2, keepdims=True)
+    err = np.abs(xf - d1 - d2).reshape(32, 32, 16)
+    assert np.all(err <= amax_r / 6 * (1 + 2.0 ** -3) + 2.0 ** -23 * np.abs(xf).reshape(32, 32, 16))
+    e1 = np.sqrt(np.mean((xf - d1) ** 2))
+    e2 = np.sqrt(np.mean((xf - d1 - d2) ** 2))
+    assert e2 < e1 / 6
+
+
+def test_dequantize_with_g_hand_values():
+    # code 0x7 (6) and 0x9 (-0.5) under scale 0x38 (1.0) and g = 448: fl32(6 / 448), fl32(-0.5 / 448)
+    d = quantize.dequantize_with_g(np.array([[0x97] + [0] * 7], np.uint8), np.array([[0x38]], np.uint8), 448.0)
+    assert d[0, 0] == np.float32(np.float32(6.0) / np.float32(448.0))
+    assert d[0, 1] == np.float32(np.float32(-0.5) / np.float32(448.0)) and not d[0, 2:].any()
+
+
+def test_two_pass_gemm_is_the_sum_of_both_contractions():
+    """D = alpha (A1 + A2) W~^T: the exact 2K contraction equals, to float64 rounding, the sum of
+    the two float64 products decoded separately (an independent evaluation route)."""
+    x = synth.normal_bf16(63, 24, 256)
+    c1, s1, c2, s2, g, ig = quantize.two_pass(x)
+    r = np.random.default_rng(64)
+    w = formats.pack_nibbles(r.integers(0, 16, (40, 256)))
+    sw = formats.round_e4m3_byte(2.0 ** r.uniform(-3, 3, (40, 16)))
+    D, S = gemm.w4a4_two_pass_exact(c1, s1, c2, s2, w, sw, 0.5)
+    ref = gemm.w4a4_float64(c1, s1, w, sw, 0.5) + gemm.w4a4_float64(c2, s2, w, sw, 0.5)
+    np.testing.assert_allclose(D, ref, rtol=1e-12, atol=1e-300)
+    one, _ = gemm.w4a4_exact(c1, s1, w, sw, 0.5)
+    exact = (formats.bf16_bits_to_f32(x).astype(np.float64) * float(g)) @ gemm.decode_nvfp4(w, sw).T * 0.5
+    assert np.linalg.norm(D - exact) < np.linalg.norm(one - exact) / 6
