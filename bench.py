@@ -229,16 +229,34 @@ def prefill(nv, steps, warmup):
     def step_row_major():
         nv.nvfp4_quantize(xd, codes, scales, g, ig, qws)
         nv.nvfp4_gemm_w4a4(codes, scales, wp, N, K, alpha_w, ig, "bf16", out, gws)
+    # two-pass prefill: value and residual passes under one g, one contraction over 2K
+    a2 = torch.empty(nv.lib().nvfp4_tiled_activation_bytes(M, 2 * K), dtype=torch.uint8, device="cuda")
+
+    def quant2():
+        nv.nvfp4_quantize_two_pass_tiled(xd, a2, g, ig, qws)
+
+    def gemm2():
+        nv.nvfp4_gemm_w4a4_two_pass_tiled(a2, M, wp, N, K, alpha_w, ig, "bf16", out)
+
+    def step2():
+        quant2()
+        gemm2()
     q_ms = time_calls(quant, steps, warmup)
     g_ms = time_calls(gemm, steps, warmup)
     t_ms = time_calls(step, steps, warmup)
     r_ms = time_calls(step_row_major, steps, warmup)
+    q2_ms = time_calls(quant2, steps, warmup)
+    g2_ms = time_calls(gemm2, steps, warmup)
+    t2_ms = time_calls(step2, steps, warmup)
     q_bytes = M * K * 2 + M * K // 2 + M * K // 16
     return dict(M=M, N=N, K=K, quantize_us=round(q_ms * 1e3, 1),
                 quantize_GBps=round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                 gemm_ms=round(g_ms, 4), gemm_TFLOPs=round(2.0 * M * N * K / (g_ms * 1e-3) / 1e12, 1),
                 total_ms=round(t_ms, 4), total_TFLOPs=round(2.0 * M * N * K / (t_ms * 1e-3) / 1e12, 1),
-                row_major_path_ms=round(r_ms, 4))
+                row_major_path_ms=round(r_ms, 4),
+                two_pass=dict(quantize_us=round(q2_ms * 1e3, 1), gemm_ms=round(g2_ms, 4),
+                              gemm_TFLOPs_2K=round(4.0 * M * N * K / (g2_ms * 1e-3) / 1e12, 1),
+                              total_ms=round(t2_ms, 4)))
 
 
 def cpu_baseline(S=8192, rows=2048, cols=8192):

@@ -143,6 +143,17 @@ nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep
                                    float alpha, const float *alpha_dev, const float *alpha_col, void *d,
                                    int out_dtype, int64_t ldd, void *stream);
 
+/* Two-pass W4A4 GEMM: D = alpha_eff * (A1 + A2)(W.SFW)^T, A1 and A2 the two
+ * passes of nvfp4_quantize_two_pass_tiled (a2_tiled, rows M, K columns per
+ * pass) against a prepared weight of shape (N, K): one contraction over 2K in
+ * which the residual half reads the same W chunks as the value half (TileLang
+ * PR #3290, "Follow-ups"). alpha_eff as for nvfp4_gemm_w4a4 (the passes share
+ * g, so alpha is the one-pass prefill's 1/(gA gW)); other arguments as for
+ * nvfp4_gemm_w4a4_tiled. Needs no workspace. */
+nvfp4_status nvfp4_gemm_w4a4_two_pass_tiled(const uint8_t *a2_tiled, const uint8_t *w_prep, int64_t M, int64_t N,
+                                            int64_t K, float alpha, const float *alpha_dev, const float *alpha_col,
+                                            void *d, int out_dtype, int64_t ldd, void *stream);
+
 /* W4A16 GEMM: y = alpha_eff * x (W.SFW)^T, x and y BF16, FP32 accumulation
  * (TileLang PR #3290, "Summary": BF16 activations against NVFP4 weights with
  * E4M3 block scales, for M = 1 .. 1024 rows). alpha, alpha_dev and alpha_col
@@ -181,6 +192,21 @@ nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8_t 
  * K % 64 == 0; other arguments as for nvfp4_quantize. */
 nvfp4_status nvfp4_quantize_tiled(const uint16_t *x, int64_t rows, int64_t K, uint8_t *a_tiled, float *g_dev,
                                   float *inv_g_dev, void *ws, size_t ws_bytes, void *stream);
+
+/* Two-pass activation quantization (TileLang PR #3290, "Follow-ups": the W4A4
+ * prefill whose activations are quantized in two NVFP4 passes, value then
+ * residual; the pages give no recipe beyond that, this library uses): pass 1
+ * is nvfp4_quantize's recipe with the tensor's global scale g; the residual
+ * r = x - fl32(code * scale / g) (code * scale exact, then one division and
+ * one subtraction in IEEE FP32) is quantized by the same steps (block maximum
+ * of |r|, scale, codes) under the same g, so both passes share one alpha.
+ *  a2_tiled  nvfp4_tiled_activation_bytes(rows, 2 K) bytes, 16-byte aligned:
+ *            the tile layout of a [rows][2K] activation whose K chunks
+ *            0 .. K/64 - 1 hold pass 1 and K/64 .. K/32 - 1 pass 2.
+ * Other arguments as for nvfp4_quantize_tiled (K % 64 == 0). */
+nvfp4_status nvfp4_quantize_two_pass_tiled(const uint16_t *x, int64_t rows, int64_t K, uint8_t *a2_tiled,
+                                           float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes,
+                                           void *stream);
 
 #ifdef __cplusplus
 }

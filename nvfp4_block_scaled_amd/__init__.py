@@ -45,6 +45,9 @@ _SIGS = [
      [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _I64, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize_tiled", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("nvfp4_quantize_two_pass_tiled", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("nvfp4_gemm_w4a4_two_pass_tiled", ctypes.c_int,
+     [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _P]),
 ]
 EXPORTED = [s[0] for s in _SIGS]
 
@@ -306,3 +309,51 @@ def nvfp4_quantize_tiled(x, out=None, g=None, inv_g=None, ws=None):
     _check(lib().nvfp4_quantize_tiled(_ptr(x), rows, K, _ptr(out), _ptr(g), _ptr(inv_g), _ptr(ws), ws.numel(),
                                       _stream()))
     return out, g, inv_g
+
+
+def nvfp4_quantize_two_pass_tiled(x, out=None, g=None, inv_g=None, ws=None):
+    """BF16 [rows][K] -> (two-pass activation in the tile layout of [rows][2K] (uint8), g, inv_g)."""
+    x = _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    rows, K = x.shape
+    dev = x.device
+    n = int(lib().nvfp4_tiled_activation_bytes(rows, 2 * K))
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=dev)
+    elif out.dtype != torch.uint8 or out.numel() < n:
+        raise ValueError("out must hold nvfp4_tiled_activation_bytes(rows, 2K) uint8")
+    if g is None:
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    if inv_g is None:
+        inv_g = torch.empty(1, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(OP_QUANTIZE, rows, 0, K), dtype=torch.uint8, device=dev)
+    _check(lib().nvfp4_quantize_two_pass_tiled(_ptr(x), rows, K, _ptr(out), _ptr(g), _ptr(inv_g), _ptr(ws),
+                                               ws.numel(), _stream()))
+    return out, g, inv_g
+
+
+def nvfp4_gemm_w4a4_two_pass_tiled(a2_tiled, M, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None,
+                                   alpha_col=None):
+    """D = alpha (A1 + A2) W^T on a two-pass activation (nvfp4_quantize_two_pass_tiled, K per pass)."""
+    a2_tiled = _u8(a2_tiled, "a2_tiled")
+    w_prep = _u8(w_prep, "w_prep")
+    if a2_tiled.numel() < int(lib().nvfp4_tiled_activation_bytes(M, 2 * K)):
+        raise ValueError("a2_tiled is smaller than nvfp4_tiled_activation_bytes(M, 2K)")
+    if w_prep.numel() != prepared_weight_bytes(N, K):
+        raise ValueError("w_prep does not match (N, K)")
+    od = {"bf16": (OUT_BF16, torch.bfloat16), "f32": (OUT_F32, torch.float32)}.get(out_dtype)
+    if od is None:
+        raise TypeError("out_dtype must be 'bf16' or 'f32'")
+    if out is None:
+        out = torch.empty((M, N), dtype=od[1], device=a2_tiled.device)
+    elif out.dtype != od[1] or out.dim() != 2 or out.shape[0] != M or out.stride(1) != 1:
+        raise ValueError("out must be [M][>=N] rows of out_dtype")
+    if alpha_dev is not None and (alpha_dev.dtype != torch.float32 or not alpha_dev.is_cuda):
+        raise TypeError("alpha_dev must be a float32 device tensor")
+    alpha_col = _check_alpha_col(alpha_col, N)
+    _check(lib().nvfp4_gemm_w4a4_two_pass_tiled(_ptr(a2_tiled), _ptr(w_prep), M, N, K, float(alpha),
+                                                _ptr(alpha_dev), _ptr(alpha_col), _ptr(out), od[0], out.stride(0),
+                                                _stream()))
+    return out

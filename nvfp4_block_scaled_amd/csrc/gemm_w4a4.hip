@@ -164,24 +164,34 @@ struct WaveOff {
 
 // Loads of chunk c: the rebased resources keep the range check on the row (A)
 // or 32-row group (W); chunks at or past nch read as zeros (length 0).
-template <int T>
+// W's chunk for chunk c of the contraction: with TWO (the two-pass activation:
+// value chunks 0 .. ktw - 1, then residual chunks ktw .. 2 ktw - 1) both halves
+// read the same W chunks.
+template <bool TWO>
+__device__ __forceinline__ int64_t w_chunk(int64_t c, int64_t ktw) {
+  return TWO && c >= ktw ? c - ktw : c;
+}
+
+template <int T, bool TWO>
 __device__ __forceinline__ void load_frags(const TileRsrc &tr, const WaveOff<T> &o, int64_t c, int64_t nch,
-                                           ChunkFrags<T> &f) {
+                                           int64_t ktw, ChunkFrags<T> &f) {
   const bool in = c < nch;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(tr.a, in ? tr.a_bytes : 0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(tr.w, in ? tr.w_bytes : 0);
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(tr.as, in ? tr.as_bytes : 0);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(tr.ws, in ? tr.ws_bytes : 0);
   const int sw = (int)(c * 1024), ssw = (int)(c * 128);   // chunk c: next code tile, next scale tile
+  const int64_t cw = w_chunk<TWO>(c, ktw);
+  const int wsw = (int)(cw * 1024), wssw = (int)(cw * 128);
 #pragma unroll
   for (int i = 0; i < T; i++) {
     f.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, o.a[i], sw, 0);
-    f.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, o.w[i], sw, 0);
+    f.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, o.w[i], wsw, 0);
   }
 #pragma unroll
   for (int i = 0; i < T; i++) {
     f.as[i] = __builtin_amdgcn_raw_buffer_load_b32(ras, o.as[i], ssw, 0);
-    f.ws[i] = __builtin_amdgcn_raw_buffer_load_b32(rws, o.ws[i], ssw, 0);
+    f.ws[i] = __builtin_amdgcn_raw_buffer_load_b32(rws, o.ws[i], wssw, 0);
   }
 }
 
@@ -196,14 +206,16 @@ __device__ __forceinline__ void load_frags(const TileRsrc &tr, const WaveOff<T> 
 // which stalls each for the previous one's full latency (measured 42 against
 // 36 cycles per MFMA at T = 4). The chunk's sixteen loads are spread over the
 // four steps (35.0 against 36.3 cycles per MFMA with all of them in step 0).
-template <int P, int T>
+template <int P, int T, bool TWO>
 __device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff<T> &o, int64_t c, int64_t nch,
-                                             ChunkFrags<T> f[3], ChunkScales &sc, half8_t a[T], half8_t b[T],
+                                             int64_t ktw, ChunkFrags<T> f[3], ChunkScales &sc, half8_t a[T], half8_t b[T],
                                              f32x16_t acc[T][T]) {
   constexpr int kValuPerMfma = 16 / T + (T == 4 ? 1 : 0);
   // chunk c + 2's loads, one kind per step: A codes, W codes, A scales, W scales
   const bool in2 = c + 2 < nch;
   const int sw2 = (int)((c + 2) * 1024), ssw2 = (int)((c + 2) * 128);
+  const int64_t cw2 = w_chunk<TWO>(c + 2, ktw);
+  const int wsw2 = (int)(cw2 * 1024), wssw2 = (int)(cw2 * 128);
   ChunkFrags<T> &f2 = f[(P + 2) % 3];
 #pragma unroll
   for (int s = 0; s < 4; s++) {
@@ -214,7 +226,7 @@ __device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff<T
     } else if (s == 1) {
       const __amdgpu_buffer_rsrc_t rw = make_rsrc(tr.w, in2 ? tr.w_bytes : 0);
 #pragma unroll
-      for (int i = 0; i < T; i++) f2.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, o.w[i], sw2, 0);
+      for (int i = 0; i < T; i++) f2.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, o.w[i], wsw2, 0);
     } else if (s == 2) {
       const __amdgpu_buffer_rsrc_t ras = make_rsrc(tr.as, in2 ? tr.as_bytes : 0);
 #pragma unroll
@@ -222,7 +234,7 @@ __device__ __forceinline__ void chunk_direct(const TileRsrc &tr, const WaveOff<T
     } else {
       const __amdgpu_buffer_rsrc_t rws = make_rsrc(tr.ws, in2 ? tr.ws_bytes : 0);
 #pragma unroll
-      for (int i = 0; i < T; i++) f2.ws[i] = __builtin_amdgcn_raw_buffer_load_b32(rws, o.ws[i], ssw2, 0);
+      for (int i = 0; i < T; i++) f2.ws[i] = __builtin_amdgcn_raw_buffer_load_b32(rws, o.ws[i], wssw2, 0);
     }
     half8_t an[T], bn[T];
     if (s < 3) {
@@ -337,7 +349,10 @@ __device__ __forceinline__ void tile_origin(const Params &p, int tile, int64_t &
 // tiles of a last round that would leave at least half the CUs idle.
 // COLS: p.alpha_col is set (a separate instantiation, so that the kernel
 // without a per-column scale keeps its registers for the main loop).
-template <bool OUT_BF16, int T, bool COLS>
+// TWO: A is a two-pass activation of 2K columns (value, then residual, in the
+// tile layout) against W of K columns: the contraction runs over 2K, and chunk
+// c >= K/64 uses W's chunk c - K/64.
+template <bool OUT_BF16, int T, bool COLS, bool TWO>
 __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p) {
   constexpr int BT = 64 * T;                      // workgroup tile edge
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * 32 * 32 * T * 4];
@@ -350,8 +365,9 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
   int pid = blockIdx.x;
   if ((G & 7) == 0) pid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const float alpha = load_alpha(p.alpha, p.alpha_dev);
-  const int64_t nch = p.K / 64;
-  const int64_t kt = p.K / 64;
+  const int64_t ktw = p.K / 64;                   // W's chunks
+  const int64_t kt = TWO ? 2 * ktw : ktw;         // A's chunks, the contraction's length
+  const int64_t nch = kt;
 
   const int lane = t & 63, r = lane & 31;
   WaveOff<T> o;
@@ -359,8 +375,8 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
   for (int i = 0; i < T; i++) {
     o.a[i] = (uint32_t)(((wm * T + i) * kt) * 1024 + lane * 16);
     o.as[i] = (uint32_t)(((wm * T + i) * kt) * 128 + r * 4);
-    o.w[i] = (uint32_t)(((wn * T + i) * kt) * 1024 + lane * 16);
-    o.ws[i] = (uint32_t)(((wn * T + i) * kt) * 128 + r * 4);
+    o.w[i] = (uint32_t)(((wn * T + i) * ktw) * 1024 + lane * 16);
+    o.ws[i] = (uint32_t)(((wn * T + i) * ktw) * 128 + r * 4);
   }
 
   for (int tile = pid; tile < p.count; tile += G) {
@@ -371,12 +387,12 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
     const int64_t Mp = padded_rows(p.M);
     tr.a = p.a_tiled + (m0 >> 5) * kt * 1024;
     tr.a_bytes = (Mp - m0) / 32 * kt * 1024;
-    tr.as = p.a_tiled + Mp * p.K / 2 + (m0 >> 5) * kt * 128;
+    tr.as = p.a_tiled + (TWO ? Mp * kt * 32 : Mp * p.K / 2) + (m0 >> 5) * kt * 128;
     tr.as_bytes = (Mp - m0) / 32 * kt * 128;
-    tr.w = p.w_prep + (n0 >> 5) * kt * 1024;
-    tr.w_bytes = (p.N - n0) / 32 * kt * 1024;
-    tr.ws = p.w_prep + p.N * p.K / 2 + (n0 >> 5) * kt * 128;
-    tr.ws_bytes = (p.N - n0) / 32 * kt * 128;
+    tr.w = p.w_prep + (n0 >> 5) * ktw * 1024;
+    tr.w_bytes = (p.N - n0) / 32 * ktw * 1024;
+    tr.ws = p.w_prep + p.N * p.K / 2 + (n0 >> 5) * ktw * 128;
+    tr.ws_bytes = (p.N - n0) / 32 * ktw * 128;
 
     f32x16_t acc[T][T];
 #pragma unroll
@@ -386,14 +402,14 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
     ChunkFrags<T> f[3];
     ChunkScales sc;
     half8_t a[T], b[T];
-    load_frags<T>(tr, o, 0, nch, f[0]);
-    load_frags<T>(tr, o, 1, nch, f[1]);
+    load_frags<T, TWO>(tr, o, 0, nch, ktw, f[0]);
+    load_frags<T, TWO>(tr, o, 1, nch, ktw, f[1]);
     convert_scales<T>(f[0], sc);
     unpack_step<T>(f[0], sc, 0, a, b);
     for (int64_t c = 0; c < nch; c += 3) {
-      chunk_direct<0, T>(tr, o, c, nch, f, sc, a, b, acc);
-      chunk_direct<1, T>(tr, o, c + 1, nch, f, sc, a, b, acc);
-      chunk_direct<2, T>(tr, o, c + 2, nch, f, sc, a, b, acc);
+      chunk_direct<0, T, TWO>(tr, o, c, nch, ktw, f, sc, a, b, acc);
+      chunk_direct<1, T, TWO>(tr, o, c + 1, nch, ktw, f, sc, a, b, acc);
+      chunk_direct<2, T, TWO>(tr, o, c + 2, nch, ktw, f, sc, a, b, acc);
     }
     __syncthreads();
     epilogue<OUT_BF16, T, COLS>(smem, p, m0, n0, wm, wn, alpha, acc);
@@ -429,16 +445,22 @@ nvfp4_status check_gemm_args(const uint8_t *w_prep, int64_t M, int64_t N, int64_
   return NVFP4_OK;
 }
 
-template <int T>
+template <int T, bool TWO>
 void launch_tiles(const w4a4::Params &p, int grid, int out_dtype, hipStream_t s) {
   const dim3 g(grid), b(w4a4::kThreads);
   if (out_dtype == NVFP4_OUT_BF16) {
-    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, true>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, false>), g, b, 0, s, p);
+    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, true, TWO>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, false, TWO>), g, b, 0, s, p);
   } else {
-    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, true>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, false>), g, b, 0, s, p);
+    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, true, TWO>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, false, TWO>), g, b, 0, s, p);
   }
+}
+
+template <int T>
+void launch_tiles(const w4a4::Params &p, int grid, int out_dtype, bool two, hipStream_t s) {
+  if (two) launch_tiles<T, true>(p, grid, out_dtype, s);
+  else launch_tiles<T, false>(p, grid, out_dtype, s);
 }
 
 // The GEMM kernel proper on A already in the tile layout (arguments checked).
@@ -451,7 +473,8 @@ void launch_tiles(const w4a4::Params &p, int grid, int out_dtype, hipStream_t s)
 //    same bits as with T = 4 alone.
 //  * Fewer: the T = 2 kernel on 128 x 128 tiles.
 nvfp4_status launch_gemm(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N, int64_t K, float alpha,
-                         const float *alpha_dev, const float *alpha_col, void *d, int out_dtype, int64_t ldd, hipStream_t s) {
+                         const float *alpha_dev, const float *alpha_col, void *d, int out_dtype, int64_t ldd, bool two,
+                         hipStream_t s) {
   DeviceInfo di;
   nvfp4_status st = device_info(&di);
   if (st != NVFP4_OK) return st;
@@ -461,20 +484,20 @@ nvfp4_status launch_gemm(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t 
     const int64_t rem = t4 % cus;
     const int64_t full = rem > 0 && 2 * rem <= cus ? t4 - rem : t4;
     w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, alpha_col, (int)tm4, (int)tn4, (int)full, 0, 0};
-    launch_tiles<4>(p, (int)cus, out_dtype, s);
+    launch_tiles<4>(p, (int)cus, out_dtype, two, s);
     NVFP4_LAUNCH_CHECK();
     if (full < t4) {
       p.count = (int)(4 * (t4 - full));   // <= 2 * cus: one workgroup per quadrant
       p.first = (int)full;
       p.quad = 1;
-      launch_tiles<2>(p, p.count, out_dtype, s);
+      launch_tiles<2>(p, p.count, out_dtype, two, s);
       NVFP4_LAUNCH_CHECK();
     }
     return NVFP4_OK;
   }
   const int64_t tm2 = (M + 127) / 128, tn2 = (N + 127) / 128, t2 = tm2 * tn2;
   w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, alpha_col, (int)tm2, (int)tn2, (int)t2, 0, 0};
-  launch_tiles<2>(p, (int)(t2 < 2 * cus ? t2 : 2 * cus), out_dtype, s);
+  launch_tiles<2>(p, (int)(t2 < 2 * cus ? t2 : 2 * cus), out_dtype, two, s);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }
@@ -513,7 +536,22 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint
   if (st != NVFP4_OK || M == 0) return st;
   if (!a_tiled) return NVFP4_ERR_NULL;
   if (!aligned(a_tiled, 16)) return NVFP4_ERR_ALIGN;
-  return launch_gemm(a_tiled, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, (hipStream_t)stream);
+  return launch_gemm(a_tiled, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, false,
+                     (hipStream_t)stream);
+}
+
+extern "C" nvfp4_status nvfp4_gemm_w4a4_two_pass_tiled(const uint8_t *a2_tiled, const uint8_t *w_prep, int64_t M,
+                                                       int64_t N, int64_t K, float alpha, const float *alpha_dev,
+                                                       const float *alpha_col, void *d, int out_dtype, int64_t ldd,
+                                                       void *stream) {
+  nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd);
+  if (st != NVFP4_OK || M == 0) return st;
+  if (!a2_tiled) return NVFP4_ERR_NULL;
+  if (!aligned(a2_tiled, 16)) return NVFP4_ERR_ALIGN;
+  // 32-bit buffer offsets inside one 256-row tile of the 2K-column activation
+  if ((int64_t)8 * (2 * K / 64) * 1024 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
+  return launch_gemm(a2_tiled, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, true,
+                     (hipStream_t)stream);
 }
 
 extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
@@ -534,5 +572,5 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a
   uint8_t *at = static_cast<uint8_t *>(ws);
   launch_tile_a(a_codes, a_scales, M, K, at, s);
   NVFP4_LAUNCH_CHECK();
-  return launch_gemm(at, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, s);
+  return launch_gemm(at, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, false, s);
 }

@@ -116,6 +116,49 @@ __device__ __forceinline__ u32x2_t quantize_block(const u32x4_t v0, const u32x4_
   return out;
 }
 
+// quantize_block on sixteen FP32 values (the residual pass of the two-pass
+// recipe): the same steps, with |v| maxima taken on floats (exact).
+__device__ __forceinline__ u32x2_t quantize_block_f32(const float (&v)[16], float g, uint32_t *sbyte) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t sb = 0;
+  if (amax != 0.0f) {
+    const float t = amax / 6.0f;
+    const float u = t * g;
+    sb = e4m3_rne_sat(u);
+  }
+  *sbyte = sb;
+  u32x2_t out = {0u, 0u};
+  if (sb != 0) {
+    const float r = g / e4m3_value(sb);
+#define NVFP4_CVT_F32(D, B) \
+  out[D] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[D], v[8 * D + 2 * B] * r, v[8 * D + 2 * B + 1] * r, 1.0f, B)
+    NVFP4_CVT_F32(0, 0); NVFP4_CVT_F32(0, 1); NVFP4_CVT_F32(0, 2); NVFP4_CVT_F32(0, 3);
+    NVFP4_CVT_F32(1, 0); NVFP4_CVT_F32(1, 1); NVFP4_CVT_F32(1, 2); NVFP4_CVT_F32(1, 3);
+#undef NVFP4_CVT_F32
+  }
+  return out;
+}
+
+// The residual of a quantized block: r_i = x_i - fl32(code_i * scale / g) for
+// the block's sixteen BF16 inputs (two 16-byte chunks), its codes and scale byte.
+// code * scale is exact in FP32; the division and the subtraction round once each.
+__device__ __forceinline__ void block_residual(const u32x4_t v0, const u32x4_t v1, u32x2_t codes, uint32_t sbyte,
+                                               float g, float (&res)[16]) {
+  const float s = sbyte ? e4m3_value(sbyte) : 0.0f;
+  // byte B of code word D: elements 8 D + 2 B (low nibble) and 8 D + 2 B + 1, from word B of chunk D
+#define NVFP4_RES(D, V, B)                                                                \
+  {                                                                                       \
+    const f32x2_t q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[D], 1.0f, B);        \
+    res[8 * D + 2 * B] = __uint_as_float(V[B] << 16) - (q[0] * s) / g;                    \
+    res[8 * D + 2 * B + 1] = __uint_as_float(V[B] & 0xFFFF0000u) - (q[1] * s) / g;        \
+  }
+  NVFP4_RES(0, v0, 0) NVFP4_RES(0, v0, 1) NVFP4_RES(0, v0, 2) NVFP4_RES(0, v0, 3)
+  NVFP4_RES(1, v1, 0) NVFP4_RES(1, v1, 1) NVFP4_RES(1, v1, 2) NVFP4_RES(1, v1, 3)
+#undef NVFP4_RES
+}
+
 // Every workgroup of pass 2 first reduces the pass-1 maxima (a few KB) to the
 // tensor maximum and forms g (block 0 stores g and 1/g).
 __device__ __forceinline__ float global_scale(const uint32_t *__restrict__ partial, int npartial, uint32_t *red,
@@ -183,16 +226,56 @@ __global__ __launch_bounds__(kThreads) void quantize_tiled_kernel(const u32x4_t 
   }
 }
 
+// Two-pass tile-layout output: the value pass into the K chunks [0, kt) of an
+// activation of 2K columns and the residual pass, under the same g, into
+// chunks [kt, 2 kt) of the same rows. Otherwise as quantize_tiled_kernel (one
+// wave per 32 x 64 tile of x, lane 32 h + r on blocks 2h, 2h + 1 of row r).
+__global__ __launch_bounds__(kThreads) void quantize_two_pass_tiled_kernel(
+    const u32x4_t *__restrict__ x, int64_t rows, int64_t K, int64_t ntiles, const uint32_t *__restrict__ partial,
+    int npartial, uint8_t *__restrict__ out, float *__restrict__ g_out, float *__restrict__ inv_g_out) {
+  __shared__ uint32_t red[kThreads / 64 + 1];
+  const float g = global_scale(partial, npartial, red, g_out, inv_g_out);
+  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+  const int64_t kt = K / 64, x_row = K / 8;
+  u32x4_t *const code_out = reinterpret_cast<u32x4_t *>(out);
+  uint16_t *const scale_out = reinterpret_cast<uint16_t *>(out + 2 * ntiles * 1024);   // 2 ntiles tiles of codes
+  const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t tile = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile < ntiles; tile += wstride) {
+    const int64_t rg = tile / kt, kk = tile - rg * kt;
+    const int64_t row = rg * 32 + r;
+    u32x4_t v[4] = {};
+    if (row < rows) {
+      const u32x4_t *src = x + row * x_row + kk * 8 + h * 4;
+#pragma unroll
+      for (int i = 0; i < 4; i++) v[i] = src[i];
+    }
+    const int64_t t1 = rg * 2 * kt + kk, t2 = t1 + kt;       // value and residual tiles of the 2K layout
+    uint32_t s0, s1;
+    const u32x2_t c0 = quantize_block(v[0], v[1], g, &s0);
+    const u32x2_t c1 = quantize_block(v[2], v[3], g, &s1);
+    code_out[t1 * 64 + lane] = u32x4_t{c0[0], c0[1], c1[0], c1[1]};
+    scale_out[t1 * 64 + 2 * r + h] = (uint16_t)(s0 | (s1 << 8));
+    float res[16];
+    block_residual(v[0], v[1], c0, s0, g, res);
+    const u32x2_t e0 = quantize_block_f32(res, g, &s0);
+    block_residual(v[2], v[3], c1, s1, g, res);
+    const u32x2_t e1 = quantize_block_f32(res, g, &s1);
+    code_out[t2 * 64 + lane] = u32x4_t{e0[0], e0[1], e1[0], e1[1]};
+    scale_out[t2 * 64 + 2 * r + h] = (uint16_t)(s0 | (s1 << 8));
+  }
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
 
 namespace {
 
-nvfp4_status quantize_common(const uint16_t *x, int64_t rows, int64_t K, bool tiled, void *codes, uint8_t *scales,
+nvfp4_status quantize_common(const uint16_t *x, int64_t rows, int64_t K, int mode, void *codes, uint8_t *scales,
                              float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes, hipStream_t s) {
   if (!ws) return NVFP4_ERR_WORKSPACE;
   if (ws_bytes < quantize_workspace_bytes(rows, K)) return NVFP4_ERR_WORKSPACE;
+  const bool tiled = mode != 0;
   if (!aligned(x, 16) || !aligned(codes, tiled ? 16 : 8) || !aligned(ws, 4) || !aligned(g_dev, 4) ||
       (inv_g_dev && !aligned(inv_g_dev, 4)))
     return NVFP4_ERR_ALIGN;
@@ -209,8 +292,13 @@ nvfp4_status quantize_common(const uint16_t *x, int64_t rows, int64_t K, bool ti
   if (tiled) {
     const int64_t ntiles = (rows + 31) / 32 * (K / 64);
     const int64_t grid = std::max<int64_t>(1, std::min(max_grid, (ntiles + kThreads / 64 - 1) / (kThreads / 64)));
-    hipLaunchKernelGGL(quantize_tiled_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x, rows, K,
-                       ntiles, (const uint32_t *)ws, kAmaxBlocks, (uint8_t *)codes, g_dev, inv_g_dev);
+    if (mode == 2)
+      hipLaunchKernelGGL(quantize_two_pass_tiled_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                         (const u32x4_t *)x, rows, K, ntiles, (const uint32_t *)ws, kAmaxBlocks, (uint8_t *)codes,
+                         g_dev, inv_g_dev);
+    else
+      hipLaunchKernelGGL(quantize_tiled_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x, rows,
+                         K, ntiles, (const uint32_t *)ws, kAmaxBlocks, (uint8_t *)codes, g_dev, inv_g_dev);
   } else {
     const int64_t grid = std::max<int64_t>(1, std::min(max_grid, (nblocks + kThreads - 1) / kThreads));
     hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, (const u32x4_t *)x, nblocks,
@@ -227,7 +315,7 @@ extern "C" nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t 
   if (!g_dev) return NVFP4_ERR_NULL;
   if (rows < 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && (!x || !codes || !scales)) return NVFP4_ERR_NULL;
-  return quantize_common(x, rows, K, false, codes, scales, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
+  return quantize_common(x, rows, K, 0, codes, scales, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
 }
 
 extern "C" nvfp4_status nvfp4_quantize_tiled(const uint16_t *x, int64_t rows, int64_t K, uint8_t *a_tiled,
@@ -236,5 +324,14 @@ extern "C" nvfp4_status nvfp4_quantize_tiled(const uint16_t *x, int64_t rows, in
   if (!g_dev) return NVFP4_ERR_NULL;
   if (rows < 0 || K <= 0 || K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && (!x || !a_tiled)) return NVFP4_ERR_NULL;
-  return quantize_common(x, rows, K, true, a_tiled, nullptr, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
+  return quantize_common(x, rows, K, 1, a_tiled, nullptr, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" nvfp4_status nvfp4_quantize_two_pass_tiled(const uint16_t *x, int64_t rows, int64_t K, uint8_t *a2_tiled,
+                                                      float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes,
+                                                      void *stream) {
+  if (!g_dev) return NVFP4_ERR_NULL;
+  if (rows < 0 || K <= 0 || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && (!x || !a2_tiled)) return NVFP4_ERR_NULL;
+  return quantize_common(x, rows, K, 2, a2_tiled, nullptr, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
 }

@@ -113,6 +113,26 @@ def test_quantize_tiled_argument_checks():
     assert q(FAKE, 64, 128, ODD, FAKE, None, FAKE, 4096, None) == nv.ERR_ALIGN
 
 
+def test_two_pass_argument_checks():
+    L = nv.lib()
+    q = L.nvfp4_quantize_two_pass_tiled
+    assert q(FAKE, 64, 128, FAKE, None, None, FAKE, 4096, None) == nv.ERR_NULL      # g_dev
+    assert q(FAKE, 64, 96, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_SHAPE      # K % 64
+    assert q(FAKE, 64, 128, FAKE, FAKE, None, None, 0, None) == nv.ERR_WORKSPACE
+    assert q(FAKE, 64, 128, ODD, FAKE, None, FAKE, 4096, None) == nv.ERR_ALIGN
+    g = L.nvfp4_gemm_w4a4_two_pass_tiled
+
+    def call(at=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ac=None, d=FAKE, dt=nv.OUT_BF16, ldd=64):
+        return g(at, w, M, N, K, alpha, None, ac, d, dt, ldd, None)
+    assert call(dt=3) == nv.ERR_DTYPE
+    assert call(K=96) == nv.ERR_SHAPE
+    assert call(M=0) == nv.OK
+    assert call(at=None) == nv.ERR_NULL
+    assert call(alpha=float("nan")) == nv.ERR_VALUE
+    assert call(at=ODD) == nv.ERR_ALIGN
+    assert call(ac=ODD) == nv.ERR_ALIGN
+
+
 def test_gemm_w4a16_argument_checks():
     f = nv.lib().nvfp4_gemm_w4a16
 

@@ -597,3 +597,66 @@ def test_prefill_quantize_then_w4a4_full():
     alpha_eff = gemm.alpha_product(alpha_w, np.float32(np.float32(1.0) / gA))
     D, S = oracle_w4a4_exact_blocked(a_ref, sa_ref, w_ref, sw_ref, alpha_eff)
     assert_close(host(out), D, S, bf16=True, what="prefill full")
+
+
+# ------------------------------------------------------------------ two-pass prefill
+
+def _two_pass_layout_ref(x_bits):
+    """The oracle's two passes, laid out as the [rows][2K] tile-layout activation."""
+    c1, s1, c2, s2, g, ig = quantize.two_pass(x_bits)
+    rows = x_bits.shape[0]
+    Mp = -(-rows // 32) * 32
+    cp = np.zeros((Mp, c1.shape[1] * 2), np.uint8)
+    sp = np.zeros((Mp, s1.shape[1] * 2), np.uint8)
+    cp[:rows], sp[:rows] = np.concatenate([c1, c2], axis=1), np.concatenate([s1, s2], axis=1)
+    ref, _ = prepared.prepare_weight(cp, sp, "ue4m3")
+    return ref, (c1, s1, c2, s2), g, ig
+
+
+@pytest.mark.parametrize("rows,K", [(1, 64), (77, 320), (256, 5120)])
+def test_quantize_two_pass_tiled_bit_exact(rows, K):
+    """Value and residual passes under one g (the two-pass prefill of TileLang PR #3290,
+    "Follow-ups"), every byte of the 2K-column tile layout against the oracle."""
+    x = synth.normal_bf16(rows * 5 + K, rows, K)
+    a2, g, ig = nv.nvfp4_quantize_two_pass_tiled(dev(x).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    ref, (_, _, c2, _), g_ref, ig_ref = _two_pass_layout_ref(x)
+    assert np.float32(g.item()) == g_ref and np.float32(ig.item()) == ig_ref
+    assert c2.any(), "the residual pass is not empty on normal data"
+    np.testing.assert_array_equal(host(a2), ref)
+
+
+def test_quantize_two_pass_edge_values():
+    """Blocks on the E2M1 grid (zero residual), an all-zero block, signed zeros and tiny values."""
+    vals = np.zeros((2, 64), np.float32)
+    vals[0, :16] = [6, 4, 3, 2, 1.5, 1, .5, 0, -6, -4, -3, -2, -1.5, -1, -.5, -0.0]
+    vals[0, 32:48] = np.linspace(-1e-3, 1e-3, 16)
+    vals[1, :] = np.linspace(-5.9, 5.7, 64)
+    vals[1, 5] = -0.0
+    x = formats.f32_to_bf16_bits(vals)
+    a2, g, _ = nv.nvfp4_quantize_two_pass_tiled(dev(x).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    ref, _, g_ref, _ = _two_pass_layout_ref(x)
+    assert np.float32(g.item()) == g_ref
+    np.testing.assert_array_equal(host(a2), ref)
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype", [(300, 320, 192, "f32"), (4000, 4192, 256, "bf16"),
+                                             (8192, 17408, 5120, "bf16")])
+def test_w4a4_two_pass_gemm(M, N, K, out_dtype):
+    """D = alpha (A1 + A2) W^T from x through the two-pass quantizer and the two-pass GEMM,
+    alpha = 1/(gA gW) as for the one-pass prefill, against the oracle's 2K contraction on its
+    own quantization of x: 128 x 128 tiles, 256 x 256 tiles with ragged edges and the last
+    round as quadrants, and the prefill layer shape (every output checked)."""
+    x = synth.normal_bf16(M + N + K, M, K)
+    b, sb = _random_nvfp4(N + 9, N, K, -3, 3)
+    wp, _ = _prep(b, sb)
+    a2, g, ig = nv.nvfp4_quantize_two_pass_tiled(dev(x).view(torch.bfloat16))
+    out = nv.nvfp4_gemm_w4a4_two_pass_tiled(a2, M, wp, N, K, 0.25, ig, out_dtype)
+    torch.cuda.synchronize()
+    c1, s1, c2, s2, g_ref, ig_ref = quantize.two_pass(x)
+    assert np.float32(ig.item()) == ig_ref
+    alpha = gemm.alpha_product(0.25, ig_ref)
+    D, S = oracle_w4a4_exact_blocked(np.concatenate([c1, c2], 1), np.concatenate([s1, s2], 1),
+                                     np.concatenate([b, b], 1), np.concatenate([sb, sb], 1), alpha)
+    assert_close(host(out), D, S, bf16=out_dtype == "bf16", what=f"two-pass {M}x{N}x{K}")
