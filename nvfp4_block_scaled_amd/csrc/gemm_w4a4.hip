@@ -32,8 +32,13 @@
 //    mod 8) take consecutive tile indices, and consecutive indices cover a
 //    kGroupM-tall band of tiles column by column, so a wave of tiles on one XCD
 //    shares A rows and W columns in that XCD's L2.
-//  * Epilogue: alpha * acc in FP32, converted (BF16 round-to-nearest-even or
+//  * Epilogue: alpha * acc in FP32 (alpha times the column's own scale when a
+//    per-column scale is given), converted (BF16 round-to-nearest-even or
 //    FP32), staged through LDS and written as 16-byte row pieces.
+//  * A last round of 256 x 256 tiles that would use at most half the CUs runs
+//    as a second launch over the tiles' 128 x 128 quadrants.
+//  * Two-pass activations (value and residual passes of one activation under
+//    one global scale) contract over 2K, both halves reading the same W chunks.
 //
 // K-order inside a 64-wide chunk: lane half h (= lane / 32) holds k in
 // [32h, 32h + 32) as four dwords; MFMA step s uses dword s of both halves, i.e.

@@ -1,4 +1,5 @@
-// BF16 -> NVFP4 activation quantizer: a tensor-max pass and a block pass.
+// BF16 -> NVFP4 activation quantizer: a tensor-max pass and a block pass (and,
+// for the two-pass prefill, a residual pass per block inside the block pass).
 //
 // Both passes are HBM-bound. Every floating-point step is a single IEEE
 // binary32 operation with round-to-nearest-even (no contraction, no fast math),
