@@ -565,6 +565,42 @@ def test_w4a16_graph_capture_replay_matches_eager():
         assert torch.equal(out, eager)
 
 
+@pytest.mark.parametrize("two_pass", [False, True])
+def test_prefill_graph_capture_replay_matches_eager(two_pass):
+    """The prefill step (on-device quantize into the tile layout, then the W4A4 GEMM with the
+    device 1/gA) captured once in a graph and replayed on new activations: every replay the
+    same bits as eager calls. 4000 x 4192 x 256: 256 x 256 tiles plus the last round as
+    quadrants (two GEMM launches), one- and two-pass."""
+    M, N, K = 4000, 4192, 256
+    b, sb = _random_nvfp4(91, N, K, -3, 3)
+    wp, _ = _prep(b, sb)
+    quant = nv.nvfp4_quantize_two_pass_tiled if two_pass else nv.nvfp4_quantize_tiled
+    gemm_fn = nv.nvfp4_gemm_w4a4_two_pass_tiled if two_pass else nv.nvfp4_gemm_w4a4_tiled
+    xd = dev(synth.normal_bf16(92, M, K)).view(torch.bfloat16).clone()
+    at, g, ig = quant(xd)                                   # buffers, and a warm-up outside capture
+    ws = torch.empty(nv.workspace_bytes(nv.OP_QUANTIZE, M, 0, K), dtype=torch.uint8, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gemm_fn(at, M, wp, N, K, 0.5, ig, "bf16", out)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            quant(xd, at, g, ig, ws)
+            gemm_fn(at, M, wp, N, K, 0.5, ig, "bf16", out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xn = dev(synth.normal_bf16(930 + rep, M, K)).view(torch.bfloat16)
+        xd.copy_(xn)
+        graph.replay()
+        torch.cuda.synchronize()
+        at2, _, ig2 = quant(xn)
+        eager = gemm_fn(at2, M, wp, N, K, 0.5, ig2, "bf16")
+        torch.cuda.synchronize()
+        assert torch.equal(at, at2) and torch.equal(ig, ig2)
+        assert torch.equal(out, eager), f"replay {rep}"
+
+
 # ------------------------------------------------------------------ prefill W4A4 with on-device quantize
 
 def test_prefill_quantize_then_w4a4_full():
