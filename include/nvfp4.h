@@ -52,12 +52,19 @@ typedef enum { NVFP4_SCALE_UE4M3 = 0, NVFP4_SCALE_E4M3 = 1 } nvfp4_scale_kind;
 typedef enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 } nvfp4_out_dtype;
 typedef enum { NVFP4_OP_W4A4 = 0, NVFP4_OP_W4A16 = 1, NVFP4_OP_QUANTIZE = 2 } nvfp4_op;
 
-/* Checks that the current HIP device is gfx950 and records its CU count.
- * Call once per device before the first GEMM (and before any graph capture). */
-nvfp4_status nvfp4_init(void);
+/* Per-device set-up, done outside any graph capture (TileLang PR #3290,
+ * "Changes": the per-device state is created up front, never lazily inside a
+ * capture). Checks that HIP device `device` is gfx950 and records its CU
+ * count, which selects the launch configurations. Calling it is optional: the
+ * first call of any entry point on a device does the same, so only a caller
+ * whose first call would be inside a capture needs it. Thread-safe; repeated
+ * calls are cheap. The calling thread's current device is left unchanged.
+ * Returns NVFP4_ERR_VALUE for a device index out of range,
+ * NVFP4_ERR_UNSUPPORTED for a device that is not gfx950. */
+nvfp4_status nvfp4_init(int device);
 
-/* Human-readable name of a status code (static string). */
-const char *nvfp4_status_string(int status);
+/* Human-readable name of a status code (static string, never NULL). */
+const char *nvfp4_status_str(int status);
 
 /* Size in bytes of a prepared weight: N*K/2 + N*K/16, the same as the packed
  * codes plus the scales (TileLang PR #3290, "Design: Weight layout").
@@ -65,6 +72,11 @@ const char *nvfp4_status_string(int status);
 size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
 
 /* Workspace bytes an op needs for (M, N, K); 0 means no workspace is used.
+ * The workspace is caller-owned device memory, sized by this query before any
+ * graph capture and passed to every call, so no call allocates (TileLang PR
+ * #3290, "Changes": the workspace of split-K partials exists before a capture
+ * and is never created inside one; one workspace per stream that runs
+ * concurrently).
  * The workspace holds A in the prepared tile layout (W4A4: (M rounded up to
  * 32) * K * 9/16 bytes); for W4A16, x in MFMA fragment order (16 < M <= 64:
  * (M rounded up to 32) * K * 2 bytes; M > 64 on 256 x 256 or 128 x 256
@@ -76,8 +88,10 @@ size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* Zeroes a workspace on `stream` with a fill kernel (no hipMemset, so it may be
- * captured). The current kernels do not need a zeroed workspace; the call is
- * kept so that a caller can clear one without hipMemset. */
+ * captured; TileLang PR #3290, "Changes", on the workspace). No kernel of this
+ * library needs a zeroed workspace: every call writes what it later reads. The
+ * call lets a caller clear one without hipMemset. ws: 16-byte aligned device
+ * memory, ws_bytes % 4 == 0 (NVFP4_ERR_ALIGN otherwise). */
 nvfp4_status nvfp4_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Prepare a weight once (TileLang PR #3290, "Design: Weight layout").
@@ -94,7 +108,13 @@ nvfp4_status nvfp4_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * NaN scale bytes (and, for UE4M3, bytes with bit 7 set) keep their codes, get
  * scale byte 0x7F (NaN) and are counted.
  *  bad_count_dev  device int32 or NULL; when given it is overwritten with the
- *  number of invalid scale bytes (read it after the stream completes). */
+ *  number of invalid scale bytes (read it after the stream completes).
+ * NaN scales are an input error (TileLang PR #3290, "Changes", input
+ * validation). They sit in device memory, so this call counts them instead of
+ * reading them back: the Python binding synchronises once after the call and
+ * raises ValueError when the count is not zero (preparation is one-time work,
+ * off the hot path). Weights prepared from such bytes give NaN in the output
+ * columns they touch. */
 nvfp4_status nvfp4_prepare_weight(const uint8_t *w_codes, const uint8_t *w_scales, int scale_kind,
                                   int64_t N, int64_t K, uint8_t *w_prep, int32_t *bad_count_dev,
                                   void *stream);

@@ -3,26 +3,47 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace nvfp4 {
 
-static DeviceInfo g_info[64];
+// One entry per device, filled exactly once (std::call_once), so host threads
+// that make their first call at the same time all see a complete entry.
+static DeviceInfo g_info[kMaxDevices];
+static nvfp4_status g_info_status[kMaxDevices];
+static std::once_flag g_info_once[kMaxDevices];
+
+static void fill_device_info(int dev) {
+  DeviceInfo &d = g_info[dev];
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+    g_info_status[dev] = NVFP4_ERR_HIP;
+    return;
+  }
+  d.num_cus = p.multiProcessorCount;
+  d.gfx950 = (strncmp(p.gcnArchName, "gfx950", 6) == 0);
+  d.device = dev;
+  g_info_status[dev] = d.gfx950 ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
+}
+
+nvfp4_status device_info_of(int dev, DeviceInfo *out) {
+  if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_UNSUPPORTED;
+  std::call_once(g_info_once[dev], fill_device_info, dev);
+  if (out) *out = g_info[dev];
+  return g_info_status[dev];
+}
 
 nvfp4_status device_info(DeviceInfo *out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_HIP;
-  if (dev < 0 || dev >= 64) return NVFP4_ERR_UNSUPPORTED;
-  DeviceInfo &d = g_info[dev];
-  if (d.device != dev) {
-    hipDeviceProp_t p;
-    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return NVFP4_ERR_HIP;
-    d.num_cus = p.multiProcessorCount;
-    d.gfx950 = (strncmp(p.gcnArchName, "gfx950", 6) == 0);
-    d.device = dev;
-  }
-  *out = d;
-  return d.gfx950 ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
+  return device_info_of(dev, out);
+}
+
+nvfp4_status device_setup(int device) {
+  (void)device;
+  return NVFP4_OK;
 }
 
 // ---------------------------------------------------------------- kernels
@@ -83,12 +104,17 @@ using namespace nvfp4;
 
 extern "C" {
 
-nvfp4_status nvfp4_init(void) {
-  DeviceInfo d;
-  return device_info(&d);
+nvfp4_status nvfp4_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return NVFP4_ERR_VALUE;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess) return NVFP4_ERR_HIP;
+  if (device >= count) return NVFP4_ERR_VALUE;
+  nvfp4_status st = device_info_of(device, nullptr);
+  if (st != NVFP4_OK) return st;
+  return device_setup(device);
 }
 
-const char *nvfp4_status_string(int s) {
+const char *nvfp4_status_str(int s) {
   switch (s) {
     case NVFP4_OK: return "ok";
     case NVFP4_ERR_NULL: return "null pointer";

@@ -106,8 +106,16 @@ struct DeviceInfo {
   bool gfx950 = false;
 };
 
-// Per-device properties, filled by nvfp4_init (or lazily by the first call).
+constexpr int kMaxDevices = 64;
+
+// Per-device properties of the current device (device_info) or of a given one,
+// filled once per device by nvfp4_init or by the first call that needs them.
 nvfp4_status device_info(DeviceInfo *out);
+nvfp4_status device_info_of(int dev, DeviceInfo *out);
+
+// Per-device set-up done by nvfp4_init beyond device_info (it makes `device`
+// current for the duration of the call and restores the caller's device).
+nvfp4_status device_setup(int device);
 
 // Workspace sizes of the ops that use one (0 = none).
 size_t w4a4_workspace_bytes(int64_t M, int64_t K);

@@ -812,16 +812,28 @@ struct XRing {
   u32x4_t v[6][T];
 };
 
+// x's fragment-order range of a split: chunks [c0, c0 + n) of the tile's row
+// tiles, one chunk = 4 steps x xmt row tiles x 1 KB.
+struct XRange {
+  const uint8_t *base;
+  int64_t bytes;
+};
+
+// Step s of chunk c (relative to the range) into v. The chunk and step go in
+// the scalar offset, which the buffer range check does not cover, so a chunk
+// at or past the end of the range gets a zero-length resource: its loads read
+// zero instead of whatever lies past the range.
 template <int T>
-__device__ __forceinline__ void load_xf(__amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[T], int64_t c, int s, int xmt,
-                                        u32x4_t (&v)[T]) {
-  const int so = (int)((c * 4 + s) * xmt * 1024);
+__device__ __forceinline__ void load_xf(const XRange &xr, const uint32_t (&ox)[T], int64_t c, int64_t n, int s,
+                                        int xmt, u32x4_t (&v)[T]) {
+  const __amdgpu_buffer_rsrc_t rx = rsrc(xr.base, c < n ? xr.bytes : 0);
+  const int so = c < n ? (int)((c * 4 + s) * xmt * 1024) : 0;
 #pragma unroll
   for (int i = 0; i < T; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], so, 0);
 }
 
 template <int P, int TM, int TN>
-__device__ __forceinline__ void chunk_d(const TileBase &tb, __amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[TM],
+__device__ __forceinline__ void chunk_d(const TileBase &tb, const XRange &rx, const uint32_t (&ox)[TM],
                                         int xmt, const uint32_t (&ow)[TN], const uint32_t (&ows)[TN], int64_t c,
                                         int64_t nch, WFrags<TN> (&f)[3], f32x2_t (&sc)[TN], XRing<TM> &xr,
                                         bf16x8_t (&b)[TN], f32x16_t (&acc)[TM][TN]) {
@@ -832,7 +844,7 @@ __device__ __forceinline__ void chunk_d(const TileBase &tb, __amdgpu_buffer_rsrc
   for (int s = 0; s < 4; s++) {
     const int g = 4 * P + s;                      // step in the three-chunk body
     // x of step g + 5 into the slot step g - 1 used
-    load_xf<TM>(rx, ox, c + (s + 5) / 4, (s + 5) % 4, xmt, xr.v[(g + 5) % 6]);
+    load_xf<TM>(rx, ox, c + (s + 5) / 4, nch, (s + 5) % 4, xmt, xr.v[(g + 5) % 6]);
     if (s == 0) {
       const __amdgpu_buffer_rsrc_t rw = rsrc(tb.w, in2 ? tb.w_bytes : 0);
 #pragma unroll
@@ -885,7 +897,7 @@ __device__ __forceinline__ void tile_mainloop_d(const Params &p, int tile, int64
   tb.ws_bytes = (p.N - n0) / 32 * kt * 128 - c0 * 128;
   // x: chunks [c0, c0 + n) of the tile's row tiles; loads past the range read zero
   const int64_t xchunk = (int64_t)4 * p.xmt * 1024;
-  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xf + c0 * xchunk, n * xchunk);
+  const XRange rx{p.xf + c0 * xchunk, n * xchunk};
   const int lane = threadIdx.x & 63;
   uint32_t ox[TM];
 #pragma unroll
@@ -900,7 +912,7 @@ __device__ __forceinline__ void tile_mainloop_d(const Params &p, int tile, int64
   bf16x8_t b[TN];
   XRing<TM> xr;
 #pragma unroll
-  for (int s = 0; s < 5; s++) load_xf<TM>(rx, ox, s / 4, s % 4, p.xmt, xr.v[s]);
+  for (int s = 0; s < 5; s++) load_xf<TM>(rx, ox, s / 4, n, s % 4, p.xmt, xr.v[s]);
   load_w<TN>(tb, ow, ows, 0, n, f[0]);
   load_w<TN>(tb, ow, ows, 1, n, f[1]);
   scales_of<TN>(f[0], sc);

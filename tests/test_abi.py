@@ -29,9 +29,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = nv.lib()
-    assert L.nvfp4_status_string(0) == b"ok"
-    assert L.nvfp4_status_string(2) == b"bad shape"
-    assert L.nvfp4_status_string(99) == b"unknown status"
+    assert L.nvfp4_status_str(0) == b"ok"
+    assert L.nvfp4_status_str(2) == b"bad shape"
+    assert L.nvfp4_status_str(99) == b"unknown status"
 
 
 def test_prepared_size():
@@ -196,3 +196,32 @@ def test_python_wrapper_type_errors():
     import torch
     with pytest.raises(TypeError):
         nv.nvfp4_gemm_w4a16(torch.zeros(2, 64), None, 32, 64)
+
+
+def test_init_rejects_bad_device_index():
+    L = nv.lib()
+    assert L.nvfp4_init(-1) == nv.ERR_VALUE
+    assert L.nvfp4_init(1 << 20) == nv.ERR_VALUE
+
+
+def test_binding_rejects_host_tensors_before_any_launch():
+    """Every caller-supplied tensor must be a device tensor: a host pointer handed to a kernel
+    would fault the GPU, so the binding raises TypeError before calling the library."""
+    import torch
+    cpu8 = torch.zeros(64, 32, dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        nv.nvfp4_prepare_weight(cpu8, torch.zeros(64, 4, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        nv.nvfp4_gemm_w4a4(cpu8, torch.zeros(64, 4, dtype=torch.uint8), torch.zeros(10, dtype=torch.uint8), 32, 64)
+    with pytest.raises(TypeError):
+        nv.nvfp4_gemm_w4a4_tiled(torch.zeros(4096, dtype=torch.uint8), 64, torch.zeros(10, dtype=torch.uint8), 32, 64)
+    with pytest.raises(TypeError):
+        nv.nvfp4_gemm_w4a16(torch.zeros(2, 64, dtype=torch.bfloat16), torch.zeros(10, dtype=torch.uint8), 32, 64)
+    with pytest.raises(TypeError):
+        nv.nvfp4_quantize(torch.zeros(2, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        nv.nvfp4_quantize_tiled(torch.zeros(2, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        nv.nvfp4_quantize_two_pass_tiled(torch.zeros(2, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        nv.nvfp4_tile_activation(cpu8, torch.zeros(64, 4, dtype=torch.uint8))

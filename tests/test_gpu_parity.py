@@ -29,7 +29,7 @@ def _random_nvfp4(seed, rows, K, lo=-4, hi=4):
 
 
 def _prep(codes, scales, kind="e4m3"):
-    wp, bad = nv.nvfp4_prepare_weight(dev(codes), dev(scales), kind)
+    wp, bad = nv.nvfp4_prepare_weight(dev(codes), dev(scales), kind, validate=False)
     torch.cuda.synchronize()
     return wp, int(bad.item())
 
@@ -46,6 +46,21 @@ def test_prepare_bit_exact(kind):
     ref, bad_ref = prepared.prepare_weight(codes, scales, kind)
     np.testing.assert_array_equal(wp.cpu().numpy(), ref)
     assert bad == bad_ref and bad > 0
+
+
+@pytest.mark.parametrize("kind,byte", [("e4m3", 0x7F), ("e4m3", 0xFF), ("ue4m3", 0x7F), ("ue4m3", 0x80)])
+def test_prepare_rejects_invalid_scale_bytes(kind, byte):
+    """Invalid scale bytes are an input error (TileLang PR #3290, "Changes", input validation):
+    the binding synchronises after the prepare and raises ValueError naming the count."""
+    N, K = 64, 128
+    codes, scales = _random_nvfp4(4, N, K)
+    scales[5, 2] = byte
+    scales[63, 7] = byte
+    with pytest.raises(ValueError, match="^2 scale bytes"):
+        nv.nvfp4_prepare_weight(dev(codes), dev(scales), kind)
+    scales[5, 2] = scales[63, 7] = 0x38
+    wp, bad = nv.nvfp4_prepare_weight(dev(codes), dev(scales), kind)     # valid again: no error
+    assert int(bad.item()) == 0
 
 
 def test_prepare_decode_shape_bit_exact():
@@ -317,6 +332,76 @@ def test_w4a4_normal_8192_full():
     assert_close(host(out), D, Sabs, bf16=True, what="8192^3 full")
 
 
+def test_w4a4_normal_4096_full():
+    """4096^3 (square sweep) in the benchmark's launch configuration: A quantized into the
+    tile layout, B quantized and prepared, nvfp4_gemm_w4a4_tiled into BF16; every output
+    checked, every quantized byte bit-exact."""
+    S = 4096
+    xa, xb = synth.square_normal(S, "A"), synth.square_normal(S, "B")
+    at, gA_t, _ = nv.nvfp4_quantize_tiled(dev(xa).view(torch.bfloat16))
+    cb, sb, gB_d, _ = nv.nvfp4_quantize(dev(xb).view(torch.bfloat16))
+    a_ref, sa_ref, gA = oracle_quantize_full(xa)
+    b_ref, sb_ref, gB = oracle_quantize_full(xb)
+    assert np.float32(gA_t.item()) == gA and np.float32(gB_d.item()) == gB
+    np.testing.assert_array_equal(host(cb), b_ref)
+    np.testing.assert_array_equal(host(sb), sb_ref)
+    # the tile layout is the prepared-weight index map; the quantizer's scales are positive and
+    # its zero-scale blocks already have zero codes, so the folds change nothing
+    tiled_ref, _ = prepared.prepare_weight(a_ref, sa_ref, "ue4m3")
+    np.testing.assert_array_equal(host(at), tiled_ref)
+    wp, _ = nv.nvfp4_prepare_weight(cb, sb, "ue4m3")
+    alpha = alpha_ab(gA, gB)
+    out = nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, float(alpha), None, "bf16")
+    torch.cuda.synchronize()
+    D, Sabs = oracle_w4a4_exact_blocked(a_ref, sa_ref, b_ref, sb_ref, alpha)
+    assert_close(host(out), D, Sabs, bf16=True, what="4096^3 full")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1200)
+def test_w4a4_large_32768_rows():
+    """32768^3 with 1 % outlier rows (x8) and 1 % zeroed blocks, in the square benchmark's
+    launch configuration (tiled A from the quantizer, prepared B, BF16 out). D is 2 GiB, so
+    row offsets exceed 2^31 bytes: the check covers 256 random rows, 64 outlier rows and the
+    first and last rows across all 32768 columns; B's quantized bytes are checked in full, A's
+    on those rows, and the row-major entry must give the tiled entry's bits."""
+    S = 32768
+    xa, outl, _ = synth.square_large(S, "A")
+    r = np.random.default_rng(S)
+    rows = np.unique(np.concatenate([r.choice(S, 256, replace=False), outl[:64], [0, S - 1]]))
+    xad = dev(xa).view(torch.bfloat16)
+    at, gA_t, _ = nv.nvfp4_quantize_tiled(xad)
+    ca, sa, gA_d, _ = nv.nvfp4_quantize(xad)
+    del xad
+    gA = quantize.global_scale(xa)
+    assert np.float32(gA_t.item()) == gA and np.float32(gA_d.item()) == gA
+    a_ref, sa_ref = quantize.quantize_rows_with_g(xa[rows], gA)
+    ridx = torch.as_tensor(rows).cuda()
+    np.testing.assert_array_equal(host(ca[ridx]), a_ref)
+    np.testing.assert_array_equal(host(sa[ridx]), sa_ref)
+    del xa
+    xb, _, _ = synth.square_large(S, "B")
+    cb, sb, gB_d, _ = nv.nvfp4_quantize(dev(xb).view(torch.bfloat16))
+    b_ref, sb_ref, gB = oracle_quantize_full(xb)
+    del xb
+    assert np.float32(gB_d.item()) == gB
+    np.testing.assert_array_equal(host(cb), b_ref)
+    np.testing.assert_array_equal(host(sb), sb_ref)
+    wp, _ = nv.nvfp4_prepare_weight(cb, sb, "ue4m3")
+    del cb, sb
+    alpha = alpha_ab(gA, gB)
+    out = nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, float(alpha), None, "bf16")
+    del at
+    std = nv.nvfp4_gemm_w4a4(ca, sa, wp, S, S, float(alpha), None, "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(out, std), "tiled and row-major entries differ"
+    del std, ca, sa, wp
+    got = host(out[ridx])
+    del out
+    D, Sabs = oracle_w4a4_exact_blocked(a_ref, sa_ref, b_ref, sb_ref, alpha, tile=1024)
+    assert_close(got, D, Sabs, bf16=True, what="32768^3 rows")
+
+
 @pytest.mark.slow
 def test_w4a4_large_16384_rows():
     """16384^3 with 1 % outlier rows (x8) and 1 % zeroed blocks in both operands, in the
@@ -431,6 +516,73 @@ def test_w4a16_big_ragged(M, N, K):
     torch.cuda.synchronize()
     y, S = gemm.w4a16(x, b, sb, alpha)
     assert_close(host(out), y, S, bf16=True, what=f"w4a16 big {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,K", [(4, 8192), (2, 16384), (1, 32768)])
+def test_w4a16_decode_largest_lds(M, K):
+    """The decode kernel stages x in LDS up to M * K * 2 = 64 KiB: the largest (M, K) at each
+    M that still takes the decode path, with a few hundred weight rows; full check."""
+    N = 320
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 13 + K)
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
+    torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"decode LDS edge M={M} K={K}")
+
+
+@pytest.mark.parametrize("M", [1, 3, 24, 100])
+def test_w4a16_misaligned_x_is_copied(M):
+    """x starting one BF16 element past a 16-byte boundary (TileLang PR #3290, "Tests": x not
+    16-byte aligned): the binding copies it to an aligned buffer; the result must match the
+    oracle on the same values."""
+    N, K = 320, 640
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 5 + 11)
+    flat = torch.zeros(M * K + 8, dtype=torch.bfloat16, device="cuda")
+    xv = flat[1:1 + M * K].view(M, K)
+    assert xv.data_ptr() % 16 == 2
+    xv.copy_(dev(x).view(torch.bfloat16))
+    out = nv.nvfp4_gemm_w4a16(xv, wp, N, K, alpha)
+    torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"misaligned x M={M}")
+
+
+def test_binding_rejects_bad_buffers_before_launch():
+    """Caller-supplied outputs and scalars are checked (device, dtype, size) before the C call,
+    so an undersized or host buffer never reaches a kernel."""
+    N, K = 64, 128
+    codes, scales = _random_nvfp4(8, N, K)
+    cd, sd = dev(codes), dev(scales)
+    with pytest.raises(ValueError):
+        nv.nvfp4_prepare_weight(cd, sd, out=torch.empty(10, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(TypeError):
+        nv.nvfp4_prepare_weight(cd, sd, out=torch.empty(N * K, dtype=torch.uint8))           # host
+    with pytest.raises(TypeError):
+        nv.nvfp4_prepare_weight(cd, sd, bad_count=torch.empty(1, dtype=torch.float32, device="cuda"))
+    wp, _ = _prep(codes, scales)
+    with pytest.raises(ValueError):      # too few columns
+        nv.nvfp4_gemm_w4a4(cd, sd, wp, N, K, out=torch.empty((N, N - 32), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(TypeError):       # host output
+        nv.nvfp4_gemm_w4a4(cd, sd, wp, N, K, out=torch.empty((N, N), dtype=torch.bfloat16))
+    with pytest.raises(TypeError):       # wrong dtype
+        nv.nvfp4_gemm_w4a4(cd, sd, wp, N, K, out=torch.empty((N, N), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):      # undersized workspace
+        nv.nvfp4_gemm_w4a4(cd, sd, wp, N, K, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):      # alpha_dev with no value
+        nv.nvfp4_gemm_w4a4(cd, sd, wp, N, K, alpha_dev=torch.empty(0, dtype=torch.float32, device="cuda"))
+    x = torch.zeros((2, K), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        nv.nvfp4_gemm_w4a16(x, wp, N, K, out=torch.empty((1, N), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize(x, codes=torch.empty(K // 2, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize(x, scales=torch.empty(1, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(TypeError):
+        nv.nvfp4_quantize(x, g=torch.empty(1, dtype=torch.float64, device="cuda"))
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize_tiled(x, out=torch.empty(100, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize_tiled(x, ws=torch.empty(4, dtype=torch.uint8, device="cuda"))
 
 
 # ------------------------------------------------------------------ per-column alpha

@@ -147,6 +147,8 @@ def test_quantizer_hand_worked(case):
     codes, scales, g, inv_g = quantize.quantize(x)
     assert list(scales[0]) == case["scales"]
     assert list(codes[0]) == case["codes_packed"]
+    if "g_bits" in case:
+        assert int(np.float32(g).view(np.uint32)) == int(case["g_bits"], 16)
 
 
 def test_quantizer_g_values():
@@ -329,9 +331,13 @@ def test_w4a16_one_hot_and_ones():
     np.testing.assert_allclose(y[1], 0.25 * Wd.sum(axis=1), rtol=1e-15)
 
 
-def test_alpha_product_is_fp32():
-    a = gemm.alpha_product(1.0 / 3.0, 3.0)
-    assert a == np.float32(np.float32(1.0 / 3.0) * np.float32(3.0))
+@pytest.mark.parametrize("case", _golden("hand_worked.json")["alpha"], ids=lambda c: c["name"])
+def test_alpha_product_hand_worked(case):
+    """alpha_eff = host alpha times the device scalar, one FP32 rounding (Colfax article,
+    "Version 3": alpha is an FP32 scale of the accumulator); values worked out by hand."""
+    a = gemm.alpha_product(case["alpha_host"], case["alpha_dev"])
+    assert isinstance(a, np.float32)
+    assert int(a.view(np.uint32)) == int(case["alpha_eff_bits"], 16)
 
 
 def test_column_alpha_is_fp32_per_column():
