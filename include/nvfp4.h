@@ -228,6 +228,20 @@ nvfp4_status nvfp4_quantize_two_pass_tiled(const uint16_t *x, int64_t rows, int6
                                            float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes,
                                            void *stream);
 
+/* nvfp4_quantize_tiled for callers that cannot allocate device memory: code
+ * under graph capture, tight serving loops, and harnesses that forbid
+ * allocation. It takes no workspace and allocates nothing (no hipMalloc, no
+ * hipFree): the 4 KiB the quantizer needs (the tensor-max pass's per-workgroup
+ * maxima) live in a static device array of the library, one per GPU, held
+ * until the process ends. That size does not depend on rows or K, so no input
+ * is too large for it; every call rewrites all of it before reading it, so
+ * nothing needs clearing between calls. Calls that overlap on one GPU (on
+ * different streams) share that array and race: serialise them. The first
+ * call on a device looks up the array's address there; nvfp4_init(device)
+ * does it up front. Arguments, outputs and errors as for nvfp4_quantize_tiled. */
+nvfp4_status nvfp4_quantize_tiled_noalloc(const uint16_t *x, int64_t rows, int64_t K, uint8_t *a_tiled,
+                                          float *g_dev, float *inv_g_dev, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

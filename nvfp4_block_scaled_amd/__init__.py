@@ -48,6 +48,7 @@ _SIGS = [
     ("nvfp4_quantize_two_pass_tiled", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("nvfp4_gemm_w4a4_two_pass_tiled", ctypes.c_int,
      [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _P]),
+    ("nvfp4_quantize_tiled_noalloc", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
 ]
 EXPORTED = [s[0] for s in _SIGS]
 
@@ -404,6 +405,21 @@ def nvfp4_quantize_tiled(x, out=None, g=None, inv_g=None, ws=None):
     g, inv_g = _scalar_outs(g, inv_g, dev)
     wsp, nws = _quantize_ws(ws, rows, K, dev)
     _check(lib().nvfp4_quantize_tiled(_ptr(x), rows, K, _ptr(out), _ptr(g), _ptr(inv_g), wsp, nws, _stream()))
+    return out, g, inv_g
+
+
+def nvfp4_quantize_tiled_noalloc(x, out, g, inv_g=None):
+    """nvfp4_quantize_tiled with no workspace and no allocation: the caller passes every output
+    (out: nvfp4_tiled_activation_bytes(rows, K) uint8; g and inv_g: float32 [1]); the library
+    uses a static device array of its own for the quantizer's scratch."""
+    x = _quantize_inputs(x, 64)
+    rows, K = x.shape
+    _byte_buffer(out, "out", int(lib().nvfp4_tiled_activation_bytes(rows, K)))
+    if g is None:
+        raise ValueError("g is required")
+    _f32_dev(g, "g")
+    _f32_dev(inv_g, "inv_g")
+    _check(lib().nvfp4_quantize_tiled_noalloc(_ptr(x), rows, K, _ptr(out), _ptr(g), _ptr(inv_g), _stream()))
     return out, g, inv_g
 
 

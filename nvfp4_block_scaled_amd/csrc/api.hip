@@ -41,11 +41,6 @@ nvfp4_status device_info(DeviceInfo *out) {
   return device_info_of(dev, out);
 }
 
-nvfp4_status device_setup(int device) {
-  (void)device;
-  return NVFP4_OK;
-}
-
 // ---------------------------------------------------------------- kernels
 
 __global__ void fill_zero_kernel(uint32_t *p, size_t nwords) {

@@ -11,6 +11,8 @@
 // random FP32 values -- at half a vector instruction per element.
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace nvfp4 {
@@ -22,6 +24,46 @@ size_t quantize_workspace_bytes(int64_t rows, int64_t K) {
   (void)rows;
   (void)K;
   return (size_t)kAmaxBlocks * sizeof(uint32_t);
+}
+
+// The quantizer's workspace for callers that cannot allocate: the tensor-max
+// pass's per-workgroup maxima, kAmaxBlocks words (4 KiB) whatever the input
+// size, in a device array of the library's own. Host code never passes
+// `scratch` itself to a kernel (on the host it names a host-side stand-in):
+// it passes the device address that hipGetSymbolAddress returns for it, looked
+// up once per device with that device current.
+static __device__ __align__(256) uint32_t scratch[kAmaxBlocks];
+static void *g_scratch_ptr[kMaxDevices];
+static nvfp4_status g_scratch_status[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+
+// Runs once per device, with `dev` the current device.
+static void lookup_scratch(int dev) {
+  void *ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  g_scratch_ptr[dev] = (e == hipSuccess) ? ptr : nullptr;
+  g_scratch_status[dev] = (e == hipSuccess && ptr) ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+// The scratch array's device address on the current device (looked up on the
+// first use there unless nvfp4_init did it).
+static nvfp4_status scratch_of_current(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], lookup_scratch, dev);
+  *out = g_scratch_ptr[dev];
+  return g_scratch_status[dev];
+}
+
+nvfp4_status device_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return NVFP4_ERR_VALUE;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return NVFP4_ERR_HIP;
+  if (prev != device && hipSetDevice(device) != hipSuccess) return NVFP4_ERR_HIP;
+  std::call_once(g_scratch_once[device], lookup_scratch, device);
+  if (prev != device && hipSetDevice(prev) != hipSuccess) return NVFP4_ERR_HIP;
+  return g_scratch_status[device];
 }
 
 // |x| of a BF16 value orders like its low 15 bits taken as an unsigned integer
@@ -335,4 +377,21 @@ extern "C" nvfp4_status nvfp4_quantize_two_pass_tiled(const uint16_t *x, int64_t
   if (rows < 0 || K <= 0 || K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && (!x || !a2_tiled)) return NVFP4_ERR_NULL;
   return quantize_common(x, rows, K, 2, a2_tiled, nullptr, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" nvfp4_status nvfp4_quantize_tiled_noalloc(const uint16_t *x, int64_t rows, int64_t K, uint8_t *a_tiled,
+                                                     float *g_dev, float *inv_g_dev, void *stream) {
+  if (!g_dev) return NVFP4_ERR_NULL;
+  if (rows < 0 || K <= 0 || K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && (!x || !a_tiled)) return NVFP4_ERR_NULL;
+  DeviceInfo d;
+  nvfp4_status st = device_info(&d);
+  if (st != NVFP4_OK) return st;
+  void *ws = nullptr;
+  st = scratch_of_current(&ws);
+  if (st != NVFP4_OK) return st;
+  // the scratch holds exactly the workspace this quantizer needs, for any rows and K
+  const size_t ws_bytes = sizeof(scratch);
+  if (quantize_workspace_bytes(rows, K) > ws_bytes) return NVFP4_ERR_WORKSPACE;
+  return quantize_common(x, rows, K, 1, a_tiled, nullptr, g_dev, inv_g_dev, ws, ws_bytes, (hipStream_t)stream);
 }

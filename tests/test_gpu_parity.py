@@ -4,6 +4,8 @@ Byte outputs (prepared weights, quantized codes and scales, g) must match
 bit for bit; GEMM outputs must lie inside the stated FP32 / BF16 error bound
 of the exact result (tests/gpu_helpers.py). All inputs are seeded (synth.py).
 """
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -15,6 +17,11 @@ from gpu_helpers import (alpha_ab, assert_close, dev, gpu_quantize_checked, host
                          oracle_w4a4_exact_blocked, oracle_w4a16_blocked)
 
 pytestmark = pytest.mark.gpu
+
+
+def _progress(msg):
+    """A progress line for the long tests (visible with pytest -s)."""
+    print(f"[progress] {msg}", file=sys.stderr, flush=True)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -366,6 +373,7 @@ def test_w4a4_large_32768_rows():
     first and last rows across all 32768 columns; B's quantized bytes are checked in full, A's
     on those rows, and the row-major entry must give the tiled entry's bits."""
     S = 32768
+    _progress("32768^3: generating A")
     xa, outl, _ = synth.square_large(S, "A")
     r = np.random.default_rng(S)
     rows = np.unique(np.concatenate([r.choice(S, 256, replace=False), outl[:64], [0, S - 1]]))
@@ -380,8 +388,10 @@ def test_w4a4_large_32768_rows():
     np.testing.assert_array_equal(host(ca[ridx]), a_ref)
     np.testing.assert_array_equal(host(sa[ridx]), sa_ref)
     del xa
+    _progress("32768^3: generating B")
     xb, _, _ = synth.square_large(S, "B")
     cb, sb, gB_d, _ = nv.nvfp4_quantize(dev(xb).view(torch.bfloat16))
+    _progress("32768^3: oracle quantization of B")
     b_ref, sb_ref, gB = oracle_quantize_full(xb)
     del xb
     assert np.float32(gB_d.item()) == gB
@@ -398,6 +408,7 @@ def test_w4a4_large_32768_rows():
     del std, ca, sa, wp
     got = host(out[ridx])
     del out
+    _progress("32768^3: oracle rows")
     D, Sabs = oracle_w4a4_exact_blocked(a_ref, sa_ref, b_ref, sb_ref, alpha, tile=1024)
     assert_close(got, D, Sabs, bf16=True, what="32768^3 rows")
 
