@@ -50,7 +50,40 @@ typedef enum {
 
 typedef enum { NVFP4_SCALE_UE4M3 = 0, NVFP4_SCALE_E4M3 = 1 } nvfp4_scale_kind;
 typedef enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 } nvfp4_out_dtype;
-typedef enum { NVFP4_OP_W4A4 = 0, NVFP4_OP_W4A16 = 1, NVFP4_OP_QUANTIZE = 2 } nvfp4_op;
+typedef enum {
+  NVFP4_OP_W4A4 = 0,        /* nvfp4_gemm_w4a4 (A row-major: the call tiles it into the workspace) */
+  NVFP4_OP_W4A16 = 1,       /* nvfp4_gemm_w4a16 */
+  NVFP4_OP_QUANTIZE = 2,    /* nvfp4_quantize and its tiled forms */
+  NVFP4_OP_W4A4_TILED = 3   /* nvfp4_gemm_w4a4_tiled and nvfp4_gemm_w4a4_two_pass_tiled */
+} nvfp4_op;
+
+/* Launch configuration of a GEMM (TileLang PR #3290, "Summary" and "Tests": a
+ * heuristic get_config, explicit configs that a caller or a test passes, and
+ * per-GPU tuned tables keyed by SM count that are not applied on another SM
+ * count; Colfax article, "Version 7: Autotuning"). Every field is an int32. */
+typedef enum {
+  NVFP4_KERNEL_AUTO = 0,          /* in a request: let the library choose */
+  NVFP4_KERNEL_W4A4_TILES = 1,    /* W4A4: persistent MFMA kernel over 256 x 256 or 128 x 128 tiles */
+  NVFP4_KERNEL_W4A16_DECODE = 2,  /* W4A16, M <= 4 and M * K * 2 <= 64 KiB: vector-ALU weight streaming */
+  NVFP4_KERNEL_W4A16_SKINNY = 3,  /* W4A16, M <= 64: MFMA over 32-row weight groups, whole K per workgroup */
+  NVFP4_KERNEL_W4A16_TILES = 4    /* W4A16: persistent MFMA kernel over 256 x 256, 128 x 256 or 128 x 128 tiles */
+} nvfp4_kernel;
+typedef enum {
+  NVFP4_TAIL_NONE = 0,       /* tiles past the last whole round of the CUs run as one more round */
+  NVFP4_TAIL_QUADRANTS = 1,  /* ... as 128 x 128 quadrants, two workgroups per CU, in a second launch */
+  NVFP4_TAIL_SPLIT = 2       /* ... split along K over the CUs; a fix-up kernel adds the FP32 partials */
+} nvfp4_tail;
+typedef enum { NVFP4_CONFIG_HEURISTIC = 0, NVFP4_CONFIG_TUNED = 1, NVFP4_CONFIG_EXPLICIT = 2 } nvfp4_config_source;
+typedef struct {
+  int32_t kernel;    /* nvfp4_kernel */
+  int32_t tile_m;    /* rows of D per workgroup tile (W4A4 and W4A16 tiles; 0 otherwise) */
+  int32_t tile_n;    /* columns of D per workgroup tile */
+  int32_t tail;      /* nvfp4_tail (W4A4 on 256 x 256 tiles; NONE otherwise) */
+  int32_t split_k;   /* K ranges per tail tile with NVFP4_TAIL_SPLIT (>= 2), else 0 */
+  int32_t dynamic;   /* W4A4: 1 = workgroups take their tiles from atomic counters in the workspace */
+  int32_t num_cus;   /* CU count the launch is sized for (0 in a request: the current device's) */
+  int32_t source;    /* nvfp4_config_source (set by nvfp4_get_config; ignored in a request) */
+} nvfp4_config;
 
 /* Per-device set-up, done outside any graph capture (TileLang PR #3290,
  * "Changes": the per-device state is created up front, never lazily inside a
@@ -86,6 +119,19 @@ size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
  * device's CU count); or per-workgroup maxima (quantize). Every call
  * overwrites what it reads. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/* The configuration a GEMM call with config == NULL uses for (op, M, N, K) on
+ * a device with num_cus CUs (num_cus == 0: the current device's): a tuned
+ * table entry when the table for that CU count has one for the shape, else the
+ * heuristic. num_cus < 0 returns the heuristic for -num_cus CUs without looking
+ * at the table (what a tuning run compares against). Host-only (no device
+ * work when num_cus != 0). op: NVFP4_OP_W4A4, NVFP4_OP_W4A4_TILED (two-pass
+ * calls: K is the contraction length 2K), or NVFP4_OP_W4A16. */
+nvfp4_status nvfp4_get_config(int op, int64_t M, int64_t N, int64_t K, int num_cus, nvfp4_config *out);
+
+/* Workspace bytes of a call that uses `config` (NULL: nvfp4_workspace_bytes).
+ * Returns 0 when the config is not valid for the shape. */
+size_t nvfp4_config_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, const nvfp4_config *config);
 
 /* Zeroes a workspace on `stream` with a fill kernel (no hipMemset, so it may be
  * captured; TileLang PR #3290, "Changes", on the workspace). No kernel of this
@@ -133,15 +179,27 @@ nvfp4_status nvfp4_prepare_weight(const uint8_t *w_codes, const uint8_t *w_scale
  *  d        [M][ldd] elements of out_dtype (FP32 or BF16 with round-to-nearest-
  *           even), device, element-aligned; ldd >= N.
  *  M >= 0 (M == 0 is a no-op), N % 32 == 0, K % 64 == 0.
- *  ws  workspace of nvfp4_workspace_bytes(NVFP4_OP_W4A4, M, N, K) bytes, device,
- *      16-byte aligned, no initialisation needed: the call first copies A into
- *      it in the prepared tile layout (nvfp4_tile_activation), then runs the
- *      GEMM from there (nvfp4_gemm_w4a4_tiled). Calls that share a workspace
- *      must not run concurrently. */
+ *  config  NULL (nvfp4_get_config's choice), or an explicit launch
+ *      configuration: kernel NVFP4_KERNEL_W4A4_TILES (or AUTO), tile_m ==
+ *      tile_n == 256 or 128, tail NONE / QUADRANTS / SPLIT with split_k in
+ *      [2, K/64] (256 x 256 tiles only), dynamic 0 or 1, num_cus >= 0. An
+ *      invalid config returns NVFP4_ERR_VALUE.
+ *  ws  workspace of nvfp4_config_workspace_bytes(NVFP4_OP_W4A4, M, N, K, config)
+ *      bytes (nvfp4_workspace_bytes for config == NULL), device, 16-byte
+ *      aligned, no initialisation needed: the call first copies A into it in
+ *      the prepared tile layout (nvfp4_tile_activation), then runs the GEMM
+ *      from there (nvfp4_gemm_w4a4_tiled), with the K-split partials and the
+ *      dynamic scheduler's counters (reset by a kernel on every call) in the
+ *      rest. Calls that share a workspace must not run concurrently.
+ * The K split of the tail (row "split-K partials + fixed-order reduce": TileLang
+ * PR #3290, "Design": FP32 partials of split tiles summed in a fixed order)
+ * sums each tile's ranges in range order, so results are bit-identical from
+ * call to call; they differ in the last bits from an unsplit launch, whose
+ * FP32 sum runs in another order. */
 nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
                              int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
-                             const float *alpha_col, void *d, int out_dtype, int64_t ldd, void *ws,
-                             size_t ws_bytes, void *stream);
+                             const float *alpha_col, void *d, int out_dtype, int64_t ldd,
+                             const nvfp4_config *config, void *ws, size_t ws_bytes, void *stream);
 
 /* Bytes of an activation in the tile layout: nvfp4_prepared_weight_bytes for M
  * rounded up to 32 rows (0 for M <= 0 or K % 64 != 0). */
@@ -158,21 +216,28 @@ nvfp4_status nvfp4_tile_activation(const uint8_t *a_codes, const uint8_t *a_scal
                                    uint8_t *a_tiled, void *stream);
 
 /* nvfp4_gemm_w4a4 on an A that nvfp4_tile_activation has already tiled; the
- * other arguments as there. Needs no workspace. */
+ * other arguments as there. The workspace (nvfp4_config_workspace_bytes with
+ * NVFP4_OP_W4A4_TILED) holds only the K-split partials and the scheduler's
+ * counters. With config == NULL, ws may be NULL: the call then runs the
+ * chosen configuration without them (a K-split tail as quadrants, a dynamic
+ * schedule as the static one), so it needs no workspace at all. */
 nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N, int64_t K,
                                    float alpha, const float *alpha_dev, const float *alpha_col, void *d,
-                                   int out_dtype, int64_t ldd, void *stream);
+                                   int out_dtype, int64_t ldd, const nvfp4_config *config, void *ws,
+                                   size_t ws_bytes, void *stream);
 
 /* Two-pass W4A4 GEMM: D = alpha_eff * (A1 + A2)(W.SFW)^T, A1 and A2 the two
  * passes of nvfp4_quantize_two_pass_tiled (a2_tiled, rows M, K columns per
  * pass) against a prepared weight of shape (N, K): one contraction over 2K in
  * which the residual half reads the same W chunks as the value half (TileLang
  * PR #3290, "Follow-ups"). alpha_eff as for nvfp4_gemm_w4a4 (the passes share
- * g, so alpha is the one-pass prefill's 1/(gA gW)); other arguments as for
- * nvfp4_gemm_w4a4_tiled. Needs no workspace. */
+ * g, so alpha is the one-pass prefill's 1/(gA gW)); other arguments, the
+ * config (sized for a contraction of length 2K) and the workspace
+ * (NVFP4_OP_W4A4_TILED with K = 2K) as for nvfp4_gemm_w4a4_tiled. */
 nvfp4_status nvfp4_gemm_w4a4_two_pass_tiled(const uint8_t *a2_tiled, const uint8_t *w_prep, int64_t M, int64_t N,
                                             int64_t K, float alpha, const float *alpha_dev, const float *alpha_col,
-                                            void *d, int out_dtype, int64_t ldd, void *stream);
+                                            void *d, int out_dtype, int64_t ldd, const nvfp4_config *config,
+                                            void *ws, size_t ws_bytes, void *stream);
 
 /* W4A16 GEMM: y = alpha_eff * x (W.SFW)^T, x and y BF16, FP32 accumulation
  * (TileLang PR #3290, "Summary": BF16 activations against NVFP4 weights with
@@ -182,13 +247,18 @@ nvfp4_status nvfp4_gemm_w4a4_two_pass_tiled(const uint8_t *a2_tiled, const uint8
  *  x  [M][ldx] BF16 (uint16 bit patterns), device, 16-byte aligned, ldx % 8 == 0, ldx >= K.
  *  y  [M][ldy] BF16, device, 2-byte aligned, ldy >= N.
  *  M >= 0, N % 32 == 0, K % 64 == 0.
- *  ws  workspace of nvfp4_workspace_bytes(NVFP4_OP_W4A16, M, N, K) bytes (may be
- *      NULL when that is 0). Calls that share a workspace must not run
- *      concurrently (use one workspace per stream). */
+ *  config  NULL (nvfp4_get_config's choice) or an explicit kernel
+ *      (TileLang PR #3290, "Tests": explicit configs): DECODE (M <= 4 and
+ *      M * K * 2 <= 64 KiB), SKINNY (M <= 64) or TILES with (tile_m, tile_n)
+ *      = (256, 256), (128, 256) or (128, 128); tail, split_k and dynamic 0.
+ *      An invalid config returns NVFP4_ERR_VALUE.
+ *  ws  workspace of nvfp4_config_workspace_bytes(NVFP4_OP_W4A16, M, N, K,
+ *      config) bytes (may be NULL when that is 0). Calls that share a
+ *      workspace must not run concurrently (use one workspace per stream). */
 nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_prep, int64_t M,
                               int64_t N, int64_t K, float alpha, const float *alpha_dev,
-                              const float *alpha_col, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
-                              void *stream);
+                              const float *alpha_col, uint16_t *y, int64_t ldy, const nvfp4_config *config,
+                              void *ws, size_t ws_bytes, void *stream);
 
 /* BF16 -> NVFP4 quantizer for activations fed to W4A4 (the format as the pages
  * use it: packed E2M1 codes, E4M3 block scales, a per-tensor global scale;

@@ -23,7 +23,25 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_VALUE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(9)
 SCALE_UE4M3, SCALE_E4M3 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
-OP_W4A4, OP_W4A16, OP_QUANTIZE = 0, 1, 2
+OP_W4A4, OP_W4A16, OP_QUANTIZE, OP_W4A4_TILED = 0, 1, 2, 3
+KERNEL_AUTO, KERNEL_W4A4_TILES, KERNEL_W4A16_DECODE, KERNEL_W4A16_SKINNY, KERNEL_W4A16_TILES = range(5)
+TAIL_NONE, TAIL_QUADRANTS, TAIL_SPLIT = range(3)
+CONFIG_HEURISTIC, CONFIG_TUNED, CONFIG_EXPLICIT = range(3)
+
+
+class Config(ctypes.Structure):
+    """nvfp4_config: a GEMM launch configuration (see include/nvfp4.h)."""
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("kernel", "tile_m", "tile_n", "tail", "split_k", "dynamic", "num_cus", "source")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+    def __repr__(self):
+        return f"Config({self.as_dict()})"
+
+
+_CFG = ctypes.POINTER(Config)
 
 # C signatures: (name, restype, argtypes)
 _P = ctypes.c_void_p
@@ -33,21 +51,23 @@ _SIGS = [
     ("nvfp4_status_str", ctypes.c_char_p, [ctypes.c_int]),
     ("nvfp4_prepared_weight_bytes", ctypes.c_size_t, [_I64, _I64]),
     ("nvfp4_workspace_bytes", ctypes.c_size_t, [ctypes.c_int, _I64, _I64, _I64]),
+    ("nvfp4_get_config", ctypes.c_int, [ctypes.c_int, _I64, _I64, _I64, ctypes.c_int, _CFG]),
+    ("nvfp4_config_workspace_bytes", ctypes.c_size_t, [ctypes.c_int, _I64, _I64, _I64, _CFG]),
     ("nvfp4_workspace_init", ctypes.c_int, [_P, ctypes.c_size_t, _P]),
     ("nvfp4_prepare_weight", ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P]),
     ("nvfp4_gemm_w4a4", ctypes.c_int,
-     [_P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P]),
+     [_P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _CFG, _P, ctypes.c_size_t, _P]),
     ("nvfp4_tiled_activation_bytes", ctypes.c_size_t, [_I64, _I64]),
     ("nvfp4_tile_activation", ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     ("nvfp4_gemm_w4a4_tiled", ctypes.c_int,
-     [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _P]),
+     [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _CFG, _P, ctypes.c_size_t, _P]),
     ("nvfp4_gemm_w4a16", ctypes.c_int,
-     [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _I64, _P, ctypes.c_size_t, _P]),
+     [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _I64, _CFG, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize_tiled", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize_two_pass_tiled", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("nvfp4_gemm_w4a4_two_pass_tiled", ctypes.c_int,
-     [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _P]),
+     [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_int, _I64, _CFG, _P, ctypes.c_size_t, _P]),
     ("nvfp4_quantize_tiled_noalloc", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
 ]
 EXPORTED = [s[0] for s in _SIGS]
@@ -173,13 +193,44 @@ def prepared_weight_bytes(N, K):
     return int(lib().nvfp4_prepared_weight_bytes(N, K))
 
 
-def workspace_bytes(op, M, N, K):
-    return int(lib().nvfp4_workspace_bytes(op, M, N, K))
+def workspace_bytes(op, M, N, K, config=None):
+    """Workspace bytes of a call with `config` (None: the library's choice)."""
+    if config is None:
+        return int(lib().nvfp4_workspace_bytes(op, M, N, K))
+    return int(lib().nvfp4_config_workspace_bytes(op, M, N, K, ctypes.byref(_config(config))))
 
 
-def workspace(op, M, N, K, device="cuda"):
-    """Allocate and zero a workspace for (op, M, N, K); None when the op needs none."""
-    n = workspace_bytes(op, M, N, K)
+def get_config(op, M, N, K, num_cus=0):
+    """The configuration a call without one uses (tuned table entry or heuristic) on a device
+    with num_cus CUs (0: the current device's)."""
+    c = Config()
+    _check(lib().nvfp4_get_config(op, M, N, K, num_cus, ctypes.byref(c)))
+    return c
+
+
+def make_config(kernel=KERNEL_AUTO, tile_m=0, tile_n=0, tail=TAIL_NONE, split_k=0, dynamic=0, num_cus=0):
+    """An explicit configuration for the GEMM calls' `config` argument."""
+    return Config(kernel, tile_m, tile_n, tail, split_k, dynamic, num_cus, CONFIG_EXPLICIT)
+
+
+def _config(config):
+    if config is None:
+        return None
+    if isinstance(config, Config):
+        return config
+    if isinstance(config, dict):
+        return make_config(**config)
+    raise TypeError("config must be a Config, a dict of its fields, or None")
+
+
+def _cfg_arg(config):
+    c = _config(config)
+    return None if c is None else ctypes.byref(c)
+
+
+def workspace(op, M, N, K, device="cuda", config=None):
+    """Allocate and zero a workspace for (op, M, N, K[, config]); None when the call needs none."""
+    n = workspace_bytes(op, M, N, K, config)
     if n == 0:
         return None
     ws = torch.empty(n, dtype=torch.uint8, device=device)
@@ -273,7 +324,7 @@ def _gemm_out(out, M, N, dtype, device):
 
 
 def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None, ws=None,
-                    alpha_col=None):
+                    alpha_col=None, config=None):
     a_codes = _u8(a_codes, "a_codes")
     a_scales = _u8(a_scales, "a_scales")
     M = a_codes.shape[0] if a_codes.dim() == 2 else 0
@@ -284,12 +335,13 @@ def nvfp4_gemm_w4a4(a_codes, a_scales, w_prep, N, K, alpha=1.0, alpha_dev=None, 
     out = _gemm_out(out, M, N, dtype, a_codes.device)
     alpha_dev = _f32_dev(alpha_dev, "alpha_dev")
     alpha_col = _check_alpha_col(alpha_col, N)
-    need = workspace_bytes(OP_W4A4, M, N, K)
+    need = workspace_bytes(OP_W4A4, M, N, K, config)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=a_codes.device)
     wsp, nws = _workspace_arg(ws, need)
     _check(lib().nvfp4_gemm_w4a4(_ptr(a_codes), _ptr(a_scales), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
-                                 _ptr(alpha_col), _ptr(out), code, _ld(out, M, N), wsp, nws, _stream()))
+                                 _ptr(alpha_col), _ptr(out), code, _ld(out, M, N), _cfg_arg(config), wsp, nws,
+                                 _stream()))
     return out
 
 
@@ -310,8 +362,12 @@ def nvfp4_tile_activation(a_codes, a_scales, out=None):
 
 
 def nvfp4_gemm_w4a4_tiled(a_tiled, M, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None,
-                          alpha_col=None):
-    """nvfp4_gemm_w4a4 on an activation already in the tile layout (nvfp4_tile_activation)."""
+                          alpha_col=None, config=None, ws=None):
+    """nvfp4_gemm_w4a4 on an activation already in the tile layout (nvfp4_tile_activation).
+
+    ws: the K-split / scheduler workspace (workspace_bytes(OP_W4A4_TILED, M, N, K, config)); when
+    None it is allocated for an explicit config, and left out otherwise (the library then runs its
+    choice without one)."""
     a_tiled = _u8(a_tiled, "a_tiled")
     if a_tiled.numel() < int(lib().nvfp4_tiled_activation_bytes(M, K)):
         raise ValueError("a_tiled is smaller than nvfp4_tiled_activation_bytes(M, K)")
@@ -320,12 +376,17 @@ def nvfp4_gemm_w4a4_tiled(a_tiled, M, w_prep, N, K, alpha=1.0, alpha_dev=None, o
     out = _gemm_out(out, M, N, dtype, a_tiled.device)
     alpha_dev = _f32_dev(alpha_dev, "alpha_dev")
     alpha_col = _check_alpha_col(alpha_col, N)
+    need = workspace_bytes(OP_W4A4_TILED, M, N, K, config)
+    if ws is None and need > 0 and config is not None:
+        ws = torch.empty(need, dtype=torch.uint8, device=a_tiled.device)
+    wsp, nws = _workspace_arg(ws, need)
     _check(lib().nvfp4_gemm_w4a4_tiled(_ptr(a_tiled), _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
-                                       _ptr(alpha_col), _ptr(out), code, _ld(out, M, N), _stream()))
+                                       _ptr(alpha_col), _ptr(out), code, _ld(out, M, N), _cfg_arg(config), wsp, nws,
+                                       _stream()))
     return out
 
 
-def nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=None, alpha_col=None):
+def nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=None, alpha_col=None, config=None):
     _on_device(x, "x")
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
@@ -339,13 +400,13 @@ def nvfp4_gemm_w4a16(x, w_prep, N, K, alpha=1.0, alpha_dev=None, out=None, ws=No
     out = _gemm_out(out, M, N, torch.bfloat16, x.device)
     alpha_dev = _f32_dev(alpha_dev, "alpha_dev")
     alpha_col = _check_alpha_col(alpha_col, N)
-    need = workspace_bytes(OP_W4A16, M, N, K)
+    need = workspace_bytes(OP_W4A16, M, N, K, config)
     if ws is None and need > 0:
-        ws = workspace(OP_W4A16, M, N, K, x.device)
+        ws = workspace(OP_W4A16, M, N, K, x.device, config)
     wsp, nws = _workspace_arg(ws, need)
     ldx = x.stride(0) if M > 1 else K
     _check(lib().nvfp4_gemm_w4a16(_ptr(x), ldx, _ptr(w_prep), M, N, K, float(alpha), _ptr(alpha_dev),
-                                  _ptr(alpha_col), _ptr(out), _ld(out, M, N), wsp, nws, _stream()))
+                                  _ptr(alpha_col), _ptr(out), _ld(out, M, N), _cfg_arg(config), wsp, nws, _stream()))
     return out
 
 
@@ -441,7 +502,7 @@ def nvfp4_quantize_two_pass_tiled(x, out=None, g=None, inv_g=None, ws=None):
 
 
 def nvfp4_gemm_w4a4_two_pass_tiled(a2_tiled, M, w_prep, N, K, alpha=1.0, alpha_dev=None, out_dtype="bf16", out=None,
-                                   alpha_col=None):
+                                   alpha_col=None, config=None, ws=None):
     """D = alpha (A1 + A2) W^T on a two-pass activation (nvfp4_quantize_two_pass_tiled, K per pass)."""
     a2_tiled = _u8(a2_tiled, "a2_tiled")
     if a2_tiled.numel() < int(lib().nvfp4_tiled_activation_bytes(M, 2 * K)):
@@ -451,7 +512,11 @@ def nvfp4_gemm_w4a4_two_pass_tiled(a2_tiled, M, w_prep, N, K, alpha=1.0, alpha_d
     out = _gemm_out(out, M, N, dtype, a2_tiled.device)
     alpha_dev = _f32_dev(alpha_dev, "alpha_dev")
     alpha_col = _check_alpha_col(alpha_col, N)
+    need = workspace_bytes(OP_W4A4_TILED, M, N, 2 * K, config)
+    if ws is None and need > 0 and config is not None:
+        ws = torch.empty(need, dtype=torch.uint8, device=a2_tiled.device)
+    wsp, nws = _workspace_arg(ws, need)
     _check(lib().nvfp4_gemm_w4a4_two_pass_tiled(_ptr(a2_tiled), _ptr(w_prep), M, N, K, float(alpha),
                                                 _ptr(alpha_dev), _ptr(alpha_col), _ptr(out), code, _ld(out, M, N),
-                                                _stream()))
+                                                _cfg_arg(config), wsp, nws, _stream()))
     return out

@@ -124,15 +124,6 @@ const char *nvfp4_status_str(int s) {
   }
 }
 
-size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
-  switch (op) {
-    case NVFP4_OP_W4A4: return w4a4_workspace_bytes(M, K);
-    case NVFP4_OP_W4A16: return w4a16_workspace_bytes(M, N, K);
-    case NVFP4_OP_QUANTIZE: return quantize_workspace_bytes(M, K);
-    default: return 0;
-  }
-}
-
 size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0) return 0;
   return (size_t)(N * K / 2 + N * K / 16);

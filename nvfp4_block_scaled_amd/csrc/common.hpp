@@ -117,10 +117,25 @@ nvfp4_status device_info_of(int dev, DeviceInfo *out);
 // current for the duration of the call and restores the caller's device).
 nvfp4_status device_setup(int device);
 
-// Workspace sizes of the ops that use one (0 = none).
-size_t w4a4_workspace_bytes(int64_t M, int64_t K);
-size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Workspace of the quantizer (0 = none), and A in the tile layout.
 size_t quantize_workspace_bytes(int64_t rows, int64_t K);
+size_t tiled_activation_bytes(int64_t M, int64_t K);
+
+// Launch configurations (config.hip): the heuristic of each GEMM, the check of
+// an explicit config, and the workspace a config needs (0 for an invalid one).
+// A resolved config has its kernel and num_cus set.
+void w4a4_default_config(int64_t M, int64_t N, int64_t K, int cus, nvfp4_config *c);
+bool w4a4_config_valid(int64_t M, int64_t N, int64_t K, const nvfp4_config &c);
+size_t w4a4_config_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, const nvfp4_config &c);
+void w4a16_default_config(int64_t M, int64_t N, int64_t K, int cus, nvfp4_config *c);
+bool w4a16_config_valid(int64_t M, int64_t N, int64_t K, const nvfp4_config &c);
+size_t w4a16_config_workspace_bytes(int64_t M, int64_t N, int64_t K, const nvfp4_config &c);
+
+// The config a call runs: the caller's (checked: NVFP4_ERR_VALUE if invalid;
+// num_cus 0 becomes device_cus) or, for NULL, the tuned table's / heuristic's
+// for device_cus CUs.
+nvfp4_status resolve_config(int op, int64_t M, int64_t N, int64_t K, const nvfp4_config *req, int device_cus,
+                            nvfp4_config *out);
 
 inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -65,12 +65,6 @@ constexpr int kSkinnyMaxM = 64;
 constexpr int kSkinnyDirectMaxM = 16;   // up to here the skinny kernel reads x rows directly
 constexpr int kDecodeLdsBytes = 64 * 1024;  // x staged in LDS: M * K * 2 bytes at most
 
-static int num_cus_or_default() {
-  DeviceInfo d;
-  if (device_info(&d) == NVFP4_OK && d.num_cus > 0) return d.num_cus;
-  return 256;
-}
-
 // Output tiles of the big kernel, as MFMA tiles per wave (TM x TN; the
 // workgroup tile is 64 TM x 64 TN):
 //  * 4 x 4 (256 x 256) when those fill the CUs, or when they are fewer but K
@@ -107,10 +101,26 @@ static void big_tile_shape(int64_t M, int64_t N, int64_t K, int cus, int &TM, in
 // slower on the 27B-class decode shapes).
 static int decode_shape(int64_t N, int cus) { return N / 32 >= 2 * cus ? 0 : 1; }
 
-static Plan make_plan(int64_t M, int64_t N, int64_t K) {
+// MFMA tiles per wave and waves along M of a TILES config's workgroup tile.
+static void tiles_of(const nvfp4_config &c, int &TM, int &TN, int &WGM) {
+  if (c.tile_m == 256) {
+    TM = TN = 4;
+    WGM = 2;
+  } else if (c.tile_n == 256) {
+    TM = 4;
+    TN = 2;
+    WGM = 1;
+  } else {
+    TM = TN = WGM = 2;
+  }
+}
+
+static bool decode_fits(int64_t M, int64_t K) { return M <= kDecodeMaxM && M * K * 2 <= kDecodeLdsBytes; }
+
+static Plan make_plan(int64_t M, int64_t N, int64_t K, const nvfp4_config &c) {
   Plan p{};
-  const int cus = num_cus_or_default();
-  if (M <= kDecodeMaxM && M * K * 2 <= kDecodeLdsBytes) {
+  const int cus = c.num_cus;
+  if (c.kernel == NVFP4_KERNEL_W4A16_DECODE) {
     p.kind = 0;
     p.dec = decode_shape(N, cus);
     const DecodeShape &sh = kDecodeShapes[p.dec];
@@ -129,7 +139,7 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K) {
         p.nfull = full;
       }
     }
-  } else if (M <= kSkinnyMaxM) {
+  } else if (c.kernel == NVFP4_KERNEL_W4A16_SKINNY) {
     p.kind = 3;
     p.grid_x = N / 32;
   } else {
@@ -178,9 +188,10 @@ struct BigSched {
   int64_t tile_cols() const { return 32 * TN * (4 / WGM); }
 };
 
-static BigSched big_sched(int64_t M, int64_t N, int64_t K, int cus) {
+static BigSched big_sched(int64_t M, int64_t N, int64_t K, const nvfp4_config &c) {
   BigSched b{};
-  big_tile_shape(M, N, K, cus, b.TM, b.TN, b.WGM);
+  const int cus = c.num_cus;
+  tiles_of(c, b.TM, b.TN, b.WGM);
   b.tiles_m = (M + b.tile_rows() - 1) / b.tile_rows();
   b.tiles_n = (N + b.tile_cols() - 1) / b.tile_cols();
   b.total = b.tiles_m * b.tiles_n;
@@ -217,10 +228,10 @@ static size_t big_partials_span(const BigSched &b) {
 static int64_t big_xmt(const BigSched &b) { return b.TM * b.TN >= 8 ? b.tiles_m * b.tile_rows() / 32 : 0; }
 static size_t big_xf_bytes(const BigSched &b, int64_t K) { return (size_t)big_xmt(b) * 32 * (size_t)K * 2; }
 
-static size_t workspace_for(const Plan &p, int64_t M, int64_t N, int64_t K) {
+static size_t workspace_for(const Plan &p, const nvfp4_config &c, int64_t M, int64_t N, int64_t K) {
   if (p.kind == 3) return M > kSkinnyDirectMaxM ? skinny_x_bytes(M, K) : 0;
   if (p.kind == 4) {
-    const BigSched b = big_sched(M, N, K, num_cus_or_default());
+    const BigSched b = big_sched(M, N, K, c);
     return big_partials_span(b) + big_xf_bytes(b, K);
   }
   return 0;
@@ -1114,10 +1125,42 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
 
 }  // namespace w4a16
 
-size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0) return 0;
-  w4a16::Plan p = w4a16::make_plan(M, N, K);
-  return w4a16::workspace_for(p, M, N, K);
+// The heuristic configuration: the decode kernel while x fits in its LDS
+// (M <= 4), the skinny kernel up to M = 64, else the tile kernel with
+// big_tile_shape's tiles.
+void w4a16_default_config(int64_t M, int64_t N, int64_t K, int cus, nvfp4_config *c) {
+  *c = nvfp4_config{};
+  c->num_cus = cus;
+  if (w4a16::decode_fits(M, K)) {
+    c->kernel = NVFP4_KERNEL_W4A16_DECODE;
+  } else if (M <= w4a16::kSkinnyMaxM) {
+    c->kernel = NVFP4_KERNEL_W4A16_SKINNY;
+  } else {
+    int TM, TN, WGM;
+    w4a16::big_tile_shape(M, N, K, cus, TM, TN, WGM);
+    c->kernel = NVFP4_KERNEL_W4A16_TILES;
+    c->tile_m = 32 * TM * WGM;
+    c->tile_n = 32 * TN * (4 / WGM);
+  }
+}
+
+bool w4a16_config_valid(int64_t M, int64_t N, int64_t K, const nvfp4_config &c) {
+  (void)N;
+  if (c.num_cus <= 0 || c.tail != NVFP4_TAIL_NONE || c.split_k != 0 || c.dynamic != 0) return false;
+  switch (c.kernel) {
+    case NVFP4_KERNEL_W4A16_DECODE: return w4a16::decode_fits(M, K);
+    case NVFP4_KERNEL_W4A16_SKINNY: return M <= w4a16::kSkinnyMaxM;
+    case NVFP4_KERNEL_W4A16_TILES:
+      return (c.tile_m == 256 && c.tile_n == 256) || (c.tile_m == 128 && c.tile_n == 256) ||
+             (c.tile_m == 128 && c.tile_n == 128);
+    default: return false;
+  }
+}
+
+size_t w4a16_config_workspace_bytes(int64_t M, int64_t N, int64_t K, const nvfp4_config &c) {
+  if (M <= 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0 || !w4a16_config_valid(M, N, K, c)) return 0;
+  const w4a16::Plan p = w4a16::make_plan(M, N, K, c);
+  return w4a16::workspace_for(p, c, M, N, K);
 }
 
 }  // namespace nvfp4
@@ -1125,8 +1168,9 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 using namespace nvfp4;
 
 extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_prep, int64_t M, int64_t N,
-                                         int64_t K, float alpha, const float *alpha_dev, const float *alpha_col, uint16_t *y, int64_t ldy,
-                                         void *ws, size_t ws_bytes, void *stream) {
+                                         int64_t K, float alpha, const float *alpha_dev, const float *alpha_col,
+                                         uint16_t *y, int64_t ldy, const nvfp4_config *config, void *ws,
+                                         size_t ws_bytes, void *stream) {
   if (M < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0 || ldx < K || ldy < N) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
   if (!x || !w_prep || !y) return NVFP4_ERR_NULL;
@@ -1137,8 +1181,11 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   DeviceInfo di;
   nvfp4_status st = device_info(&di);
   if (st != NVFP4_OK) return st;
-  const w4a16::Plan plan = w4a16::make_plan(M, N, K);
-  const size_t need = w4a16::workspace_for(plan, M, N, K);
+  nvfp4_config cfg;
+  st = resolve_config(NVFP4_OP_W4A16, M, N, K, config, di.num_cus, &cfg);
+  if (st != NVFP4_OK) return st;
+  const w4a16::Plan plan = w4a16::make_plan(M, N, K, cfg);
+  const size_t need = w4a16::workspace_for(plan, cfg, M, N, K);
   if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
@@ -1171,7 +1218,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
 #undef NVFP4_DECODE_SHAPE
 #undef NVFP4_DECODE_CASE
   } else if (plan.kind == 4) {
-    const w4a16::BigSched b = w4a16::big_sched(M, N, K, di.num_cus);
+    const w4a16::BigSched b = w4a16::big_sched(M, N, K, cfg);
     // fragment-order x: 32-bit offsets inside it
     if (b.total > 0x7FFFFFFF || w4a16::big_xf_bytes(b, K) > 0x7FFFFFFFull) return NVFP4_ERR_SHAPE;
     if (b.TM * b.TN < 8 && (int64_t)128 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;   // LDS path: 32-bit x offsets
@@ -1217,7 +1264,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
       NVFP4_LAUNCH_CHECK();
     }
     const unsigned grid = (unsigned)plan.grid_x;
-    const int W = w4a16::skinny_waves(N, di.num_cus);
+    const int W = w4a16::skinny_waves(N, cfg.num_cus);
 #define NVFP4_SKINNY(MTV, XFV, WV, NGV)                                                                         \
   hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV, WV, NGV>), dim3(grid / NGV), dim3(WV * 64), 0, s, x, ldx,     \
                      w_prep, M, N, K, alpha, alpha_dev, alpha_col, y, ldy, xf)

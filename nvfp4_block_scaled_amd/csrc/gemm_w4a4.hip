@@ -92,10 +92,39 @@ struct Params {
   const float *alpha_dev;
   const float *alpha_col;   // per-column scale [N] or null
   int tiles_m, tiles_n;     // tile grid of D (in workgroup tiles; in 256 x 256 tiles when quad)
-  int count;                // tiles this launch computes
-  int first;                // quad: first 256 x 256 tile (raster index) whose quadrants it computes
+  int count;                // whole tiles this launch computes (raster indices 0 .. count - 1)
+  int first;                // quad / split: first 256 x 256 tile (raster index) whose quadrants or
+                            // K ranges it computes
   int quad;                 // 1: 128 x 128 workgroups on the quadrants of 256 x 256 tiles first ..
+  int split;                // K ranges of each split tile (>= 2 when nsplit > 0)
+  int nsplit;               // tiles first .. first + nsplit - 1 are split along K
+  float *partials;          // FP32 partial tile of split work unit count + q at slot q
+  uint32_t *sched;          // dynamic scheduling counters (null: static schedule)
 };
+
+// FP32 values of one 256 x 256 partial tile, in MFMA accumulator order:
+// [wave][i][j][lane][16].
+constexpr int64_t kPartialFloats = 4 * 4 * 4 * 64 * 16;
+constexpr int kSchedCounters = 8;          // one work counter per XCD
+constexpr size_t kSchedBytes = 256;        // their workspace region
+
+// Work units of a launch: the whole tiles, then split * nsplit K ranges.
+__host__ __device__ inline int work_units(const Params &p) { return p.count + p.nsplit * p.split; }
+
+// Tile and K chunks [c0, c1) of work unit u (whole tiles: all nch chunks).
+__device__ __forceinline__ void unit_chunks(const Params &p, int u, int64_t nch, int &tile, int64_t &c0,
+                                            int64_t &c1) {
+  if (u < p.count) {
+    tile = u;
+    c0 = 0;
+    c1 = nch;
+    return;
+  }
+  const int v = u - p.count, q = v % p.split;
+  tile = p.first + v / p.split;
+  c0 = nch * q / p.split;
+  c1 = nch * (q + 1) / p.split;
+}
 
 // Raw buffer resource over [base, base + bytes); loads at offsets >= bytes
 // return 0 (the hardware range check), which zero-fills ragged rows/columns
@@ -348,6 +377,45 @@ __device__ __forceinline__ void tile_origin(const Params &p, int tile, int64_t &
   }
 }
 
+// The FP32 accumulators of a split work unit to its partial slot (T = 4 only):
+// lane-contiguous 64 bytes per MFMA tile, so each wave writes 4 KB runs.
+template <int T>
+__device__ __forceinline__ void store_partial(const Params &p, int u, f32x16_t acc[T][T]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float *slot = p.partials + (int64_t)(u - p.count) * kPartialFloats;
+#pragma unroll
+  for (int i = 0; i < T; i++)
+#pragma unroll
+    for (int j = 0; j < T; j++) {
+      f32x4_t *dst = reinterpret_cast<f32x4_t *>(slot + (((wave * T + i) * T + j) * 64 + lane) * 16);
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        dst[q] = f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
+}
+
+// Dynamic schedule: the workgroups of hardware XCD x (ids congruent to x
+// mod 8) take the work units of their own share of each round of G units from
+// a counter of their own, sched[x], so an XCD's L2 sees the same tiles as
+// under the static schedule while the order inside an XCD follows whichever
+// workgroup is free first. The counters are zeroed by sched_reset_kernel,
+// launched just before on the same stream. Every workgroup leaves the loop at
+// its first fetch past the last unit, so the grid always drains.
+__device__ __forceinline__ int fetch_unit(const Params &p, int G, int *s_unit) {
+  const int nx = (G & 7) == 0 ? 8 : 1, per = G / nx, x = blockIdx.x % nx;
+  __syncthreads();   // every wave has read the previous unit
+  if (threadIdx.x == 0) {
+    const int f = (int)atomicAdd(&p.sched[x], 1u);
+    *s_unit = (f / per) * G + x * per + f % per;
+  }
+  __syncthreads();
+  return *s_unit;
+}
+
+__global__ void sched_reset_kernel(uint32_t *sched) {
+  if (threadIdx.x < kSchedCounters) sched[threadIdx.x] = 0u;
+}
+
 // T = 4: 256 x 256 workgroup tiles, one workgroup per CU (all 512 registers of
 // a lane in use). T = 2: 128 x 128 tiles, two workgroups per CU: for problems
 // with fewer 256 x 256 tiles than CUs, and for the quadrants of the 256 x 256
@@ -357,10 +425,16 @@ __device__ __forceinline__ void tile_origin(const Params &p, int tile, int64_t &
 // TWO: A is a two-pass activation of 2K columns (value, then residual, in the
 // tile layout) against W of K columns: the contraction runs over 2K, and chunk
 // c >= K/64 uses W's chunk c - K/64.
-template <bool OUT_BF16, int T, bool COLS, bool TWO>
+// XS (T = 4): the extended schedule, a separate instantiation so that the
+// plain one keeps its registers: work units are the whole tiles, then the K
+// ranges of split tiles, whose accumulators go to partial slots for
+// split_fixup_kernel instead of D; with p.sched, workgroups fetch their units
+// dynamically.
+template <bool OUT_BF16, int T, bool COLS, bool TWO, bool XS>
 __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p) {
   constexpr int BT = 64 * T;                      // workgroup tile edge
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * 32 * 32 * T * 4];
+  __shared__ int s_unit;
   const int t = threadIdx.x;
   const int wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -372,7 +446,8 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
   const float alpha = load_alpha(p.alpha, p.alpha_dev);
   const int64_t ktw = p.K / 64;                   // W's chunks
   const int64_t kt = TWO ? 2 * ktw : ktw;         // A's chunks, the contraction's length
-  const int64_t nch = kt;
+  const int units = XS ? work_units(p) : p.count;
+  const bool dyn = XS && p.sched != nullptr;
 
   const int lane = t & 63, r = lane & 31;
   WaveOff<T> o;
@@ -384,7 +459,10 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
     o.ws[i] = (uint32_t)(((wn * T + i) * ktw) * 128 + r * 4);
   }
 
-  for (int tile = pid; tile < p.count; tile += G) {
+  for (int u = dyn ? fetch_unit(p, G, &s_unit) : pid; u < units; u = dyn ? fetch_unit(p, G, &s_unit) : u + G) {
+    int tile = u;
+    int64_t c0 = 0, nch = kt;                      // chunks [c0, nch); loads at or past nch read zero
+    if constexpr (XS) unit_chunks(p, u, kt, tile, c0, nch);
     int64_t m0, n0;
     tile_origin<BT>(p, tile, m0, n0);
     if (m0 >= p.M || n0 >= p.N) continue;   // a quadrant past the edge of D (uniform per workgroup)
@@ -407,32 +485,85 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
     ChunkFrags<T> f[3];
     ChunkScales sc;
     half8_t a[T], b[T];
-    load_frags<T, TWO>(tr, o, 0, nch, ktw, f[0]);
-    load_frags<T, TWO>(tr, o, 1, nch, ktw, f[1]);
+    load_frags<T, TWO>(tr, o, c0, nch, ktw, f[0]);
+    load_frags<T, TWO>(tr, o, c0 + 1, nch, ktw, f[1]);
     convert_scales<T>(f[0], sc);
     unpack_step<T>(f[0], sc, 0, a, b);
     if constexpr (COLS) {
       // chunks in threes, the last ones padded with all-zero chunks: a tail as below
       // would push this instantiation's extra epilogue registers into more spills
       // (measured 7 % slower at 8192^3)
-      for (int64_t c = 0; c < nch; c += 3) {
+      for (int64_t c = c0; c < nch; c += 3) {
         chunk_direct<0, T, TWO>(tr, o, c, nch, ktw, f, sc, a, b, acc);
         chunk_direct<1, T, TWO>(tr, o, c + 1, nch, ktw, f, sc, a, b, acc);
         chunk_direct<2, T, TWO>(tr, o, c + 2, nch, ktw, f, sc, a, b, acc);
       }
     } else {
-      int64_t c = 0;
+      int64_t c = c0;
       for (; c + 3 <= nch; c += 3) {
         chunk_direct<0, T, TWO>(tr, o, c, nch, ktw, f, sc, a, b, acc);
         chunk_direct<1, T, TWO>(tr, o, c + 1, nch, ktw, f, sc, a, b, acc);
         chunk_direct<2, T, TWO>(tr, o, c + 2, nch, ktw, f, sc, a, b, acc);
       }
-      // the one or two chunks left when K/64 is not a multiple of 3 (ring position 0, then 1)
+      // the one or two chunks left when the range is not a multiple of 3 (ring position 0, then 1)
       if (c < nch) chunk_direct<0, T, TWO>(tr, o, c, nch, ktw, f, sc, a, b, acc);
       if (c + 1 < nch) chunk_direct<1, T, TWO>(tr, o, c + 1, nch, ktw, f, sc, a, b, acc);
     }
+    if (XS && u >= p.count) {
+      store_partial<T>(p, u, acc);
+      continue;
+    }
     __syncthreads();
     epilogue<OUT_BF16, T, COLS>(smem, p, m0, n0, wm, wn, alpha, acc);
+  }
+}
+
+// Sums the partial tiles of each split 256 x 256 tile in range order (a fixed
+// order, so the result does not depend on which workgroup ran which range)
+// and applies the epilogue. Workgroup = (split tile, wave, MFMA row i) of the
+// main kernel's layout; thread = (MFMA column j, lane): 16 values, four ranges'
+// loads in flight at a time.
+template <bool OUT_BF16, bool COLS>
+__global__ __launch_bounds__(256) void split_fixup_kernel(Params p) {
+  const int tl = blockIdx.x >> 4, wi = blockIdx.x & 15, wave = wi >> 2, i = wi & 3;
+  const int j = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+  int64_t m0, n0;
+  tile_origin<256>(p, p.first + tl, m0, n0);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t col = n0 + wn * 128 + j * 32 + r;
+  const int64_t row0 = m0 + wm * 128 + i * 32 + 4 * h;
+  const float *base =
+      p.partials + (int64_t)tl * p.split * kPartialFloats + (((wave * 4 + i) * 4 + j) * 64 + lane) * 16;
+  f32x16_t sum = f32x16_t{};
+  for (int q0 = 0; q0 < p.split; q0 += 4) {
+    f32x4_t v[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const f32x4_t *src = reinterpret_cast<const f32x4_t *>(base + (int64_t)(q0 + b) * kPartialFloats);
+#pragma unroll
+      for (int q = 0; q < 4; q++) v[b][q] = q0 + b < p.split ? src[q] : f32x4_t{};
+    }
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+      if (q0 + b < p.split)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+          for (int e = 0; e < 4; e++) sum[4 * q + e] = sum[4 * q + e] + v[b][q][e];
+  }
+  if (col >= p.N) return;
+  const float alpha = load_alpha(p.alpha, p.alpha_dev);
+  const float aj = COLS ? alpha * p.alpha_col[col] : alpha;
+#pragma unroll
+  for (int e = 0; e < 16; e++) {
+    const int64_t m = row0 + 8 * (e >> 2) + (e & 3);
+    if (m < p.M) {
+      const float v = aj * sum[e];
+      if (OUT_BF16)
+        reinterpret_cast<uint16_t *>(p.d)[m * p.ldd + col] = f32_to_bf16_rne(v);
+      else
+        reinterpret_cast<float *>(p.d)[m * p.ldd + col] = v;
+    }
   }
 }
 
@@ -441,9 +572,111 @@ __global__ __launch_bounds__(kThreads, T == 4 ? 1 : 2) void gemm_kernel(Params p
 
 using namespace nvfp4;
 
-size_t nvfp4::w4a4_workspace_bytes(int64_t M, int64_t K) {
+size_t nvfp4::tiled_activation_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || K % 64 != 0) return 0;
   return (size_t)(w4a4::padded_rows(M) * K / 2 + w4a4::padded_rows(M) * K / 16);
+}
+
+namespace {
+
+// How a resolved config runs (M, N) with a contraction of nch chunks.
+struct Plan {
+  int T;               // MFMA tiles per wave and dimension (4: 256 x 256, 2: 128 x 128)
+  int tiles_m, tiles_n;
+  int grid;            // workgroups of the main launch
+  int count;           // whole tiles of the main launch
+  int split, nsplit;   // K ranges per split tile, split tiles
+  int quad;            // tiles whose quadrants a second launch computes
+  bool dynamic;
+};
+
+Plan make_plan(int64_t M, int64_t N, const nvfp4_config &c) {
+  Plan p{};
+  const int64_t cus = c.num_cus;
+  p.dynamic = c.dynamic != 0;
+  if (c.tile_m == 256) {
+    p.T = 4;
+    p.tiles_m = (int)((M + 255) / 256);
+    p.tiles_n = (int)((N + 255) / 256);
+    const int64_t t = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t rem = c.tail == NVFP4_TAIL_NONE ? 0 : t % cus;
+    p.count = (int)(t - rem);
+    if (c.tail == NVFP4_TAIL_QUADRANTS) p.quad = (int)rem;
+    if (c.tail == NVFP4_TAIL_SPLIT && rem > 0) {
+      p.split = c.split_k;
+      p.nsplit = (int)rem;
+    }
+    const int64_t units = p.count + (int64_t)p.nsplit * p.split;
+    p.grid = (int)(units < cus ? units : cus);
+  } else {
+    p.T = 2;
+    p.tiles_m = (int)((M + 127) / 128);
+    p.tiles_n = (int)((N + 127) / 128);
+    const int64_t t = (int64_t)p.tiles_m * p.tiles_n;
+    p.count = (int)t;
+    p.grid = (int)(t < 2 * cus ? t : 2 * cus);
+  }
+  return p;
+}
+
+// Workspace of the tiled GEMM under a plan: the dynamic schedule's counters,
+// then the split ranges' partial tiles.
+size_t sched_bytes(const Plan &p) { return p.dynamic ? w4a4::kSchedBytes : 0; }
+size_t partial_bytes(const Plan &p) { return (size_t)p.nsplit * p.split * w4a4::kPartialFloats * 4; }
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+}  // namespace
+
+// The heuristic configuration for a contraction of length K:
+//  * at least as many 256 x 256 tiles as CUs: those tiles, persistent. When
+//    they do not make whole rounds and the last round would use at most half
+//    the CUs, the leftover tiles run as 128 x 128 quadrants in a second launch,
+//    or, for K >= kSplitMinK, split in two along K (the partials and their
+//    fix-up cost about as much as 50 us of tile work, which only a long K
+//    amortises: at K = 17408 the split took 8192 x 5120 from 989.5 to 971.4 us,
+//    while at K = 5120 quadrants beat it, 992 against 1012.5 us on the prefill
+//    shape);
+//  * fewer: 128 x 128 tiles, two workgroups per CU.
+constexpr int64_t kSplitMinK = 12288;
+
+void nvfp4::w4a4_default_config(int64_t M, int64_t N, int64_t K, int cus, nvfp4_config *c) {
+  *c = nvfp4_config{};
+  c->kernel = NVFP4_KERNEL_W4A4_TILES;
+  c->num_cus = cus;
+  const int64_t t4 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (t4 >= cus) {
+    c->tile_m = c->tile_n = 256;
+    const int64_t rem = t4 % cus;
+    if (rem > 0 && 2 * rem <= cus) {
+      if (K >= kSplitMinK) {
+        c->tail = NVFP4_TAIL_SPLIT;
+        c->split_k = 2;
+      } else {
+        c->tail = NVFP4_TAIL_QUADRANTS;
+      }
+    }
+  } else {
+    c->tile_m = c->tile_n = 128;
+  }
+}
+
+bool nvfp4::w4a4_config_valid(int64_t M, int64_t N, int64_t K, const nvfp4_config &c) {
+  (void)M;
+  (void)N;
+  if (c.kernel != NVFP4_KERNEL_W4A4_TILES || c.num_cus <= 0 || (c.dynamic != 0 && c.dynamic != 1)) return false;
+  if (c.tile_m != c.tile_n || (c.tile_m != 256 && c.tile_m != 128)) return false;
+  if (c.tail < NVFP4_TAIL_NONE || c.tail > NVFP4_TAIL_SPLIT) return false;
+  if (c.tile_m == 128 && (c.tail != NVFP4_TAIL_NONE || c.dynamic != 0)) return false;
+  if (c.tail == NVFP4_TAIL_SPLIT) return c.split_k >= 2 && c.split_k <= K / 64;
+  return c.split_k == 0;
+}
+
+size_t nvfp4::w4a4_config_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, const nvfp4_config &c) {
+  if (M <= 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 64 != 0 || !w4a4_config_valid(M, N, K, c)) return 0;
+  const Plan p = make_plan(M, N, c);
+  const size_t tail = sched_bytes(p) + partial_bytes(p);
+  if (op == NVFP4_OP_W4A4_TILED) return tail;
+  return round256(tiled_activation_bytes(M, K)) + tail;
 }
 
 namespace {
@@ -465,60 +698,124 @@ nvfp4_status check_gemm_args(const uint8_t *w_prep, int64_t M, int64_t N, int64_
   return NVFP4_OK;
 }
 
-template <int T, bool TWO>
+template <int T, bool TWO, bool XS>
 void launch_tiles(const w4a4::Params &p, int grid, int out_dtype, hipStream_t s) {
   const dim3 g(grid), b(w4a4::kThreads);
   if (out_dtype == NVFP4_OUT_BF16) {
-    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, true, TWO>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, false, TWO>), g, b, 0, s, p);
+    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, true, TWO, XS>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((w4a4::gemm_kernel<true, T, false, TWO, XS>), g, b, 0, s, p);
   } else {
-    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, true, TWO>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, false, TWO>), g, b, 0, s, p);
+    if (p.alpha_col) hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, true, TWO, XS>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((w4a4::gemm_kernel<false, T, false, TWO, XS>), g, b, 0, s, p);
   }
 }
 
+// The extended schedule (split ranges, dynamic fetch) exists for T = 4 only.
 template <int T>
 void launch_tiles(const w4a4::Params &p, int grid, int out_dtype, bool two, hipStream_t s) {
-  if (two) launch_tiles<T, true>(p, grid, out_dtype, s);
-  else launch_tiles<T, false>(p, grid, out_dtype, s);
+  const bool xs = T == 4 && (p.nsplit > 0 || p.sched != nullptr);
+  if (two) {
+    if (xs) launch_tiles<4, true, true>(p, grid, out_dtype, s);
+    else launch_tiles<T, true, false>(p, grid, out_dtype, s);
+  } else {
+    if (xs) launch_tiles<4, false, true>(p, grid, out_dtype, s);
+    else launch_tiles<T, false, false>(p, grid, out_dtype, s);
+  }
 }
 
-// The GEMM kernel proper on A already in the tile layout (arguments checked).
-//  * At least as many 256 x 256 tiles as CUs: the T = 4 kernel, one persistent
-//    workgroup per CU. When the tiles do not make whole rounds and the last
-//    round would use at most half the CUs, that round's tiles are left to a
-//    second launch of the T = 2 kernel on their 128 x 128 quadrants (two
-//    workgroups per CU, so the round takes about half as long). Each output
-//    element sees the same sequence of MFMAs either way: the results are the
-//    same bits as with T = 4 alone.
-//  * Fewer: the T = 2 kernel on 128 x 128 tiles.
+void launch_fixup(const w4a4::Params &p, int out_dtype, hipStream_t s) {
+  const dim3 g((unsigned)(p.nsplit * 16)), b(256);
+  if (out_dtype == NVFP4_OUT_BF16) {
+    if (p.alpha_col) hipLaunchKernelGGL((w4a4::split_fixup_kernel<true, true>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((w4a4::split_fixup_kernel<true, false>), g, b, 0, s, p);
+  } else {
+    if (p.alpha_col) hipLaunchKernelGGL((w4a4::split_fixup_kernel<false, true>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((w4a4::split_fixup_kernel<false, false>), g, b, 0, s, p);
+  }
+}
+
+// The GEMM proper on A in the tile layout under a resolved config (arguments
+// checked; tail is the workspace region of the counters and partials, or null
+// when the plan needs none). Launches, in stream order:
+//  * static schedule: the persistent kernel over the whole tiles, then the
+//    tail: the quadrant launch, or the split tiles' K ranges (the extended
+//    instantiation, in a launch of their own so that the whole tiles keep the
+//    plain one's registers) and the fix-up;
+//  * dynamic schedule: the counters' reset, then one launch of the extended
+//    instantiation over the whole tiles and the split ranges, then the fix-up.
+// An output element sees the same MFMA sequence in a whole tile and in a
+// quadrant, so those give the same bits; a split tile sums its ranges'
+// partials instead.
 nvfp4_status launch_gemm(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N, int64_t K, float alpha,
                          const float *alpha_dev, const float *alpha_col, void *d, int out_dtype, int64_t ldd, bool two,
-                         hipStream_t s) {
-  DeviceInfo di;
-  nvfp4_status st = device_info(&di);
-  if (st != NVFP4_OK) return st;
-  const int64_t cus = di.num_cus;
-  const int64_t tm4 = (M + 255) / 256, tn4 = (N + 255) / 256, t4 = tm4 * tn4;
-  if (t4 >= cus) {
-    const int64_t rem = t4 % cus;
-    const int64_t full = rem > 0 && 2 * rem <= cus ? t4 - rem : t4;
-    w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, alpha_col, (int)tm4, (int)tn4, (int)full, 0, 0};
-    launch_tiles<4>(p, (int)cus, out_dtype, two, s);
+                         const nvfp4_config &cfg, uint8_t *tail, hipStream_t s) {
+  const Plan pl = make_plan(M, N, cfg);
+  w4a4::Params p{};
+  p.a_tiled = a_tiled;
+  p.w_prep = w_prep;
+  p.d = d;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ldd = ldd;
+  p.alpha = alpha;
+  p.alpha_dev = alpha_dev;
+  p.alpha_col = alpha_col;
+  p.tiles_m = pl.tiles_m;
+  p.tiles_n = pl.tiles_n;
+  p.count = pl.count;
+  p.first = pl.count;
+  float *partials = pl.nsplit > 0 ? reinterpret_cast<float *>(tail + sched_bytes(pl)) : nullptr;
+  const int64_t cus = cfg.num_cus;
+  if (pl.dynamic) {
+    p.sched = reinterpret_cast<uint32_t *>(tail);
+    p.split = pl.split;
+    p.nsplit = pl.nsplit;
+    p.partials = partials;
+    hipLaunchKernelGGL(w4a4::sched_reset_kernel, dim3(1), dim3(64), 0, s, p.sched);
     NVFP4_LAUNCH_CHECK();
-    if (full < t4) {
-      p.count = (int)(4 * (t4 - full));   // <= 2 * cus: one workgroup per quadrant
-      p.first = (int)full;
-      p.quad = 1;
-      launch_tiles<2>(p, p.count, out_dtype, two, s);
+    if (pl.grid > 0) {
+      launch_tiles<4>(p, pl.grid, out_dtype, two, s);
       NVFP4_LAUNCH_CHECK();
     }
-    return NVFP4_OK;
+  } else {
+    if (pl.count > 0) {
+      const int grid = (int)(pl.T == 4 ? std::min<int64_t>(cus, pl.count) : pl.grid);
+      if (pl.T == 4) launch_tiles<4>(p, grid, out_dtype, two, s);
+      else launch_tiles<2>(p, grid, out_dtype, two, s);
+      NVFP4_LAUNCH_CHECK();
+    }
+    if (pl.nsplit > 0) {
+      w4a4::Params q = p;             // the split tiles' K ranges only
+      q.count = 0;
+      q.split = pl.split;
+      q.nsplit = pl.nsplit;
+      q.partials = partials;
+      const int64_t units = (int64_t)pl.nsplit * pl.split;
+      launch_tiles<4>(q, (int)std::min<int64_t>(cus, units), out_dtype, two, s);
+      NVFP4_LAUNCH_CHECK();
+    }
   }
-  const int64_t tm2 = (M + 127) / 128, tn2 = (N + 127) / 128, t2 = tm2 * tn2;
-  w4a4::Params p{a_tiled, w_prep, d, M, N, K, ldd, alpha, alpha_dev, alpha_col, (int)tm2, (int)tn2, (int)t2, 0, 0};
-  launch_tiles<2>(p, (int)(t2 < 2 * cus ? t2 : 2 * cus), out_dtype, two, s);
-  NVFP4_LAUNCH_CHECK();
+  if (pl.nsplit > 0) {
+    w4a4::Params q = p;
+    q.count = pl.dynamic ? pl.count : 0;
+    q.split = pl.split;
+    q.nsplit = pl.nsplit;
+    q.partials = partials;
+    launch_fixup(q, out_dtype, s);
+    NVFP4_LAUNCH_CHECK();
+  }
+  if (pl.quad > 0) {
+    w4a4::Params q = p;
+    q.count = 4 * pl.quad;   // one workgroup per quadrant
+    q.first = pl.count;
+    q.quad = 1;
+    q.split = q.nsplit = 0;
+    q.partials = nullptr;
+    q.sched = nullptr;
+    launch_tiles<2>(q, q.count, out_dtype, two, s);
+    NVFP4_LAUNCH_CHECK();
+  }
   return NVFP4_OK;
 }
 
@@ -529,9 +826,32 @@ void launch_tile_a(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, i
                      M, K, at);
 }
 
+// Resolves the config of a tiled-A call (contraction length Kc) and finds its
+// workspace region. With no caller config and a workspace that cannot hold
+// what the chosen config needs, the K-split tail becomes quadrants and the
+// schedule static, which need none.
+nvfp4_status tiled_config(int64_t M, int64_t N, int64_t Kc, const nvfp4_config *config, int cus, void *ws,
+                          size_t ws_bytes, nvfp4_config *cfg, uint8_t **tail) {
+  nvfp4_status st = resolve_config(NVFP4_OP_W4A4_TILED, M, N, Kc, config, cus, cfg);
+  if (st != NVFP4_OK) return st;
+  size_t need = w4a4_config_workspace_bytes(NVFP4_OP_W4A4_TILED, M, N, Kc, *cfg);
+  if (need > 0 && (!ws || ws_bytes < need)) {
+    if (config) return NVFP4_ERR_WORKSPACE;
+    if (cfg->tail == NVFP4_TAIL_SPLIT) {
+      cfg->tail = NVFP4_TAIL_QUADRANTS;
+      cfg->split_k = 0;
+    }
+    cfg->dynamic = 0;
+    need = 0;
+  }
+  if (need > 0 && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+  *tail = need > 0 ? static_cast<uint8_t *>(ws) : nullptr;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
-extern "C" size_t nvfp4_tiled_activation_bytes(int64_t M, int64_t K) { return w4a4_workspace_bytes(M, K); }
+extern "C" size_t nvfp4_tiled_activation_bytes(int64_t M, int64_t K) { return tiled_activation_bytes(M, K); }
 
 extern "C" nvfp4_status nvfp4_tile_activation(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
                                               uint8_t *a_tiled, void *stream) {
@@ -551,18 +871,27 @@ extern "C" nvfp4_status nvfp4_tile_activation(const uint8_t *a_codes, const uint
 extern "C" nvfp4_status nvfp4_gemm_w4a4_tiled(const uint8_t *a_tiled, const uint8_t *w_prep, int64_t M, int64_t N,
                                               int64_t K, float alpha, const float *alpha_dev,
                                               const float *alpha_col, void *d, int out_dtype, int64_t ldd,
+                                              const nvfp4_config *config, void *ws, size_t ws_bytes,
                                               void *stream) {
   nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd);
   if (st != NVFP4_OK || M == 0) return st;
   if (!a_tiled) return NVFP4_ERR_NULL;
   if (!aligned(a_tiled, 16)) return NVFP4_ERR_ALIGN;
-  return launch_gemm(a_tiled, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, false,
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != NVFP4_OK) return st;
+  nvfp4_config cfg;
+  uint8_t *tail = nullptr;
+  st = tiled_config(M, N, K, config, di.num_cus, ws, ws_bytes, &cfg, &tail);
+  if (st != NVFP4_OK) return st;
+  return launch_gemm(a_tiled, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, false, cfg, tail,
                      (hipStream_t)stream);
 }
 
 extern "C" nvfp4_status nvfp4_gemm_w4a4_two_pass_tiled(const uint8_t *a2_tiled, const uint8_t *w_prep, int64_t M,
                                                        int64_t N, int64_t K, float alpha, const float *alpha_dev,
                                                        const float *alpha_col, void *d, int out_dtype, int64_t ldd,
+                                                       const nvfp4_config *config, void *ws, size_t ws_bytes,
                                                        void *stream) {
   nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd);
   if (st != NVFP4_OK || M == 0) return st;
@@ -570,27 +899,41 @@ extern "C" nvfp4_status nvfp4_gemm_w4a4_two_pass_tiled(const uint8_t *a2_tiled, 
   if (!aligned(a2_tiled, 16)) return NVFP4_ERR_ALIGN;
   // 32-bit buffer offsets inside one 256-row tile of the 2K-column activation
   if ((int64_t)8 * (2 * K / 64) * 1024 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
-  return launch_gemm(a2_tiled, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, true,
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != NVFP4_OK) return st;
+  nvfp4_config cfg;
+  uint8_t *tail = nullptr;
+  st = tiled_config(M, N, 2 * K, config, di.num_cus, ws, ws_bytes, &cfg, &tail);
+  if (st != NVFP4_OK) return st;
+  return launch_gemm(a2_tiled, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, true, cfg, tail,
                      (hipStream_t)stream);
 }
 
 extern "C" nvfp4_status nvfp4_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_prep,
                                         int64_t M, int64_t N, int64_t K, float alpha, const float *alpha_dev,
-                                        const float *alpha_col, void *d, int out_dtype, int64_t ldd, void *ws,
-                                        size_t ws_bytes, void *stream) {
+                                        const float *alpha_col, void *d, int out_dtype, int64_t ldd,
+                                        const nvfp4_config *config, void *ws, size_t ws_bytes, void *stream) {
   nvfp4_status st = check_gemm_args(w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd);
   if (st != NVFP4_OK || M == 0) return st;
   if (!a_codes || !a_scales) return NVFP4_ERR_NULL;
   if (!aligned(a_codes, 16) || !aligned(a_scales, 4)) return NVFP4_ERR_ALIGN;
-  const size_t need = w4a4_workspace_bytes(M, K);
-  if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+  // the workspace holds at least A's tile copy (checked before any device query)
+  if (!ws || ws_bytes < tiled_activation_bytes(M, K)) return NVFP4_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
   DeviceInfo di;
   st = device_info(&di);
   if (st != NVFP4_OK) return st;
+  nvfp4_config cfg;
+  st = resolve_config(NVFP4_OP_W4A4, M, N, K, config, di.num_cus, &cfg);
+  if (st != NVFP4_OK) return st;
+  const size_t need = w4a4_config_workspace_bytes(NVFP4_OP_W4A4, M, N, K, cfg);
+  if (ws_bytes < need) return NVFP4_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *at = static_cast<uint8_t *>(ws);
+  uint8_t *tail = at + round256(tiled_activation_bytes(M, K));
+  if (need == round256(tiled_activation_bytes(M, K))) tail = nullptr;
   launch_tile_a(a_codes, a_scales, M, K, at, s);
   NVFP4_LAUNCH_CHECK();
-  return launch_gemm(at, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, false, s);
+  return launch_gemm(at, w_prep, M, N, K, alpha, alpha_dev, alpha_col, d, out_dtype, ldd, false, cfg, tail, s);
 }

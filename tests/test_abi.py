@@ -15,6 +15,7 @@ HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 
 def _declared():
     text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)          # declarations only, not comments
     return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
 
 
@@ -55,7 +56,7 @@ def test_gemm_w4a4_argument_checks():
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["a"], a["s"], a["w"], a["M"], a["N"], a["K"], a["alpha"], a["ad"], a["ac"], a["d"], a["dt"],
-                 a["ldd"], a["ws"], a["nws"], None)
+                 a["ldd"], None, a["ws"], a["nws"], None)
     assert call(dt=7) == nv.ERR_DTYPE
     assert call(K=96) == nv.ERR_SHAPE
     assert call(N=48) == nv.ERR_SHAPE
@@ -90,7 +91,7 @@ def test_tile_activation_and_tiled_gemm_argument_checks():
     g = L.nvfp4_gemm_w4a4_tiled
 
     def call(at=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ac=None, d=FAKE, dt=nv.OUT_BF16, ldd=64):
-        return g(at, w, M, N, K, alpha, None, ac, d, dt, ldd, None)
+        return g(at, w, M, N, K, alpha, None, ac, d, dt, ldd, None, None, 0, None)
     assert call(dt=5) == nv.ERR_DTYPE
     assert call(K=96) == nv.ERR_SHAPE
     assert call(N=40) == nv.ERR_SHAPE
@@ -123,7 +124,7 @@ def test_two_pass_argument_checks():
     g = L.nvfp4_gemm_w4a4_two_pass_tiled
 
     def call(at=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ac=None, d=FAKE, dt=nv.OUT_BF16, ldd=64):
-        return g(at, w, M, N, K, alpha, None, ac, d, dt, ldd, None)
+        return g(at, w, M, N, K, alpha, None, ac, d, dt, ldd, None, None, 0, None)
     assert call(dt=3) == nv.ERR_DTYPE
     assert call(K=96) == nv.ERR_SHAPE
     assert call(M=0) == nv.OK
@@ -137,7 +138,7 @@ def test_gemm_w4a16_argument_checks():
     f = nv.lib().nvfp4_gemm_w4a16
 
     def call(x=FAKE, ldx=128, w=FAKE, M=1, N=64, K=128, alpha=1.0, ac=None, y=FAKE, ldy=64, ws=None, nws=0):
-        return f(x, ldx, w, M, N, K, alpha, None, ac, y, ldy, ws, nws, None)
+        return f(x, ldx, w, M, N, K, alpha, None, ac, y, ldy, None, ws, nws, None)
     assert call(K=100) == nv.ERR_SHAPE
     assert call(ldx=64) == nv.ERR_SHAPE
     assert call(ldy=32) == nv.ERR_SHAPE
@@ -225,3 +226,104 @@ def test_binding_rejects_host_tensors_before_any_launch():
         nv.nvfp4_quantize_two_pass_tiled(torch.zeros(2, 64, dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         nv.nvfp4_tile_activation(cpu8, torch.zeros(64, 4, dtype=torch.uint8))
+
+
+def _golden_figures():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "pages_figures.json")) as f:
+        return json.load(f)
+
+
+def test_get_config_heuristic_and_tile_counts():
+    """The heuristic's tiles: 256 x 256 when they fill the CUs (8192^3: 1024 tiles, whole rounds,
+    no tail), else 128 x 128. At 2048^2 that gives 16 x 16 = 256 tiles, the count the Colfax
+    article gives for 128 x 128 tiles (section 'Version 6: 12 MMA Warps'); its 192 x 128 tile is
+    not a shape of this library, so an explicit config asking for it is rejected."""
+    c = nv.get_config(nv.OP_W4A4_TILED, 8192, 8192, 8192, 256)
+    assert (c.kernel, c.tile_m, c.tile_n, c.tail, c.dynamic, c.num_cus, c.source) == \
+        (nv.KERNEL_W4A4_TILES, 256, 256, nv.TAIL_NONE, 0, 256, nv.CONFIG_HEURISTIC)
+    for case in _golden_figures()["tile_counts"]["cases"]:
+        M, N = case["M"], case["N"]
+        if case["tile_m"] == 128 and case["tile_n"] == 128:
+            c = nv.get_config(nv.OP_W4A4_TILED, M, N, 2048, 256)
+            assert (c.tile_m, c.tile_n) == (128, 128)
+            assert -(-M // c.tile_m) * -(-N // c.tile_n) == case["tiles"]
+        else:
+            cfg = nv.make_config(nv.KERNEL_W4A4_TILES, case["tile_m"], case["tile_n"], num_cus=256)
+            assert nv.lib().nvfp4_config_workspace_bytes(nv.OP_W4A4, M, N, 2048, ctypes.byref(cfg)) == 0
+    # a last round of at most half the CUs: quadrants, or a two-way K split when K is long
+    c = nv.get_config(nv.OP_W4A4_TILED, 8192, 16896, 5120, 256)   # 32 x 66 = 2112 tiles, 64 left over
+    assert (c.tail, c.split_k, c.source) == (nv.TAIL_QUADRANTS, 0, nv.CONFIG_HEURISTIC)
+    c = nv.get_config(nv.OP_W4A4_TILED, 8192, 5376, 17408, 256)   # 32 x 21 = 672 tiles, 160 left over
+    assert c.tail == nv.TAIL_NONE
+    c = nv.get_config(nv.OP_W4A4_TILED, 8192, 4608, 16384, 256)   # 32 x 18 = 576 tiles, 64 left over
+    assert (c.tail, c.split_k) == (nv.TAIL_SPLIT, 2)
+    c = nv.get_config(nv.OP_W4A16, 1, 5120, 5120, 256)
+    assert c.kernel == nv.KERNEL_W4A16_DECODE
+    c = nv.get_config(nv.OP_W4A16, 32, 5120, 5120, 256)
+    assert c.kernel == nv.KERNEL_W4A16_SKINNY
+    c = nv.get_config(nv.OP_W4A16, 1024, 34816, 5120, 256)
+    assert (c.kernel, c.tile_m, c.tile_n) == (nv.KERNEL_W4A16_TILES, 256, 256)
+
+
+def test_tuned_table_is_per_cu_count():
+    """A tuned entry applies only on the CU count it was measured on (TileLang PR #3290,
+    'Tests': the tuned table is not applied on another SM count)."""
+    # 34816 x 5120 at M = 384: 128 x 256 tiles measured 20 % faster than the heuristic's 256 x 256
+    tuned = nv.get_config(nv.OP_W4A16, 384, 34816, 5120, 256)
+    heur = nv.get_config(nv.OP_W4A16, 384, 34816, 5120, -256)
+    assert tuned.source == nv.CONFIG_TUNED and tuned.num_cus == 256
+    assert (tuned.kernel, tuned.tile_m, tuned.tile_n) == (nv.KERNEL_W4A16_TILES, 128, 256)
+    assert heur.source == nv.CONFIG_HEURISTIC and (heur.tile_m, heur.tile_n) == (256, 256)
+    for cus in (304, 255, 80):
+        c = nv.get_config(nv.OP_W4A16, 384, 34816, 5120, cus)
+        assert c.source == nv.CONFIG_HEURISTIC and c.num_cus == cus
+    # outside an entry's M range the heuristic applies on 256 CUs too
+    assert nv.get_config(nv.OP_W4A16, 128, 34816, 5120, 256).source == nv.CONFIG_HEURISTIC
+
+
+def test_configs_are_valid_for_every_shape():
+    """Every config the library picks, for M = 1 .. 1024 on the decode layer shapes and the
+    square sizes and on three CU counts, is one its own check accepts (a positive workspace
+    size whenever the op needs one, and the same size through both queries)."""
+    L = nv.lib()
+    shapes = [(6144, 5120), (5120, 5120), (34816, 5120), (5120, 17408), (2048, 2048), (8192, 8192)]
+    for cus in (256, 304, 80):
+        for N, K in shapes:
+            for M in (1, 2, 3, 4, 5, 8, 16, 17, 32, 33, 64, 65, 96, 128, 200, 256, 384, 512, 1000, 1024):
+                for op in (nv.OP_W4A16, nv.OP_W4A4_TILED, nv.OP_W4A4):
+                    c = nv.get_config(op, M, N, K, cus)
+                    assert c.num_cus == cus
+                    n = L.nvfp4_config_workspace_bytes(op, M, N, K, ctypes.byref(c))
+                    if op == nv.OP_W4A4:
+                        assert n >= L.nvfp4_tiled_activation_bytes(M, K) > 0, (op, M, N, K, cus)
+                    if c.tail == nv.TAIL_SPLIT:
+                        assert n >= c.split_k * 256 * 256 * 4 > 0
+
+
+def test_explicit_config_checks():
+    L = nv.lib()
+    ws = L.nvfp4_config_workspace_bytes
+
+    def w(op, M, N, K, **kw):
+        return ws(op, M, N, K, ctypes.byref(nv.make_config(**kw)))
+    # W4A4: 256 or 128 square tiles; tails and the dynamic schedule need 256 x 256 tiles
+    assert w(nv.OP_W4A4_TILED, 4096, 4096, 4096, tile_m=256, tile_n=256, num_cus=256) == 0   # nothing to hold
+    assert w(nv.OP_W4A4_TILED, 4096, 4096, 4096, tile_m=256, tile_n=256, dynamic=1, num_cus=256) == 256
+    assert w(nv.OP_W4A4_TILED, 2048, 2048, 2048, tile_m=256, tile_n=256, tail=nv.TAIL_SPLIT, split_k=4,
+             num_cus=256) == 64 * 4 * 256 * 256 * 4
+    assert w(nv.OP_W4A4_TILED, 2048, 2048, 2048, tile_m=128, tile_n=128, tail=nv.TAIL_SPLIT, split_k=4,
+             num_cus=256) == 0
+    assert w(nv.OP_W4A4_TILED, 2048, 2048, 2048, tile_m=128, tile_n=128, dynamic=1, num_cus=256) == 0
+    assert w(nv.OP_W4A4_TILED, 2048, 2048, 2048, tile_m=256, tile_n=256, tail=nv.TAIL_SPLIT, split_k=33,
+             num_cus=256) == 0      # more ranges than K chunks
+    assert w(nv.OP_W4A4_TILED, 2048, 2048, 2048, tile_m=256, tile_n=128, num_cus=256) == 0
+    assert w(nv.OP_W4A4_TILED, 2048, 2048, 2048, kernel=nv.KERNEL_W4A16_TILES, tile_m=256, tile_n=256,
+             num_cus=256) == 0
+    # W4A16: the decode kernel while x fits its LDS, skinny up to M = 64, three tile shapes
+    assert w(nv.OP_W4A16, 5, 5120, 5120, kernel=nv.KERNEL_W4A16_DECODE, num_cus=256) == 0
+    assert w(nv.OP_W4A16, 65, 5120, 5120, kernel=nv.KERNEL_W4A16_SKINNY, num_cus=256) == 0
+    assert w(nv.OP_W4A16, 24, 5120, 5120, kernel=nv.KERNEL_W4A16_SKINNY, num_cus=256) == 32 * 5120 * 2
+    assert w(nv.OP_W4A16, 1, 5120, 5120, kernel=nv.KERNEL_W4A16_TILES, tile_m=256, tile_n=128, num_cus=256) == 0
+    assert w(nv.OP_W4A16, 1, 5120, 5120, kernel=nv.KERNEL_AUTO, num_cus=256) == 0
+    assert w(nv.OP_W4A16, 1, 5120, 5120, kernel=nv.KERNEL_W4A16_TILES, tile_m=128, tile_n=128, num_cus=256) > 0

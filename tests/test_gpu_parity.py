@@ -4,6 +4,7 @@ Byte outputs (prepared weights, quantized codes and scales, g) must match
 bit for bit; GEMM outputs must lie inside the stated FP32 / BF16 error bound
 of the exact result (tests/gpu_helpers.py). All inputs are seeded (synth.py).
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -229,12 +230,120 @@ def test_w4a4_last_round_quadrants_same_bits():
     wp, _ = _prep(b[:N], sb[:N])
     wpw, _ = _prep(b, sb)
     A, SA = dev(a), dev(sa)
-    out = nv.nvfp4_gemm_w4a4(A, SA, wp, N, K, 0.63, None, "bf16")
+    quads = nv.make_config(nv.KERNEL_W4A4_TILES, 256, 256, nv.TAIL_QUADRANTS)
+    out = nv.nvfp4_gemm_w4a4(A, SA, wp, N, K, 0.63, None, "bf16", config=quads)
     wide = nv.nvfp4_gemm_w4a4(A, SA, wpw, Nw, K, 0.63, None, "bf16")
     torch.cuda.synchronize()
     assert torch.equal(out, wide[:, :N]), "quadrant launch must give the T = 4 kernel's bits"
     D, S = oracle_w4a4_exact_blocked(a, sa, b[:N], sb[:N], 0.63)
     assert_close(host(out), D, S, bf16=True, what=f"last-round quadrants {M}x{N}x{K}")
+
+
+_W4A4_CONFIGS = {
+    "none": dict(tile_m=256, tile_n=256),
+    "quadrants": dict(tile_m=256, tile_n=256, tail=nv.TAIL_QUADRANTS),
+    "split2": dict(tile_m=256, tile_n=256, tail=nv.TAIL_SPLIT, split_k=2),
+    "split7": dict(tile_m=256, tile_n=256, tail=nv.TAIL_SPLIT, split_k=7),
+    "none_dynamic": dict(tile_m=256, tile_n=256, dynamic=1),
+    "split3_dynamic": dict(tile_m=256, tile_n=256, tail=nv.TAIL_SPLIT, split_k=3, dynamic=1),
+    "tiles128": dict(tile_m=128, tile_n=128),
+}
+
+
+@pytest.fixture(scope="module")
+def _w4a4_config_case():
+    """4000 x 4192 x 1088: 16 x 17 = 272 tiles of 256 x 256, ragged in both directions, K = 17
+    chunks (so split ranges are unequal: 8 / 9 chunks, or 2-3 of 7)."""
+    M, N, K = 4000, 4192, 1088
+    a, sa = _random_nvfp4(171, M, K)
+    b, sb = _random_nvfp4(172, N, K)
+    wp, _ = _prep(b, sb)
+    ac = _alpha_col(173, N)
+    D, S = oracle_w4a4_exact_blocked(a, sa, b, sb, gemm.column_alpha(0.83, ac))
+    return dict(M=M, N=N, K=K, A=dev(a), SA=dev(sa), wp=wp, ac=dev(ac), D=D, S=S)
+
+
+@pytest.mark.parametrize("name", list(_W4A4_CONFIGS))
+def test_w4a4_explicit_configs(_w4a4_config_case, name):
+    """Every schedule the W4A4 config can ask for (TileLang PR #3290, "Tests": explicit configs),
+    with a per-column alpha, FP32 out: the tail as one more round, as quadrants, or split along K
+    with a fixed-order fix-up (row "split-K partials + fixed-order reduce"), and the dynamic
+    (atomic-counter) schedule; each within the bound of the exact result and bit-identical on
+    repeat. Schedules that run every element's MFMA sequence unchanged give the bits of the
+    plain one."""
+    c = _w4a4_config_case
+    cfg = nv.make_config(nv.KERNEL_W4A4_TILES, **_W4A4_CONFIGS[name])
+    run = lambda cf: nv.nvfp4_gemm_w4a4(c["A"], c["SA"], c["wp"], c["N"], c["K"], 0.83, None, "f32",
+                                         alpha_col=c["ac"], config=cf)
+    out, again = run(cfg), run(cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), "repeat calls must be bit-identical"
+    if name in ("none", "quadrants", "none_dynamic"):
+        plain = run(nv.make_config(nv.KERNEL_W4A4_TILES, **_W4A4_CONFIGS["none"]))
+        torch.cuda.synchronize()
+        assert torch.equal(out, plain)
+    assert_close(host(out), c["D"], c["S"], bf16=False, what=f"w4a4 config {name}")
+
+
+def test_w4a4_all_tiles_split_2048():
+    """2048^3 with every one of its 64 256 x 256 tiles split into 4 K ranges (no whole tile:
+    the 256 work units are all ranges) and the BF16 epilogue in the fix-up; full check."""
+    S = 2048
+    xa, xb = synth.square_normal(S, "A"), synth.square_normal(S, "B")
+    a, sa, gA, _ = quantize.quantize(xa)
+    b, sb, gB, _ = quantize.quantize(xb)
+    alpha = alpha_ab(gA, gB)
+    wp, _ = _prep(b, sb, "ue4m3")
+    cfg = nv.make_config(nv.KERNEL_W4A4_TILES, 256, 256, nv.TAIL_SPLIT, 4)
+    out = nv.nvfp4_gemm_w4a4(dev(a), dev(sa), wp, S, S, float(alpha), None, "bf16", config=cfg)
+    torch.cuda.synchronize()
+    D, Sabs = oracle_w4a4_exact_blocked(a, sa, b, sb, alpha)
+    assert_close(host(out), D, Sabs, bf16=True, what="2048^3 all tiles split")
+
+
+def test_w4a4_config_errors():
+    """Invalid explicit configs return NVFP4_ERR_VALUE (ValueError) before any launch; an explicit
+    K-split without a workspace returns NVFP4_ERR_WORKSPACE."""
+    M, N, K = 256, 256, 128
+    a, sa = _random_nvfp4(5, M, K)
+    b, sb = _random_nvfp4(6, N, K)
+    wp, _ = _prep(b, sb)
+    A, SA = dev(a), dev(sa)
+    bad = [dict(tile_m=256, tile_n=128), dict(tile_m=192, tile_n=192), dict(tile_m=128, tile_n=128, dynamic=1),
+           dict(tile_m=256, tile_n=256, tail=nv.TAIL_SPLIT, split_k=1),
+           dict(tile_m=256, tile_n=256, tail=nv.TAIL_SPLIT, split_k=3),           # K has 2 chunks
+           dict(tile_m=256, tile_n=256, tail=7), dict(kernel=nv.KERNEL_W4A16_SKINNY, tile_m=256, tile_n=256)]
+    for kw in bad:
+        kw = dict(kernel=nv.KERNEL_W4A4_TILES, **kw) if "kernel" not in kw else kw
+        cfg = nv.make_config(**kw)
+        st = nv.lib().nvfp4_gemm_w4a4(nv._ptr(A), nv._ptr(SA), nv._ptr(wp), M, N, K, 1.0, None, None,
+                                      nv._ptr(torch.empty(1, device="cuda")), nv.OUT_F32, N, ctypes.byref(cfg),
+                                      nv._ptr(torch.empty(1 << 20, dtype=torch.uint8, device="cuda")), 1 << 20,
+                                      None)
+        assert st == nv.ERR_VALUE, kw
+    at = nv.nvfp4_tile_activation(A, SA)
+    split = nv.make_config(nv.KERNEL_W4A4_TILES, 256, 256, nv.TAIL_SPLIT, 2)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    st = nv.lib().nvfp4_gemm_w4a4_tiled(nv._ptr(at), nv._ptr(wp), M, N, K, 1.0, None, None, nv._ptr(out), nv.OUT_F32,
+                                        N, ctypes.byref(split), None, 0, None)
+    assert st == nv.ERR_WORKSPACE
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,N,K,kernel,tile", [
+    (1, 320, 640, nv.KERNEL_W4A16_SKINNY, (0, 0)), (3, 320, 640, nv.KERNEL_W4A16_TILES, (128, 128)),
+    (4, 4160, 2048, nv.KERNEL_W4A16_DECODE, (0, 0)), (20, 4160, 2048, nv.KERNEL_W4A16_TILES, (128, 256)),
+    (64, 2080, 1024, nv.KERNEL_W4A16_TILES, (256, 256)), (100, 2080, 1024, nv.KERNEL_W4A16_TILES, (128, 128)),
+    (300, 8224, 640, nv.KERNEL_W4A16_TILES, (128, 256)), (40, 8224, 640, nv.KERNEL_W4A16_SKINNY, (0, 0))])
+def test_w4a16_explicit_configs(M, N, K, kernel, tile):
+    """Each W4A16 kernel forced on shapes where the heuristic picks another (TileLang PR #3290,
+    "Tests": explicit configs): full check against the oracle."""
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 3 + N + K)
+    cfg = nv.make_config(kernel, tile[0], tile[1])
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha, config=cfg)
+    torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"w4a16 config {kernel} {tile} M={M}")
 
 
 @pytest.mark.parametrize("M,K", [(64, 128), (77, 320), (1, 64)])
@@ -728,29 +837,39 @@ def test_w4a16_graph_capture_replay_matches_eager():
         assert torch.equal(out, eager)
 
 
+@pytest.mark.parametrize("mode", ["no_workspace", "split", "split_dynamic"])
 @pytest.mark.parametrize("two_pass", [False, True])
-def test_prefill_graph_capture_replay_matches_eager(two_pass):
+def test_prefill_graph_capture_replay_matches_eager(two_pass, mode):
     """The prefill step (on-device quantize into the tile layout, then the W4A4 GEMM with the
     device 1/gA) captured once in a graph and replayed on new activations: every replay the
-    same bits as eager calls. 4000 x 4192 x 256: 256 x 256 tiles plus the last round as
-    quadrants (two GEMM launches), one- and two-pass."""
+    same bits as eager calls. 4000 x 4192 x 256 (K = 512 two-pass): 256 x 256 tiles plus a last
+    round of 16 tiles, run as quadrants (the library's choice without a workspace: two GEMM
+    launches), split along K with the fix-up (two launches), or split with the dynamic schedule
+    (counter reset, GEMM, fix-up: three launches); one- and two-pass."""
     M, N, K = 4000, 4192, 256
     b, sb = _random_nvfp4(91, N, K, -3, 3)
     wp, _ = _prep(b, sb)
     quant = nv.nvfp4_quantize_two_pass_tiled if two_pass else nv.nvfp4_quantize_tiled
     gemm_fn = nv.nvfp4_gemm_w4a4_two_pass_tiled if two_pass else nv.nvfp4_gemm_w4a4_tiled
+    Kc = 2 * K if two_pass else K
+    cfg = None
+    if mode != "no_workspace":
+        cfg = nv.make_config(nv.KERNEL_W4A4_TILES, 256, 256, nv.TAIL_SPLIT, 2, dynamic=int(mode == "split_dynamic"))
+    gws = None
+    if mode != "no_workspace":
+        gws = torch.empty(nv.workspace_bytes(nv.OP_W4A4_TILED, M, N, Kc, cfg), dtype=torch.uint8, device="cuda")
     xd = dev(synth.normal_bf16(92, M, K)).view(torch.bfloat16).clone()
     at, g, ig = quant(xd)                                   # buffers, and a warm-up outside capture
     ws = torch.empty(nv.workspace_bytes(nv.OP_QUANTIZE, M, 0, K), dtype=torch.uint8, device="cuda")
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    gemm_fn(at, M, wp, N, K, 0.5, ig, "bf16", out)
+    gemm_fn(at, M, wp, N, K, 0.5, ig, "bf16", out, config=cfg, ws=gws)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     st = torch.cuda.Stream()
     with torch.cuda.stream(st):
         with torch.cuda.graph(graph, stream=st):
             quant(xd, at, g, ig, ws)
-            gemm_fn(at, M, wp, N, K, 0.5, ig, "bf16", out)
+            gemm_fn(at, M, wp, N, K, 0.5, ig, "bf16", out, config=cfg, ws=gws)
     torch.cuda.synchronize()
     for rep in range(3):
         xn = dev(synth.normal_bf16(930 + rep, M, K)).view(torch.bfloat16)
@@ -758,7 +877,7 @@ def test_prefill_graph_capture_replay_matches_eager(two_pass):
         graph.replay()
         torch.cuda.synchronize()
         at2, _, ig2 = quant(xn)
-        eager = gemm_fn(at2, M, wp, N, K, 0.5, ig2, "bf16")
+        eager = gemm_fn(at2, M, wp, N, K, 0.5, ig2, "bf16", config=cfg, ws=gws)
         torch.cuda.synchronize()
         assert torch.equal(at, at2) and torch.equal(ig, ig2)
         assert torch.equal(out, eager), f"replay {rep}"
