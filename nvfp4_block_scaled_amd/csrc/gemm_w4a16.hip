@@ -412,16 +412,31 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
 // with NG full 32 x 32 MT partial tiles; the waves are added in a fixed tree
 // (W/2 + W/2, ..., 1 + 1) through LDS. W = 8 waves, or 16 when there are
 // fewer row groups than CUs (more loads in flight on each busy CU; measured
-// 17 % faster at M = 8 on 5120 x 17408, slower on 34816 x 5120).
+// 17 % faster at M = 8 on 5120 x 17408, slower on 34816 x 5120). This
+// fragment kernel serves 16 < M <= 64, and M <= 16 only when the row kernel
+// below cannot address x with 32-bit offsets.
 constexpr int kSkAhead = 1;   // tiles per wave and ring batch
 
-static int skinny_waves(int64_t N, int cus) { return N / 32 < cus ? 16 : 8; }
-
-// Row groups per workgroup with 8 waves: each x fragment a wave loads then
-// feeds NG MFMAs, so x is read from L2 by groups / NG workgroups (34816 x 5120:
-// M = 16 from 43.2 to 35.5 us, M = 64 from 61.6 to 58.1 us; four groups per
-// workgroup, at 116+ registers, left too few workgroups resident).
-constexpr int kSkinnyNG = 2;
+// Launch shape of the skinny kernels: W waves, NG row groups per workgroup,
+// and RP > 0 (x rows padded to RP = 8 or 16) for the kernel that
+// stages x rows through LDS and dequantizes per scale block (M <= 16), 0 for
+// the kernel with x fragments in registers (M <= 64). Measured on the 27B-class
+// layer shapes (graph replays, one box): at M = 8 the row kernel took
+// 6144 x 5120 from 9.6 to 6.9 us, 5120 x 17408 from 22.7 to 15.9 us and
+// 34816 x 5120 from 31.2 to 23.1 us; at M = 24 and 32 it measured no faster
+// than the fragment kernel with its x copy (its 16 per-block multiplies per
+// step outweigh the saved conversions), so that kernel keeps M > 16.
+struct SkinnyShape {
+  int W, NG, RP;
+};
+static SkinnyShape skinny_shape(int64_t M, int64_t N, int cus) {
+  const int64_t groups = N / 32;
+  const int RP = M <= 8 ? 8 : M <= 16 ? 16 : 0;
+  if (groups < cus) return {16, 1, RP};
+  return {8, groups % 2 == 0 ? 2 : 1, RP};
+}
+// Register-ring stages of the row kernel (deeper rings measured slower).
+constexpr int kSkinnyRowsDepth = 2;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   bf16x8_t b;
@@ -554,6 +569,145 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
           const int64_t m = 32 * mt + 8 * (j >> 2) + 4 * h + (j & 3);
           if (m < M) y[m * ldy + n] = f32_to_bf16_rne(an * acc[q][mt][j]);
         }
+    }
+  }
+}
+
+// The skinny contraction for M <= RP <= 16 without barriers: wave w takes the
+// tiles w, w + W, ... through a D-deep register ring, as the direct skinny
+// kernel does, and stages each tile's x (RP rows x 64 columns, one coalesced
+// 16-byte load per lane and RP / 8 pieces) through a private LDS slot: the
+// wave writes the tile into its slot in fragment order and reads its four
+// fragments back (LDS operations of one wave complete in order, so no barrier
+// is needed, and the next tile's write cannot pass the reads). The texture
+// path then moves the RP real rows of x (1 KB per tile for RP = 8) instead of
+// 32 rows of fragments. Dequantization: one MFMA per 16-element scale block
+// (a lane-half swap of the code dwords gives every lane block b's 8 codes for
+// its half), with the power of two of the block scale folded into the
+// conversion (exact) and its mantissa (frexp, in [0.5, 1)) applied to that
+// block's MFMA result in the rows < RP; the factor 2 is applied at the end.
+template <int W, int NG, int RP, int D>
+__global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                                  const uint8_t *__restrict__ wp, int64_t M, int64_t N,
+                                                                  int64_t K, float alpha, const float *alpha_dev,
+                                                                  const float *alpha_col, uint16_t *__restrict__ y,
+                                                                  int64_t ldy) {
+  constexpr int JR = RP / 2;                  // accumulator registers of rows < RP
+  constexpr int SLOT = RP * 128;              // a tile's x fragments: 4 blocks x 2 halves x RP rows x 16 B
+  constexpr int PPL = RP / 8;                 // 16-byte x pieces per lane and tile
+  constexpr int LDS_F = W * SLOT / 4;         // the x slots, then one row group's partial tiles (JR * 64 floats per wave)
+  __shared__ __attribute__((aligned(16))) float lds[LDS_F];
+  const int64_t T = K / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int h = lane >> 5, r = lane & 31;
+  const int64_t g0 = (int64_t)blockIdx.x * NG;
+  const uint8_t *cb = wp + ((g0 * T) << 10);
+  const uint8_t *sb = wp + N * K / 2 + ((g0 * T) << 7);
+  const uint32_t oc = (uint32_t)lane * 16u, os = (uint32_t)r * 4u;
+  // one resource per row group and kind, ending at the group's last tile: the
+  // offsets of tiles past it fall outside the range and read zero
+  __amdgpu_buffer_rsrc_t rc[NG], rs[NG];
+#pragma unroll
+  for (int q = 0; q < NG; q++) {
+    rc[q] = make_rsrc16(cb + ((q * T) << 10), T << 10);
+    rs[q] = make_rsrc16(sb + ((q * T) << 7), T << 7);
+  }
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, M * ldx * 2);   // rows >= M read zero
+  uint8_t *slot = reinterpret_cast<uint8_t *>(lds) + wave * SLOT;
+  uint32_t xgo[PPL], xlo[PPL];
+#pragma unroll
+  for (int i = 0; i < PPL; i++) {
+    const int m = 8 * i + (lane >> 3), pc = lane & 7;   // row, 8-column piece of the tile
+    xgo[i] = (uint32_t)(((int64_t)m * ldx + 8 * pc) * 2);
+    xlo[i] = (uint32_t)((pc >> 1) * (2 * RP * 16) + ((pc & 1) * RP + m) * 16);   // step = 16-block, half
+  }
+  const uint32_t frag = (uint32_t)((h * RP + (r & (RP - 1))) * 16);
+  struct Stage {
+    u32x4_t cw[NG];
+    uint32_t sw[NG];
+    u32x4_t xg[PPL];
+  };
+  auto issue = [&](Stage &st, int64_t t) {
+    const uint32_t tc = t < T ? (uint32_t)t : (uint32_t)T;   // T: the first offset past the range
+#pragma unroll
+    for (int q = 0; q < NG; q++) {
+      st.cw[q] = __builtin_amdgcn_raw_buffer_load_b128(rc[q], oc + (tc << 10), 0, kNonTemporal);
+      st.sw[q] = __builtin_amdgcn_raw_buffer_load_b32(rs[q], os + (tc << 7), 0, kNonTemporal);
+    }
+    const uint32_t xt = (uint32_t)((t < T ? t : T - 1) * 128);
+#pragma unroll
+    for (int i = 0; i < PPL; i++) st.xg[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xgo[i] + xt, 0, 0);
+  };
+  float acc[NG][JR];
+#pragma unroll
+  for (int q = 0; q < NG; q++)
+#pragma unroll
+    for (int jj = 0; jj < JR; jj++) acc[q][jj] = 0.0f;
+  auto compute = [&](const Stage &st) {
+#pragma unroll
+    for (int i = 0; i < PPL; i++) *reinterpret_cast<u32x4_t *>(slot + xlo[i]) = st.xg[i];
+    u32x4_t xv[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) xv[b] = *reinterpret_cast<const u32x4_t *>(slot + b * (2 * RP * 16) + frag);
+#pragma unroll
+    for (int q = 0; q < NG; q++) {
+      const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st.sw[q], 1.0f, false);
+      const f32x2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st.sw[q], 1.0f, true);
+      const float sc[4] = {s01[0], s01[1], s23[0], s23[1]};
+      const auto p02 = __builtin_amdgcn_permlane32_swap(st.cw[q][0], st.cw[q][1], false, false);
+      const auto p13 = __builtin_amdgcn_permlane32_swap(st.cw[q][2], st.cw[q][3], false, false);
+      const uint32_t bw[4] = {p02[0], p13[0], p02[1], p13[1]};
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+        const bf16x2_t w2[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[b], sc[b], 0),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[b], sc[b], 1),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[b], sc[b], 2),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[b], sc[b], 3)};
+        bf16x8_t bv;
+        __builtin_memcpy(&bv, w2, 16);
+        const f32x16_t rb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xv[b]), bv, f32x16_t{}, 0, 0, 0);
+        const float mb = __builtin_amdgcn_frexp_mantf(sc[b]);
+#pragma unroll
+        for (int jj = 0; jj < JR; jj++) acc[q][jj] = __builtin_fmaf(mb, rb[jj], acc[q][jj]);
+      }
+    }
+  };
+  Stage stg[D];
+#pragma unroll
+  for (int d = 0; d < D; d++) issue(stg[d], wave + (int64_t)d * W);
+  const int64_t nt = wave < T ? (T - wave + W - 1) / W : 0;   // this wave's tiles
+  int64_t i = 0;
+  for (; i + D <= nt; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+      compute(stg[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(stg[d], wave + (i + d + D) * W);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D - 1; d++)
+    if (i + d < nt) compute(stg[d]);
+  // per row group: the waves' partial tiles (rows < RP) to LDS, then every
+  // thread adds its elements over the waves in order
+  const float al = load_alpha(alpha, alpha_dev);
+#pragma unroll
+  for (int q = 0; q < NG; q++) {
+    __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < JR; jj++) lds[(wave * JR + jj) * 64 + lane] = acc[q][jj];
+    __syncthreads();
+    for (int e = threadIdx.x; e < JR * 64; e += W * 64) {
+      const int jj = e / 64, l = e % 64;
+      const int64_t m = 8 * (jj >> 2) + 4 * (l >> 5) + (jj & 3);
+      if (m >= M) continue;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; w++) v += lds[(w * JR + jj) * 64 + l];
+      const int64_t n = (g0 + q) * 32 + (l & 31);
+      // 2: the frexp mantissas lie in [0.5, 1)
+      y[m * ldy + n] = f32_to_bf16_rne(col_alpha(al, alpha_col, n) * (2.0f * v));
     }
   }
 }
@@ -1256,33 +1410,50 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   } else if (plan.kind == 3) {
     if (plan.grid_x > 0x7FFFFFFF || M * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
     const int MT = M <= 32 ? 1 : 2;
-    const bool xf_path = M > w4a16::kSkinnyDirectMaxM;
+    w4a16::SkinnyShape sh = w4a16::skinny_shape(M, N, cfg.num_cus);
+    if (sh.RP != 0 && (((int64_t)32 * ldx + K + 64 * sh.W) * 2 > 0xFFFFFFFFll || K / 64 * 1024 > 0x7FFFFFFFll))
+      sh.RP = 0;   // 32-bit x and weight offsets
+    const bool xf_path = sh.RP == 0 && M > w4a16::kSkinnyDirectMaxM;
+    if (xf_path && (int64_t)MT * 64 * K > 0x7FFFFFFFll) return NVFP4_ERR_SHAPE;   // 32-bit fragment offsets
     uint8_t *xf = static_cast<uint8_t *>(ws);
     if (xf_path) {
       hipLaunchKernelGGL(w4a16::tile_x_kernel, dim3((unsigned)(K / 64 * MT)), dim3(256), 0, s, x, ldx, M, K, MT,
                          reinterpret_cast<u32x4_t *>(xf));
       NVFP4_LAUNCH_CHECK();
     }
-    const unsigned grid = (unsigned)plan.grid_x;
-    const int W = w4a16::skinny_waves(N, cfg.num_cus);
-#define NVFP4_SKINNY(MTV, XFV, WV, NGV)                                                                         \
-  hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV, WV, NGV>), dim3(grid / NGV), dim3(WV * 64), 0, s, x, ldx,     \
-                     w_prep, M, N, K, alpha, alpha_dev, alpha_col, y, ldy, xf)
-    const bool ng = W == 8 && plan.grid_x % w4a16::kSkinnyNG == 0;
-    if (W == 16) {
-      if (!xf_path) NVFP4_SKINNY(1, false, 16, 1);
-      else if (MT == 1) NVFP4_SKINNY(1, true, 16, 1);
-      else NVFP4_SKINNY(2, true, 16, 1);
-    } else if (ng) {
-      if (!xf_path) NVFP4_SKINNY(1, false, 8, w4a16::kSkinnyNG);
-      else if (MT == 1) NVFP4_SKINNY(1, true, 8, w4a16::kSkinnyNG);
-      else NVFP4_SKINNY(2, true, 8, w4a16::kSkinnyNG);
-    } else {
-      if (!xf_path) NVFP4_SKINNY(1, false, 8, 1);
-      else if (MT == 1) NVFP4_SKINNY(1, true, 8, 1);
-      else NVFP4_SKINNY(2, true, 8, 1);
+    const unsigned grid = (unsigned)(plan.grid_x / sh.NG);
+    if (sh.RP > 0) {
+#define NVFP4_SKINNY_ROWS(WV, NGV, RPV)                                                                          \
+  if (sh.W == WV && sh.NG == NGV && sh.RP == RPV) {                                                              \
+    hipLaunchKernelGGL((w4a16::skinny_rows_kernel<WV, NGV, RPV, w4a16::kSkinnyRowsDepth>), dim3(grid),           \
+                       dim3(WV * 64), 0, s, x, ldx, w_prep, M, N, K, alpha, alpha_dev, alpha_col, y, ldy);      \
+  } else
+      NVFP4_SKINNY_ROWS(16, 1, 8)
+      NVFP4_SKINNY_ROWS(16, 1, 16)
+      NVFP4_SKINNY_ROWS(8, 2, 8)
+      NVFP4_SKINNY_ROWS(8, 2, 16)
+      NVFP4_SKINNY_ROWS(8, 1, 8)
+      NVFP4_SKINNY_ROWS(8, 1, 16)
+      return NVFP4_ERR_SHAPE;
+#undef NVFP4_SKINNY_ROWS
+      NVFP4_LAUNCH_CHECK();
+      return NVFP4_OK;
     }
+#define NVFP4_SKINNY_X(WV, NGV, MTV, XFV)                                                                      \
+  hipLaunchKernelGGL((w4a16::skinny_kernel<MTV, XFV, WV, NGV>), dim3(grid), dim3(WV * 64), 0, s, x, ldx,           \
+                     w_prep, M, N, K, alpha, alpha_dev, alpha_col, y, ldy, xf)
+#define NVFP4_SKINNY(WV, NGV)                                                                                  \
+  if (sh.W == WV && sh.NG == NGV) {                                                                            \
+    if (!xf_path) NVFP4_SKINNY_X(WV, NGV, 1, false);                                                          \
+    else if (MT == 1) NVFP4_SKINNY_X(WV, NGV, 1, true);                                                       \
+    else NVFP4_SKINNY_X(WV, NGV, 2, true);                                                                    \
+  } else
+    NVFP4_SKINNY(16, 1)
+    NVFP4_SKINNY(8, 2)
+    NVFP4_SKINNY(8, 1)
+    return NVFP4_ERR_SHAPE;
 #undef NVFP4_SKINNY
+#undef NVFP4_SKINNY_X
   }
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;

@@ -813,6 +813,37 @@ def test_w4a16_zero_negative_scales_and_strided_out():
     assert (host(big[:, N:]) == 0).all()
 
 
+@pytest.mark.parametrize("M", [5, 8, 16])
+@pytest.mark.parametrize("N", [96, 17408])
+def test_w4a16_row_kernel_scale_edges(M, N):
+    """M <= 16 runs the row kernel, which folds the power of two of each block scale into the
+    code conversion and multiplies the block's MFMA result by the scale's frexp mantissa:
+    zero, negative and -0 scales, every E4M3 subnormal, the largest normal (448) against the
+    largest codes, and a NaN scale byte (its column must come out NaN in every row). 3 row
+    groups (16 waves each) and 544 (8 waves, two groups per workgroup)."""
+    K = 256
+    b, sb = _random_nvfp4(91 + M, N, K)
+    codes = synth.random_codes(92 + M, N, K)
+    codes[3] = np.where(np.arange(K) % 2 == 0, 0x7, 0xF)        # +-6 against scale 448
+    b = formats.pack_nibbles(codes)
+    sb[0, :] = 0x00
+    sb[1, :] |= 0x80                                             # negative scales
+    sb[2, :] = np.arange(K // 16) % 7 + 1                         # subnormals 0x01 .. 0x07
+    sb[3, :] = 0x7E
+    sb[4, 1] = 0x7F                                              # NaN in block 1 of row 4
+    sb[5, :] = 0x80                                              # -0
+    sb[6, :] = np.arange(K // 16) % 2 + 0x07                     # largest subnormal / smallest normal
+    x = synth.normal_bf16(93 + M, M, K)
+    wp, bad = _prep(b, sb)
+    assert bad == 1
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, 0.37)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.isnan(got[:, 4]).all(), "a NaN scale must make its column NaN"
+    y, S = gemm.w4a16(x, b, sb, 0.37)
+    assert_close(got, y, S, bf16=True, what=f"row kernel scale edges M={M} N={N}")
+
+
 def test_w4a16_graph_capture_replay_matches_eager():
     M, N, K = 1, 5120, 5120
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, 77)
