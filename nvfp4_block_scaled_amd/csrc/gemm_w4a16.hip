@@ -958,11 +958,17 @@ __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t
   scales_of<T>(f[0], sc);
   read_x<T>(smem, 0, wm, a);
   deq_w<T>(f[0], sc, 0, b);
-  for (int64_t c = 0; c < n; c += 3) {
+  // chunks in threes (the register ring's period), then the one or two left:
+  // padding the range to a multiple of three ran up to two all-zero chunks
+  // (a 16-chunk K range took 18)
+  int64_t c = 0;
+  for (; c + 3 <= n; c += 3) {
     chunk<0, T>(tb, p.ldx, ow, ows, c, n, f, sc, smem, wm, a, b, acc);
     chunk<1, T>(tb, p.ldx, ow, ows, c + 1, n, f, sc, smem, wm, a, b, acc);
     chunk<2, T>(tb, p.ldx, ow, ows, c + 2, n, f, sc, smem, wm, a, b, acc);
   }
+  if (c < n) chunk<0, T>(tb, p.ldx, ow, ows, c, n, f, sc, smem, wm, a, b, acc);
+  if (c + 1 < n) chunk<1, T>(tb, p.ldx, ow, ows, c + 1, n, f, sc, smem, wm, a, b, acc);
 }
 
 // The main loop with x read straight into registers from its fragment-order
@@ -1082,11 +1088,14 @@ __device__ __forceinline__ void tile_mainloop_d(const Params &p, int tile, int64
   load_w<TN>(tb, ow, ows, 1, n, f[1]);
   scales_of<TN>(f[0], sc);
   deq_w<TN>(f[0], sc, 0, b);
-  for (int64_t c = 0; c < n; c += 3) {
+  int64_t c = 0;   // chunks in threes, then the one or two left (as in tile_mainloop)
+  for (; c + 3 <= n; c += 3) {
     chunk_d<0, TM, TN>(tb, rx, ox, p.xmt, ow, ows, c, n, f, sc, xr, b, acc);
     chunk_d<1, TM, TN>(tb, rx, ox, p.xmt, ow, ows, c + 1, n, f, sc, xr, b, acc);
     chunk_d<2, TM, TN>(tb, rx, ox, p.xmt, ow, ows, c + 2, n, f, sc, xr, b, acc);
   }
+  if (c < n) chunk_d<0, TM, TN>(tb, rx, ox, p.xmt, ow, ows, c, n, f, sc, xr, b, acc);
+  if (c + 1 < n) chunk_d<1, TM, TN>(tb, rx, ox, p.xmt, ow, ows, c + 1, n, f, sc, xr, b, acc);
 }
 
 // Epilogue of a whole tile: per wave 32 x 32TN staging of BF16 in LDS (after
