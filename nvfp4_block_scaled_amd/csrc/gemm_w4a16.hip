@@ -60,7 +60,11 @@ struct DecodeShape {
 constexpr DecodeShape kDecodeShapes[] = {{32, 8, 2}, {32, 12, 2}};
 constexpr int kDecodeWavesPerCu = 32;   // resident waves per CU at M = 1 (at most 64 registers)
 
-constexpr int kDecodeMaxM = 4;
+constexpr int kDecodeMaxM = 4;          // the decode kernel's instantiations (explicit configs)
+// The heuristic's decode range: from M = 3 the skinny row kernel is faster on
+// the 27B-class layers (graph replays, M = 4: 34816 x 5120 31.6 -> 23.3 us,
+// 6144 x 5120 8.7 -> 6.7 us; M = 2: decode 20.9 against 23.8 us).
+constexpr int kDecodeDefaultMaxM = 2;
 constexpr int kSkinnyMaxM = 64;
 constexpr int kSkinnyDirectMaxM = 16;   // up to here the skinny kernel reads x rows directly
 constexpr int kDecodeLdsBytes = 64 * 1024;  // x staged in LDS: M * K * 2 bytes at most
@@ -1294,7 +1298,7 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
 void w4a16_default_config(int64_t M, int64_t N, int64_t K, int cus, nvfp4_config *c) {
   *c = nvfp4_config{};
   c->num_cus = cus;
-  if (w4a16::decode_fits(M, K)) {
+  if (w4a16::decode_fits(M, K) && M <= w4a16::kDecodeDefaultMaxM) {
     c->kernel = NVFP4_KERNEL_W4A16_DECODE;
   } else if (M <= w4a16::kSkinnyMaxM) {
     c->kernel = NVFP4_KERNEL_W4A16_SKINNY;

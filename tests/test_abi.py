@@ -260,6 +260,8 @@ def test_get_config_heuristic_and_tile_counts():
     assert (c.tail, c.split_k) == (nv.TAIL_SPLIT, 2)
     c = nv.get_config(nv.OP_W4A16, 1, 5120, 5120, 256)
     assert c.kernel == nv.KERNEL_W4A16_DECODE
+    assert nv.get_config(nv.OP_W4A16, 2, 5120, 5120, 256).kernel == nv.KERNEL_W4A16_DECODE
+    assert nv.get_config(nv.OP_W4A16, 3, 5120, 5120, 256).kernel == nv.KERNEL_W4A16_SKINNY   # the row kernel
     c = nv.get_config(nv.OP_W4A16, 32, 5120, 5120, 256)
     assert c.kernel == nv.KERNEL_W4A16_SKINNY
     c = nv.get_config(nv.OP_W4A16, 1024, 34816, 5120, 256)

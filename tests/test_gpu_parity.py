@@ -605,9 +605,11 @@ def test_w4a16_wide_decode(M, N, K):
     including a K that leaves the last tile batch partly empty; full check. With
     256 CUs and M = 1, one whole round of 1024 workgroups runs first and the groups
     left over are cut: 34048 rows (40 left) into 8-row workgroups, 35968 (100 left)
-    into 16-row ones; 36896 (129 left) and 65536 (two whole rounds) are not cut."""
+    into 16-row ones; 36896 (129 left) and 65536 (two whole rounds) are not cut. The decode
+    kernel is asked for explicitly: from M = 3 the library's own choice is the skinny kernel."""
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 7 + N)
-    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha,
+                              config=nv.make_config(nv.KERNEL_W4A16_DECODE))
     torch.cuda.synchronize()
     y, S = gemm.w4a16(x, b, sb, alpha)
     assert_close(host(out), y, S, bf16=True, what=f"wide decode M={M} {N}x{K}")
@@ -641,10 +643,12 @@ def test_w4a16_big_ragged(M, N, K):
 @pytest.mark.parametrize("M,K", [(4, 8192), (2, 16384), (1, 32768)])
 def test_w4a16_decode_largest_lds(M, K):
     """The decode kernel stages x in LDS up to M * K * 2 = 64 KiB: the largest (M, K) at each
-    M that still takes the decode path, with a few hundred weight rows; full check."""
+    M that still takes the decode path (asked for explicitly), with a few hundred weight rows;
+    full check."""
     N = 320
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 13 + K)
-    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
+    out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha,
+                              config=nv.make_config(nv.KERNEL_W4A16_DECODE))
     torch.cuda.synchronize()
     y, S = gemm.w4a16(x, b, sb, alpha)
     assert_close(host(out), y, S, bf16=True, what=f"decode LDS edge M={M} K={K}")
