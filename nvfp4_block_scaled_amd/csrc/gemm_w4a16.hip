@@ -618,14 +618,23 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
   }
   const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, M * ldx * 2);   // rows >= M read zero
   uint8_t *slot = reinterpret_cast<uint8_t *>(lds) + wave * SLOT;
+  // Lane piece: row m, 8 columns 8 pc of the tile, pc = 2 b + hh for 16-block b
+  // and k-half hh; in fragment order it is unit (b, hh, m). Within each group
+  // of 8 units (8 rows of one b, hh) the unit index is XORed with pc, so the 8
+  // lanes that write one row's 128 bytes, and the 8 lanes that read a fragment,
+  // hit 8 distinct 16-byte bank groups (unswizzled, the writes conflicted ~10
+  // cycles per LDS instruction).
   uint32_t xgo[PPL], xlo[PPL];
 #pragma unroll
   for (int i = 0; i < PPL; i++) {
     const int m = 8 * i + (lane >> 3), pc = lane & 7;   // row, 8-column piece of the tile
     xgo[i] = (uint32_t)(((int64_t)m * ldx + 8 * pc) * 2);
-    xlo[i] = (uint32_t)((pc >> 1) * (2 * RP * 16) + ((pc & 1) * RP + m) * 16);   // step = 16-block, half
+    xlo[i] = (uint32_t)((pc >> 1) * (2 * RP * 16) + ((pc & 1) * RP + (m ^ pc)) * 16);
   }
-  const uint32_t frag = (uint32_t)((h * RP + (r & (RP - 1))) * 16);
+  uint32_t frag[4];
+#pragma unroll
+  for (int b = 0; b < 4; b++)
+    frag[b] = (uint32_t)((b * 2 * RP + h * RP + ((r & (RP - 1)) ^ (2 * b + h))) * 16);
   struct Stage {
     u32x4_t cw[NG];
     uint32_t sw[NG];
@@ -652,7 +661,7 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
     for (int i = 0; i < PPL; i++) *reinterpret_cast<u32x4_t *>(slot + xlo[i]) = st.xg[i];
     u32x4_t xv[4];
 #pragma unroll
-    for (int b = 0; b < 4; b++) xv[b] = *reinterpret_cast<const u32x4_t *>(slot + b * (2 * RP * 16) + frag);
+    for (int b = 0; b < 4; b++) xv[b] = *reinterpret_cast<const u32x4_t *>(slot + frag[b]);
 #pragma unroll
     for (int q = 0; q < NG; q++) {
       const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st.sw[q], 1.0f, false);
