@@ -156,6 +156,34 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K, const nvfp4_config &c) {
 // roundup32(M) rows x K BF16.
 static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 32 * 32) * (size_t)K * 2; }
 
+// Launch shape of the skinny kernels: W waves, NG row groups per workgroup,
+// and RP > 0 (x rows padded to RP = 8, 16, 32 or 64) for the row kernel, which
+// stages x rows through LDS, or RP = 0 for the fragment kernel, which reads a
+// fragment-order copy of x from the workspace (or, for M <= 16, x directly).
+// The row kernel needs no workspace: rows >= M read whatever in-range bytes
+// their 32-bit offsets reach (or zero) and only feed output rows that are not
+// stored, and rows < M stay below the M ldx 2 bytes the dispatch bounds.
+// Measured on the 27B-class layer shapes (graph replays, one box), fragment
+// kernel with its copy -> row kernel:
+//   M = 8:  6144 x 5120 9.6 -> 6.5 us, 5120 x 17408 22.7 -> 15.5 us, 34816 x 5120 31.2 -> 23.3 us;
+//   M = 17: 13.0 -> 9.1 us, 30.5 -> 21.6 us, 36.1 -> 29.5 us;
+//   M = 33: 17.7 -> 13.0 us, 44.2 -> 33.0 us, 50.9 -> 46.9 us.
+// With two row groups per workgroup the RP = 64 kernel holds 190 registers
+// (one workgroup per CU) and loses at M = 64 on 34816 x 5120 (55.4 against
+// 52.0 us), so weights with at least as many row groups as CUs keep the
+// fragment kernel above M = 48.
+struct SkinnyShape {
+  int W, NG, RP;
+};
+static SkinnyShape skinny_shape(int64_t M, int64_t N, int64_t K, int cus) {
+  const int64_t groups = N / 32;
+  int RP = M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 0;
+  if (RP == 64 && groups >= cus && M > 48) RP = 0;
+  if (K / 64 * 1024 > 0x7FFFFFFFll) RP = 0;   // the row kernel's 32-bit weight offsets
+  if (groups < cus) return {RP == 64 ? 8 : 16, 1, RP};
+  return {8, groups % 2 == 0 ? 2 : 1, RP};
+}
+
 // Schedule of the big kernel (tile shapes: big_tile_shape).
 //  * 256 x 256 tiles (one workgroup per CU): G = CUs persistent workgroups
 //    each run full / G whole tiles; the rem = total - full tiles left over are
@@ -233,7 +261,8 @@ static int64_t big_xmt(const BigSched &b) { return b.TM * b.TN >= 8 ? b.tiles_m 
 static size_t big_xf_bytes(const BigSched &b, int64_t K) { return (size_t)big_xmt(b) * 32 * (size_t)K * 2; }
 
 static size_t workspace_for(const Plan &p, const nvfp4_config &c, int64_t M, int64_t N, int64_t K) {
-  if (p.kind == 3) return M > kSkinnyDirectMaxM ? skinny_x_bytes(M, K) : 0;
+  if (p.kind == 3)
+    return M > kSkinnyDirectMaxM && skinny_shape(M, N, K, c.num_cus).RP == 0 ? skinny_x_bytes(M, K) : 0;
   if (p.kind == 4) {
     const BigSched b = big_sched(M, N, K, c);
     return big_partials_span(b) + big_xf_bytes(b, K);
@@ -413,32 +442,15 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(const uint16_t *__restri
 // check). Weights and x fragments are loaded one tile per wave ahead (a
 // two-tile register ring): the x fragments cost 16 MT registers per tile, and
 // deeper rings lowered the occupancy enough to measure slower. Each wave ends
-// with NG full 32 x 32 MT partial tiles; the waves are added in a fixed tree
-// (W/2 + W/2, ..., 1 + 1) through LDS. W = 8 waves, or 16 when there are
-// fewer row groups than CUs (more loads in flight on each busy CU; measured
-// 17 % faster at M = 8 on 5120 x 17408, slower on 34816 x 5120). This
-// fragment kernel serves 16 < M <= 64, and M <= 16 only when the row kernel
-// below cannot address x with 32-bit offsets.
+// with NG full 32 x 32 MT partial tiles; they are added in wave order through
+// LDS, one output tile at a time (a fixed tree of 4 levels with 8 barriers
+// cost ~1 us more per call). W = 8 waves, or 16 when there are fewer row
+// groups than CUs (more loads in flight on each busy CU; measured 17 % faster
+// at M = 8 on 5120 x 17408, slower on 34816 x 5120). This fragment kernel
+// serves 48 < M <= 64 on weights with at least as many row groups as CUs, and
+// otherwise only K beyond the row kernel's 32-bit weight offsets.
 constexpr int kSkAhead = 1;   // tiles per wave and ring batch
 
-// Launch shape of the skinny kernels: W waves, NG row groups per workgroup,
-// and RP > 0 (x rows padded to RP = 8 or 16) for the kernel that
-// stages x rows through LDS and dequantizes per scale block (M <= 16), 0 for
-// the kernel with x fragments in registers (M <= 64). Measured on the 27B-class
-// layer shapes (graph replays, one box): at M = 8 the row kernel took
-// 6144 x 5120 from 9.6 to 6.9 us, 5120 x 17408 from 22.7 to 15.9 us and
-// 34816 x 5120 from 31.2 to 23.1 us; at M = 24 and 32 it measured no faster
-// than the fragment kernel with its x copy (its 16 per-block multiplies per
-// step outweigh the saved conversions), so that kernel keeps M > 16.
-struct SkinnyShape {
-  int W, NG, RP;
-};
-static SkinnyShape skinny_shape(int64_t M, int64_t N, int cus) {
-  const int64_t groups = N / 32;
-  const int RP = M <= 8 ? 8 : M <= 16 ? 16 : 0;
-  if (groups < cus) return {16, 1, RP};
-  return {8, groups % 2 == 0 ? 2 : 1, RP};
-}
 // Register-ring stages of the row kernel (deeper rings measured slower).
 constexpr int kSkinnyRowsDepth = 2;
 
@@ -472,7 +484,7 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
                                                              uint16_t *__restrict__ y, int64_t ldy,
                                                              const uint8_t *__restrict__ xf) {
   constexpr int U = kSkAhead;                          // tiles per wave per batch
-  __shared__ f32x16_t red[W / 2][NG][MT][64];
+  __shared__ float red[W * 16 * 64];                   // one output tile of every wave
   const int64_t T = K / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, r = lane & 31;
@@ -544,59 +556,60 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
     issue(b0, t0 + 2 * step);
     compute(b1, t0 + step);
   }
-  // fixed-order tree over the waves' partial tiles (W/2 + W/2, ..., 1 + 1)
+  // per output tile: every wave's partial tile to LDS (element j of lane l at
+  // (wave * 16 + j) * 64 + l, so each store and load of a wave is one
+  // contiguous 256 bytes), then every thread adds its elements over the waves
+  // in wave order
+  const float al = load_alpha(alpha, alpha_dev);
 #pragma unroll
-  for (int half = W / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half)
+  for (int q = 0; q < NG; q++) {
+    const int64_t n = (g0 + q) * 32 + r;
 #pragma unroll
-      for (int q = 0; q < NG; q++)
+    for (int mt = 0; mt < MT; mt++) {
+      __syncthreads();
 #pragma unroll
-        for (int mt = 0; mt < MT; mt++) red[wave - half][q][mt][lane] = acc[q][mt];
-    __syncthreads();
-    if (wave < half)
+      for (int j = 0; j < 16; j++) red[(wave * 16 + j) * 64 + lane] = acc[q][mt][j];
+      __syncthreads();
 #pragma unroll
-      for (int q = 0; q < NG; q++)
+      for (int e = wave; e < 16; e += W) {   // e: the accumulator element this wave adds up
+        const int64_t m = 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+        float v = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; mt++) acc[q][mt] += red[wave][q][mt][lane];
-    __syncthreads();
-  }
-  if (wave == 0) {
-    const float al = load_alpha(alpha, alpha_dev);
-#pragma unroll
-    for (int q = 0; q < NG; q++) {
-      const int64_t n = (g0 + q) * 32 + r;
-      const float an = col_alpha(al, alpha_col, n);
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const int64_t m = 32 * mt + 8 * (j >> 2) + 4 * h + (j & 3);
-          if (m < M) y[m * ldy + n] = f32_to_bf16_rne(an * acc[q][mt][j]);
-        }
+        for (int w = 0; w < W; w++) v += red[(w * 16 + e) * 64 + lane];
+        if (m < M) y[m * ldy + n] = f32_to_bf16_rne(col_alpha(al, alpha_col, n) * v);
+      }
     }
   }
 }
 
-// The skinny contraction for M <= RP <= 16 without barriers: wave w takes the
-// tiles w, w + W, ... through a D-deep register ring, as the direct skinny
-// kernel does, and stages each tile's x (RP rows x 64 columns, one coalesced
-// 16-byte load per lane and RP / 8 pieces) through a private LDS slot: the
-// wave writes the tile into its slot in fragment order and reads its four
+// The skinny contraction for M <= RP <= 64 without barriers in the main loop:
+// wave w takes the tiles w, w + W, ... through a D-deep register ring, as the
+// direct skinny kernel does, and stages each tile's x (RP rows x 64 columns,
+// RP / 8 coalesced 16-byte loads per lane) through a private LDS slot: the
+// wave writes the tile into its slot in fragment order and reads its
 // fragments back (LDS operations of one wave complete in order, so no barrier
 // is needed, and the next tile's write cannot pass the reads). The texture
 // path then moves the RP real rows of x (1 KB per tile for RP = 8) instead of
-// 32 rows of fragments. Dequantization: one MFMA per 16-element scale block
-// (a lane-half swap of the code dwords gives every lane block b's 8 codes for
-// its half), with the power of two of the block scale folded into the
-// conversion (exact) and its mantissa (frexp, in [0.5, 1)) applied to that
-// block's MFMA result in the rows < RP; the factor 2 is applied at the end.
+// 32 rows of fragments, and no copy of x is made. The slot's 16-byte units
+// are XOR-swizzled within each run of 8 rows, so the stores of one row's
+// 128 bytes and the loads of a fragment each hit 8 distinct bank groups.
+// Dequantization, RP <= 16: one MFMA per 16-element scale block (a lane-half
+// swap of the code dwords gives every lane block b's 8 codes for its half),
+// with the power of two of the block scale folded into the conversion (exact)
+// and its mantissa (frexp, in [0.5, 1)) applied to that block's MFMA result in
+// the rows < RP; the factor 2 is applied at the end. RP = 32 and 64: the
+// codes are dequantized exactly to BF16 (E2M1 -> FP32, times the scale) and
+// the MFMAs of the RP / 32 x tiles accumulate, as in the fragment kernel (16
+// per-block multiplies for 32 rows outweigh the saved conversions).
 template <int W, int NG, int RP, int D>
 __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__restrict__ x, int64_t ldx,
                                                                   const uint8_t *__restrict__ wp, int64_t M, int64_t N,
                                                                   int64_t K, float alpha, const float *alpha_dev,
                                                                   const float *alpha_col, uint16_t *__restrict__ y,
                                                                   int64_t ldy) {
-  constexpr int JR = RP / 2;                  // accumulator registers of rows < RP
+  constexpr bool FULL = RP >= 32;             // full dequantization, MFMAs accumulate
+  constexpr int MTR = FULL ? RP / 32 : 1;     // 32-row x tiles
+  constexpr int JR = FULL ? 16 : RP / 2;      // accumulator registers per x tile holding rows < RP
   constexpr int SLOT = RP * 128;              // a tile's x fragments: 4 blocks x 2 halves x RP rows x 16 B
   constexpr int PPL = RP / 8;                 // 16-byte x pieces per lane and tile
   constexpr int LDS_F = W * SLOT / 4;         // the x slots, then one row group's partial tiles (JR * 64 floats per wave)
@@ -631,10 +644,18 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
     xgo[i] = (uint32_t)(((int64_t)m * ldx + 8 * pc) * 2);
     xlo[i] = (uint32_t)((pc >> 1) * (2 * RP * 16) + ((pc & 1) * RP + (m ^ pc)) * 16);
   }
-  uint32_t frag[4];
+  uint32_t frag[MTR][4];
 #pragma unroll
-  for (int b = 0; b < 4; b++)
-    frag[b] = (uint32_t)((b * 2 * RP + h * RP + ((r & (RP - 1)) ^ (2 * b + h))) * 16);
+  for (int mt = 0; mt < MTR; mt++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      if constexpr (FULL) {   // step s = b: k = 32 h + 8 s, unit (2 h + s / 2, s % 2, 32 mt + r)
+        frag[mt][b] =
+            (uint32_t)(((2 * h + (b >> 1)) * 2 * RP + (b & 1) * RP + ((32 * mt + r) ^ (4 * h + b))) * 16);
+      } else {
+        frag[mt][b] = (uint32_t)((b * 2 * RP + h * RP + ((r & (RP - 1)) ^ (2 * b + h))) * 16);
+      }
+    }
   struct Stage {
     u32x4_t cw[NG];
     uint32_t sw[NG];
@@ -651,17 +672,33 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
 #pragma unroll
     for (int i = 0; i < PPL; i++) st.xg[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xgo[i] + xt, 0, 0);
   };
-  float acc[NG][JR];
+  f32x16_t acc[NG][MTR];
 #pragma unroll
   for (int q = 0; q < NG; q++)
 #pragma unroll
-    for (int jj = 0; jj < JR; jj++) acc[q][jj] = 0.0f;
+    for (int mt = 0; mt < MTR; mt++) acc[q][mt] = f32x16_t{};
   auto compute = [&](const Stage &st) {
 #pragma unroll
     for (int i = 0; i < PPL; i++) *reinterpret_cast<u32x4_t *>(slot + xlo[i]) = st.xg[i];
-    u32x4_t xv[4];
+    u32x4_t xv[MTR][4];
 #pragma unroll
-    for (int b = 0; b < 4; b++) xv[b] = *reinterpret_cast<const u32x4_t *>(slot + frag[b]);
+    for (int mt = 0; mt < MTR; mt++)
+#pragma unroll
+      for (int b = 0; b < 4; b++) xv[mt][b] = *reinterpret_cast<const u32x4_t *>(slot + frag[mt][b]);
+    if constexpr (FULL) {
+#pragma unroll
+      for (int q = 0; q < NG; q++) {
+        const f32x2_t sc = e4m3x2_to_f32(st.sw[q] >> (16 * h));
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          const bf16x8_t bv = dequant8_bf16(st.cw[q][s], sc[s >> 1]);
+#pragma unroll
+          for (int mt = 0; mt < MTR; mt++)
+            acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xv[mt][s]), bv, acc[q][mt], 0, 0, 0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NG; q++) {
       const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st.sw[q], 1.0f, false);
@@ -678,10 +715,10 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
                                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[b], sc[b], 3)};
         bf16x8_t bv;
         __builtin_memcpy(&bv, w2, 16);
-        const f32x16_t rb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xv[b]), bv, f32x16_t{}, 0, 0, 0);
+        const f32x16_t rb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xv[0][b]), bv, f32x16_t{}, 0, 0, 0);
         const float mb = __builtin_amdgcn_frexp_mantf(sc[b]);
 #pragma unroll
-        for (int jj = 0; jj < JR; jj++) acc[q][jj] = __builtin_fmaf(mb, rb[jj], acc[q][jj]);
+        for (int jj = 0; jj < JR; jj++) acc[q][0][jj] = __builtin_fmaf(mb, rb[jj], acc[q][0][jj]);
       }
     }
   };
@@ -702,27 +739,29 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
 #pragma unroll
   for (int d = 0; d < D - 1; d++)
     if (i + d < nt) compute(stg[d]);
-  // per row group: the waves' partial tiles (rows < RP) to LDS, then every
-  // thread adds its elements over the waves in order
+  // per row group and x tile: the waves' partial tiles (rows < RP) to LDS,
+  // then every thread adds its elements over the waves in order
   const float al = load_alpha(alpha, alpha_dev);
 #pragma unroll
-  for (int q = 0; q < NG; q++) {
-    __syncthreads();
+  for (int q = 0; q < NG; q++)
 #pragma unroll
-    for (int jj = 0; jj < JR; jj++) lds[(wave * JR + jj) * 64 + lane] = acc[q][jj];
-    __syncthreads();
-    for (int e = threadIdx.x; e < JR * 64; e += W * 64) {
-      const int jj = e / 64, l = e % 64;
-      const int64_t m = 8 * (jj >> 2) + 4 * (l >> 5) + (jj & 3);
-      if (m >= M) continue;
-      float v = 0.0f;
+    for (int mt = 0; mt < MTR; mt++) {
+      __syncthreads();
 #pragma unroll
-      for (int w = 0; w < W; w++) v += lds[(w * JR + jj) * 64 + l];
-      const int64_t n = (g0 + q) * 32 + (l & 31);
-      // 2: the frexp mantissas lie in [0.5, 1)
-      y[m * ldy + n] = f32_to_bf16_rne(col_alpha(al, alpha_col, n) * (2.0f * v));
+      for (int jj = 0; jj < JR; jj++) lds[(wave * JR + jj) * 64 + lane] = acc[q][mt][jj];
+      __syncthreads();
+      for (int e = threadIdx.x; e < JR * 64; e += W * 64) {
+        const int jj = e / 64, l = e % 64;
+        const int64_t m = 32 * mt + 8 * (jj >> 2) + 4 * (l >> 5) + (jj & 3);
+        if (m >= M) continue;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; w++) v += lds[(w * JR + jj) * 64 + l];
+        const int64_t n = (g0 + q) * 32 + (l & 31);
+        // 2: the frexp mantissas lie in [0.5, 1)
+        y[m * ldy + n] = f32_to_bf16_rne(col_alpha(al, alpha_col, n) * (FULL ? v : 2.0f * v));
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------- big MFMA kernel (M > 64)
@@ -1432,9 +1471,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   } else if (plan.kind == 3) {
     if (plan.grid_x > 0x7FFFFFFF || M * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
     const int MT = M <= 32 ? 1 : 2;
-    w4a16::SkinnyShape sh = w4a16::skinny_shape(M, N, cfg.num_cus);
-    if (sh.RP != 0 && (((int64_t)32 * ldx + K + 64 * sh.W) * 2 > 0xFFFFFFFFll || K / 64 * 1024 > 0x7FFFFFFFll))
-      sh.RP = 0;   // 32-bit x and weight offsets
+    const w4a16::SkinnyShape sh = w4a16::skinny_shape(M, N, K, cfg.num_cus);
     const bool xf_path = sh.RP == 0 && M > w4a16::kSkinnyDirectMaxM;
     if (xf_path && (int64_t)MT * 64 * K > 0x7FFFFFFFll) return NVFP4_ERR_SHAPE;   // 32-bit fragment offsets
     uint8_t *xf = static_cast<uint8_t *>(ws);
@@ -1456,6 +1493,11 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
       NVFP4_SKINNY_ROWS(8, 2, 16)
       NVFP4_SKINNY_ROWS(8, 1, 8)
       NVFP4_SKINNY_ROWS(8, 1, 16)
+      NVFP4_SKINNY_ROWS(16, 1, 32)
+      NVFP4_SKINNY_ROWS(8, 2, 32)
+      NVFP4_SKINNY_ROWS(8, 1, 32)
+      NVFP4_SKINNY_ROWS(8, 2, 64)
+      NVFP4_SKINNY_ROWS(8, 1, 64)
       return NVFP4_ERR_SHAPE;
 #undef NVFP4_SKINNY_ROWS
       NVFP4_LAUNCH_CHECK();

@@ -173,12 +173,19 @@ def test_workspace_sizes():
     assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 33, 64, 128) == 64 * 128 * 9 // 16
     assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 0, 64, 128) == 0
     assert L.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 0, 5120) >= 4
-    # W4A16 (no device here: the plan assumes 256 CUs). Decode (M <= 4) needs none; the
-    # skinny kernel's x copy for 16 < M <= 64 is 32 rows x K BF16.
+    # W4A16 (no device here: the plan assumes 256 CUs). Decode (M <= 4) and the row kernel
+    # (M <= 64, M <= 48 on weights of >= 256 row groups) need none; the fragment kernel's x
+    # copy is roundup32(M) rows x K BF16.
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1, 34816, 5120) == 0
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 4, 34816, 5120) == 0
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 16, 34816, 5120) == 0
-    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 24, 17408, 4160) == 32 * 4160 * 2
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 24, 17408, 4160) == 0
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 48, 34816, 5120) == 0
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 64, 5120, 17408) == 0       # 160 row groups
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 49, 34816, 5120) == 64 * 5120 * 2
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 64, 8192, 5120) == 64 * 5120 * 2   # 256 row groups
+    # K past the row kernel's 32-bit weight offsets: the fragment kernel and its copy
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 24, 64, (1 << 27) + 64) == 32 * ((1 << 27) + 64) * 2
     # M = 128 on 34816 x 5120: 136 tiles of 128 x 256, all split over 256 workgroups (two
     # 128 KiB partial slots each), then x for one 128-row tile in fragment order
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 128, 34816, 5120) == 256 * 2 * 128 * 1024 + 128 * 5120 * 2
@@ -325,7 +332,9 @@ def test_explicit_config_checks():
     # W4A16: the decode kernel while x fits its LDS, skinny up to M = 64, three tile shapes
     assert w(nv.OP_W4A16, 5, 5120, 5120, kernel=nv.KERNEL_W4A16_DECODE, num_cus=256) == 0
     assert w(nv.OP_W4A16, 65, 5120, 5120, kernel=nv.KERNEL_W4A16_SKINNY, num_cus=256) == 0
-    assert w(nv.OP_W4A16, 24, 5120, 5120, kernel=nv.KERNEL_W4A16_SKINNY, num_cus=256) == 32 * 5120 * 2
+    assert w(nv.OP_W4A16, 24, 5120, 5120, kernel=nv.KERNEL_W4A16_SKINNY, num_cus=256) == 0      # row kernel
+    assert w(nv.OP_W4A16, 56, 5120, 5120, kernel=nv.KERNEL_W4A16_SKINNY, num_cus=256) == 0      # 160 groups < CUs
+    assert w(nv.OP_W4A16, 56, 5120, 5120, kernel=nv.KERNEL_W4A16_SKINNY, num_cus=64) == 64 * 5120 * 2  # fragment
     assert w(nv.OP_W4A16, 1, 5120, 5120, kernel=nv.KERNEL_W4A16_TILES, tile_m=256, tile_n=128, num_cus=256) == 0
     assert w(nv.OP_W4A16, 1, 5120, 5120, kernel=nv.KERNEL_AUTO, num_cus=256) == 0
     assert w(nv.OP_W4A16, 1, 5120, 5120, kernel=nv.KERNEL_W4A16_TILES, tile_m=128, tile_n=128, num_cus=256) > 0

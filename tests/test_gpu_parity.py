@@ -583,13 +583,15 @@ def test_w4a16_small_shapes(M, N, K):
     assert_close(host(out), y, S, bf16=True, what=f"w4a16 M={M} {N}x{K}")
 
 
-@pytest.mark.parametrize("M", [6, 16, 24, 40, 64])
+@pytest.mark.parametrize("M", [6, 16, 24, 33, 40, 48, 49, 64])
 @pytest.mark.parametrize("N,K", [(17408, 4160), (17440, 1088), (2048, 8192)])
 def test_w4a16_skinny_long_k(M, N, K):
-    """4 < M <= 64 with many tiles per wave; full check. M <= 16 reads x rows directly
-    (rows >= M zero), 24 and 40 / 64 read the fragment-order copy with one or two x
-    tiles. 544 row groups: 8 waves per workgroup, two groups each, 65 tiles over the
-    waves. 545 groups (odd): 8 waves, one group each. 64 groups: 16 waves, 8 tiles each."""
+    """4 < M <= 64 with many tiles per wave; full check. The row kernel stages x rows through
+    LDS, padded to 8, 16, 32 or 64 (rows >= M zero); on 544 and 545 row groups (at least one
+    per CU) M = 49 and 64 run the fragment kernel on its fragment-order copy of x (two x
+    tiles), on 64 groups the row kernel. 544 row groups: 8 waves per workgroup, two groups
+    each, 65 tiles over the waves. 545 groups (odd): 8 waves, one group each. 64 groups: 16
+    waves (8 at 64 padded rows), 8 or 16 tiles each."""
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M * 7 + N + K)
     out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
     torch.cuda.synchronize()
@@ -817,14 +819,15 @@ def test_w4a16_zero_negative_scales_and_strided_out():
     assert (host(big[:, N:]) == 0).all()
 
 
-@pytest.mark.parametrize("M", [5, 8, 16])
+@pytest.mark.parametrize("M", [5, 8, 16, 24, 40])
 @pytest.mark.parametrize("N", [96, 17408])
 def test_w4a16_row_kernel_scale_edges(M, N):
-    """M <= 16 runs the row kernel, which folds the power of two of each block scale into the
-    code conversion and multiplies the block's MFMA result by the scale's frexp mantissa:
-    zero, negative and -0 scales, every E4M3 subnormal, the largest normal (448) against the
-    largest codes, and a NaN scale byte (its column must come out NaN in every row). 3 row
-    groups (16 waves each) and 544 (8 waves, two groups per workgroup)."""
+    """The row kernel at M <= 16 folds the power of two of each block scale into the code
+    conversion and multiplies the block's MFMA result by the scale's frexp mantissa; at
+    M = 24 and 40 (32 and 64 padded rows) it dequantizes in full. Zero, negative and -0
+    scales, every E4M3 subnormal, the largest normal (448) against the largest codes, and a
+    NaN scale byte (its column must come out NaN in every row). 3 row groups (16 waves each,
+    8 at 64 rows) and 544 (8 waves, two groups per workgroup)."""
     K = 256
     b, sb = _random_nvfp4(91 + M, N, K)
     codes = synth.random_codes(92 + M, N, K)
