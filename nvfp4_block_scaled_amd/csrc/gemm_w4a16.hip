@@ -29,6 +29,8 @@
 //    on scheduling.
 #include "common.hpp"
 
+#include <utility>
+
 namespace nvfp4 {
 namespace w4a16 {
 
@@ -792,6 +794,14 @@ namespace big {
 
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
+// Ring depths of the 128 x 128 LDS path when the grid holds one workgroup per
+// CU: W loaded kDeepW - 1 chunks ahead, x kDeepX chunks ahead (3 and 1 with
+// two workgroups per CU, whose registers must fit twice). Measured at M = 128
+// (graph replays, one box): 6144 x 5120 28.6 -> 28.0 us, 5120 x 17408
+// 46.3 -> 45.4 us, and 6144 x 5120 at M = 512 55.3 -> 53.4 us; (6, 3), (4, 2)
+// and (8, 3) were no better.
+constexpr int kDeepW = 6;
+constexpr int kDeepX = 2;
 
 struct Params {
   const uint16_t *x;
@@ -912,19 +922,22 @@ __device__ __forceinline__ void scales_of(const WFrags<T> &f, f32x2_t (&sc)[T]) 
   for (int j = 0; j < T; j++) sc[j] = e4m3x2_to_f32(f.ws[j] >> (16 * h));
 }
 
-// One chunk. f[P] holds chunk c's W, f[(P+1)%3] chunk c + 1's; LDS buffer c & 1
-// holds chunk c's x. On entry (a, b) are step 0's operands and sc chunk c's
-// scales; on exit, chunk c + 1's.
-template <int P, int T>
+// One chunk c, at phase P of the rings: W goes through a DW-chunk register
+// ring (f[c % DW] holds chunk c's fragments, loaded DW - 1 chunks ahead) and x
+// through an XA-chunk register ring (xr[c % XA] receives chunk c + XA, loaded
+// XA chunks ahead) into LDS buffer c & 1 at the end of chunk c - 1. On entry
+// (a, b) are step 0's operands and sc chunk c's scales; on exit, chunk
+// c + 1's.
+template <int P, int T, int DW, int XA>
 __device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uint32_t (&ow)[T],
-                                      const uint32_t (&ows)[T], int64_t c, int64_t nch, WFrags<T> (&f)[3],
-                                      f32x2_t (&sc)[T], uint8_t *smem, int wm, bf16x8_t (&a)[T], bf16x8_t (&b)[T],
-                                      f32x16_t (&acc)[T][T]) {
+                                      const uint32_t (&ows)[T], int64_t c, int64_t nch, WFrags<T> (&f)[DW],
+                                      XRegs<T> (&xr)[XA], f32x2_t (&sc)[T], uint8_t *smem, int wm, bf16x8_t (&a)[T],
+                                      bf16x8_t (&b)[T], f32x16_t (&acc)[T][T]) {
   constexpr int kValu = 16 / T + 1;                 // dequant instructions per MFMA, rounded up
-  XRegs<T> xr;
-  load_x<T>(tb, ldx, c + 1, nch, xr);
+  constexpr int FW = P % DW, FN = (P + 1) % DW;
+  load_x<T>(tb, ldx, c + XA, nch, xr[P % XA]);      // its previous chunk went into LDS at the end of chunk c - 1
   __builtin_amdgcn_sched_barrier(0);   // x first (see above)
-  load_w<T>(tb, ow, ows, c + 2, nch, f[(P + 2) % 3]);
+  load_w<T>(tb, ow, ows, c + DW - 1, nch, f[(P + DW - 1) % DW]);
   uint8_t *cur = smem + (c & 1) * (64 * T * 128);
   uint8_t *nxt = smem + ((c + 1) & 1) * (64 * T * 128);
 #pragma unroll
@@ -932,10 +945,10 @@ __device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uin
     bf16x8_t an[T], bn[T];
     if (s < 3) {
       read_x<T>(cur, s + 1, wm, an);
-      deq_w<T>(f[P], sc, s + 1, bn);
+      deq_w<T>(f[FW], sc, s + 1, bn);
     } else {
-      scales_of<T>(f[(P + 1) % 3], sc);
-      deq_w<T>(f[(P + 1) % 3], sc, 0, bn);
+      scales_of<T>(f[FN], sc);
+      deq_w<T>(f[FN], sc, 0, bn);
     }
 #pragma unroll
     for (int i = 0; i < T; i++)
@@ -955,9 +968,27 @@ __device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uin
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  store_x<T>(nxt, xr);
+  store_x<T>(nxt, xr[(P + 1) % XA]);
   lds_barrier();
   read_x<T>(nxt, 0, wm, a);   // the next chunk's step-0 x, now that it is in LDS
+}
+
+// Chunks c + Q, Q in Qs, while below n (the conditions are uniform over the
+// workgroup, so every wave meets the same barriers).
+template <int T, int DW, int XA, int... Qs>
+__device__ __forceinline__ void chunk_run(std::integer_sequence<int, Qs...>, bool all, const TileBase &tb,
+                                          int64_t ldx, const uint32_t (&ow)[T], const uint32_t (&ows)[T], int64_t c,
+                                          int64_t n, WFrags<T> (&f)[DW], XRegs<T> (&xr)[XA], f32x2_t (&sc)[T],
+                                          uint8_t *smem, int wm, bf16x8_t (&a)[T], bf16x8_t (&b)[T],
+                                          f32x16_t (&acc)[T][T]) {
+  ((all || c + Qs < n ? chunk<Qs, T, DW, XA>(tb, ldx, ow, ows, c + Qs, n, f, xr, sc, smem, wm, a, b, acc) : void()),
+   ...);
+}
+
+constexpr int ring_period(int a, int b) {
+  int p = a;
+  while (p % b != 0) p += a;
+  return p;
 }
 
 __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int &tm, int &tn) {
@@ -973,7 +1004,7 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // Chunks [c0, c0 + n) of tile `tile` into acc (zeroed first). The tile bases
 // are moved to chunk c0, so chunk c of the loop is chunk c0 + c of the tile and
 // the loads past the range are empty.
-template <int T>
+template <int T, int DW, int XA>
 __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t c0, int64_t n, uint8_t *smem,
                                               const uint32_t (&ow)[T], const uint32_t (&ows)[T], int wm,
                                               f32x16_t (&acc)[T][T], int64_t &m0, int64_t &n0) {
@@ -995,32 +1026,32 @@ __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t
   for (int i = 0; i < T; i++)
 #pragma unroll
     for (int j = 0; j < T; j++) acc[i][j] = f32x16_t{};
-  WFrags<T> f[3];
+  WFrags<T> f[DW];
+  XRegs<T> xr[XA];
   f32x2_t sc[T];
   bf16x8_t a[T], b[T];
   __syncthreads();   // the previous tile's waves are done with the LDS buffers
-  {
-    XRegs<T> xr;
-    load_x<T>(tb, p.ldx, 0, n, xr);
-    load_w<T>(tb, ow, ows, 0, n, f[0]);
-    load_w<T>(tb, ow, ows, 1, n, f[1]);
-    store_x<T>(smem, xr);
-  }
+  load_x<T>(tb, p.ldx, 0, n, xr[0]);
+#pragma unroll
+  for (int q = 1; q < XA; q++) load_x<T>(tb, p.ldx, q, n, xr[q]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < DW - 1; q++) load_w<T>(tb, ow, ows, q, n, f[q]);
+  store_x<T>(smem, xr[0]);
   lds_barrier();
   scales_of<T>(f[0], sc);
   read_x<T>(smem, 0, wm, a);
   deq_w<T>(f[0], sc, 0, b);
-  // chunks in threes (the register ring's period), then the one or two left:
-  // padding the range to a multiple of three ran up to two all-zero chunks
-  // (a 16-chunk K range took 18)
+  // chunks in whole periods of the two rings, then the ones left (padding the
+  // range to whole periods ran all-zero chunks: a 16-chunk K range took 18
+  // with the three-chunk period)
+  constexpr int PER = ring_period(DW, XA);
+  using Period = std::make_integer_sequence<int, PER>;
   int64_t c = 0;
-  for (; c + 3 <= n; c += 3) {
-    chunk<0, T>(tb, p.ldx, ow, ows, c, n, f, sc, smem, wm, a, b, acc);
-    chunk<1, T>(tb, p.ldx, ow, ows, c + 1, n, f, sc, smem, wm, a, b, acc);
-    chunk<2, T>(tb, p.ldx, ow, ows, c + 2, n, f, sc, smem, wm, a, b, acc);
-  }
-  if (c < n) chunk<0, T>(tb, p.ldx, ow, ows, c, n, f, sc, smem, wm, a, b, acc);
-  if (c + 1 < n) chunk<1, T>(tb, p.ldx, ow, ows, c + 1, n, f, sc, smem, wm, a, b, acc);
+  for (; c + PER <= n; c += PER)
+    chunk_run<T, DW, XA>(Period{}, true, tb, p.ldx, ow, ows, c, n, f, xr, sc, smem, wm, a, b, acc);
+  chunk_run<T, DW, XA>(std::make_integer_sequence<int, PER - 1>{}, false, tb, p.ldx, ow, ows, c, n, f, xr, sc, smem,
+                       wm, a, b, acc);
 }
 
 // The main loop with x read straight into registers from its fragment-order
@@ -1200,8 +1231,8 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
 // registers (tile_mainloop_d).
 // COLS: p.alpha_col is set (a separate instantiation, so that the kernel
 // without a per-column scale keeps its registers for the main loop).
-template <int TM, int TN, int WGM, bool COLS>
-__global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Params p) {
+template <int TM, int TN, int WGM, bool COLS, bool DEEP>
+__global__ __launch_bounds__(kThreads, TM * TN >= 8 || DEEP ? 1 : 2) void big_kernel(Params p) {
   constexpr bool kLds = TM == 2 && TN == 2;
   constexpr int WGN = 4 / WGM;
   // LDS path: two x chunks; direct paths: the epilogue's BF16 staging
@@ -1223,7 +1254,7 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Par
   int64_t m0, n0;
   for (int tile = pid; tile < p.full; tile += G) {
     if constexpr (kLds)
-      tile_mainloop<2>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
+      tile_mainloop<2, DEEP ? kDeepW : 3, DEEP ? kDeepX : 1>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
     else
       tile_mainloop_d<TM, TN, WGM>(p, tile, 0, nch, ow, ows, wm, acc, m0, n0);
     tile_epilogue<TM, TN, COLS>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
@@ -1234,7 +1265,8 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 ? 1 : 2) void big_kernel(Par
     for (int seg = 0; s < e; seg++) {
       const int64_t rho = s / nch, c0 = s - rho * nch, c1 = min(nch, c0 + (e - s));
       if constexpr (kLds)
-        tile_mainloop<2>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm, acc, m0, n0);
+        tile_mainloop<2, DEEP ? kDeepW : 3, DEEP ? kDeepX : 1>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm,
+                                                               acc, m0, n0);
       else
         tile_mainloop_d<TM, TN, WGM>(p, p.full + (int)rho, c0, c1 - c0, ow, ows, wm, acc, m0, n0);
       float *dst = p.partials + ((int64_t)pid * 2 + seg) * partial_floats<TM, TN>() +
@@ -1334,6 +1366,25 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
       if (m < p.M && col < p.N) p.y[m * p.ldy + col] = f32_to_bf16_rne(ac * v[u][k]);
     }
   }
+}
+
+// The tile kernel's instantiations: per-column alpha or not, and for the
+// 128 x 128 LDS path the deep rings when the grid holds one workgroup per CU.
+template <int TM, int TN, int WGM>
+static void launch_big(bool one_per_cu, bool cols, unsigned grid, hipStream_t s, const Params &bp) {
+  if constexpr (TM * TN < 8) {
+    if (one_per_cu) {
+      if (cols)
+        hipLaunchKernelGGL((big_kernel<TM, TN, WGM, true, true>), dim3(grid), dim3(kThreads), 0, s, bp);
+      else
+        hipLaunchKernelGGL((big_kernel<TM, TN, WGM, false, true>), dim3(grid), dim3(kThreads), 0, s, bp);
+      return;
+    }
+  }
+  if (cols)
+    hipLaunchKernelGGL((big_kernel<TM, TN, WGM, true, false>), dim3(grid), dim3(kThreads), 0, s, bp);
+  else
+    hipLaunchKernelGGL((big_kernel<TM, TN, WGM, false, false>), dim3(grid), dim3(kThreads), 0, s, bp);
 }
 
 }  // namespace big
@@ -1449,12 +1500,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
                           (int)b.full, (int)b.rem, static_cast<float *>(ws), xf, (int)xmt};
     const unsigned grid = (unsigned)b.G, fix_grid = (unsigned)(b.rem * b.TM * b.TN);
 #define NVFP4_BIG(TMV, TNV, WGMV)                                                                                \
-  if (alpha_col)                                                                                                 \
-    hipLaunchKernelGGL((w4a16::big::big_kernel<TMV, TNV, WGMV, true>), dim3(grid), dim3(w4a16::big::kThreads), 0, s, \
-                       bp);                                                                                      \
-  else                                                                                                           \
-    hipLaunchKernelGGL((w4a16::big::big_kernel<TMV, TNV, WGMV, false>), dim3(grid), dim3(w4a16::big::kThreads), 0,   \
-                       s, bp);                                                                                   \
+  w4a16::big::launch_big<TMV, TNV, WGMV>(b.G <= cfg.num_cus, alpha_col != nullptr, grid, s, bp);                 \
   if (b.rem > 0) {                                                                                               \
     NVFP4_LAUNCH_CHECK();                                                                                        \
     hipLaunchKernelGGL((w4a16::big::big_fixup_kernel<TMV, TNV, WGMV>), dim3(fix_grid), dim3(w4a16::big::kThreads), \

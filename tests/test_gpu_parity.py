@@ -851,28 +851,43 @@ def test_w4a16_row_kernel_scale_edges(M, N):
     assert_close(got, y, S, bf16=True, what=f"row kernel scale edges M={M} N={N}")
 
 
-def test_w4a16_graph_capture_replay_matches_eager():
-    M, N, K = 1, 5120, 5120
-    x, b, sb, wp, alpha = _w4a16_case(M, N, K, 77)
+@pytest.mark.parametrize("M,N,K,tile", [(1, 5120, 5120, None), (128, 6144, 5120, (128, 128)),
+                                        (256, 8192, 1024, (128, 256)), (512, 8192, 512, (256, 256))])
+def test_w4a16_graph_capture_replay_matches_eager(M, N, K, tile):
+    """Replays of a captured call against eager calls that share its workspace, bit for bit. With
+    tiles, every tile is split along K (6144 x 5120 at M = 128: 48 tiles in 5 ranges each; 64
+    tiles over 256 workgroups otherwise), so each call writes FP32 partials into the workspace
+    and a second kernel adds them in a fixed order. The workspace starts as random bytes; two
+    replays in a row and the eager calls in between must all agree."""
+    x, b, sb, wp, alpha = _w4a16_case(M, N, K, 77 + M)
+    cfg = None if tile is None else nv.make_config(nv.KERNEL_W4A16_TILES, tile_m=tile[0], tile_n=tile[1])
     xd = dev(x).view(torch.bfloat16).clone()
-    ws = nv.workspace(nv.OP_W4A16, M, N, K)
+    ws = nv.workspace(nv.OP_W4A16, M, N, K, config=cfg)
+    if ws is not None:
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=torch.Generator().manual_seed(5)).to(ws.device))
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    nv.nvfp4_gemm_w4a16(xd, wp, N, K, alpha, out=out, ws=ws)   # warm-up outside capture
+    nv.nvfp4_gemm_w4a16(xd, wp, N, K, alpha, out=out, ws=ws, config=cfg)   # warm-up outside capture
     torch.cuda.synchronize()
+    y, S = gemm.w4a16(x, b, sb, alpha)
+    assert_close(host(out), y, S, bf16=True, what=f"w4a16 graph warm-up M={M} {N}x{K}")
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            nv.nvfp4_gemm_w4a16(xd, wp, N, K, alpha, out=out, ws=ws)
+            nv.nvfp4_gemm_w4a16(xd, wp, N, K, alpha, out=out, ws=ws, config=cfg)
     torch.cuda.synchronize()
     for rep in range(3):
         xn = synth.normal_bf16(900 + rep, M, K)
         xd.copy_(dev(xn).view(torch.bfloat16))
         g.replay()
         torch.cuda.synchronize()
-        eager = nv.nvfp4_gemm_w4a16(dev(xn).view(torch.bfloat16), wp, N, K, alpha)
+        got = out.clone()
+        g.replay()                                     # the words now read complete for this epoch
         torch.cuda.synchronize()
-        assert torch.equal(out, eager)
+        assert torch.equal(out, got)
+        eager = nv.nvfp4_gemm_w4a16(dev(xn).view(torch.bfloat16), wp, N, K, alpha, ws=ws, config=cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager)
 
 
 @pytest.mark.parametrize("mode", ["no_workspace", "split", "split_dynamic"])
