@@ -745,12 +745,14 @@ def test_w4a4_per_column_alpha(M, N, K, entry, out_dtype):
     assert not host(out)[:, ::17].any(), "zero column scales give zero columns"
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 34816, 256), (3, 320, 640), (16, 17408, 1088), (40, 2048, 1024),
-                                   (100, 512, 1024), (300, 56320, 192), (1000, 2080, 320)])
+@pytest.mark.parametrize("M,N,K", [(1, 34816, 256), (3, 320, 640), (16, 17408, 1088), (24, 17408, 1088),
+                                   (40, 2048, 1024), (56, 17408, 1088), (100, 512, 1024), (300, 56320, 192),
+                                   (1000, 2080, 320)])
 def test_w4a16_per_column_alpha_zero_negative_scales(M, N, K):
     """Per-column alpha with zero and negative block scales (the combination the pages' tests
-    name) on every W4A16 path: decode with the cut tail (1 x 34816), decode M = 3, skinny on x
-    rows (16) and on the fragment-order copy (40), the 128 x 128 split with a fix-up
+    name) on every W4A16 path: decode with the cut tail (1 x 34816), M = 3, the row kernel at 16,
+    32 (two row groups per workgroup) and 64 padded rows (16, 24, 40), the fragment kernel on
+    its fragment-order copy (56 rows of a 544-group weight), the 128 x 128 split with a fix-up
     (100 x 512, 1000 x 2080), 256 x 256 tiles with split leftovers (300 x 56320); full check."""
     x, b, sb, _, alpha = _w4a16_case(M, N, K, M + N + K + 5)
     sb = sb.copy()
