@@ -214,6 +214,20 @@ static SkinnyShape skinny_shape(int64_t M, int64_t N, int64_t K, int cus) {
 // Split ranges write FP32 partials (two slots per workgroup) that a fix-up
 // kernel adds in workgroup order.
 constexpr int kMaxKSplit = 8;
+// How a tile kernel's x reaches the MFMAs (XP): a fragment-order copy of x
+// that every wave reads into its own registers (kXDirect), or 128 rows staged
+// once per workgroup through LDS and shared by its four waves (kXLds; kXLdsDeep
+// with the deeper register rings of one workgroup per CU).
+constexpr int kXDirect = 0, kXLds = 1, kXLdsDeep = 2;
+// The 128 x 256 tiles' longest K range (chunks per workgroup) on the LDS path.
+// Measured by graph replay on the 27B-class layers, all tiles split:
+// 34816 x 5120 at M = 128 (42 chunks) 79.9 -> 72.7 us, 5120 x 17408 at M = 256
+// (42) 80.5 -> 71.8 us, 5120 x 5120 at M = 1024 (50) 80.3 -> 78.0 us; with
+// longer ranges or whole tiles the direct path's loop was faster than the copy
+// it needs: 6144 x 5120 at M = 1024 (60) 89.3 against 89.9 us, 5120 x 17408 at
+// M = 1024 (170) 187.8 against 192.3 us, 34816 x 5120 at M = 512 (whole tiles)
+// 173 against 196 us.
+constexpr int64_t kLdsMaxRange = 50;
 
 struct BigSched {
   int TM, TN, WGM;   // MFMA tiles per wave; waves along M
@@ -259,15 +273,27 @@ static size_t big_partial_bytes(const BigSched &b) { return (size_t)b.TM * b.TN 
 static size_t big_partials_span(const BigSched &b) {
   return b.rem > 0 ? ((size_t)b.G * 2 * big_partial_bytes(b) + 255) / 256 * 256 : 0;
 }
-static int64_t big_xmt(const BigSched &b) { return b.TM * b.TN >= 8 ? b.tiles_m * b.tile_rows() / 32 : 0; }
-static size_t big_xf_bytes(const BigSched &b, int64_t K) { return (size_t)big_xmt(b) * 32 * (size_t)K * 2; }
+// The x path of a schedule: 128 x 128 tiles always stage x through LDS (deep
+// rings when the grid holds one workgroup per CU); 128 x 256 tiles do when
+// every tile is split and the ranges are short; 256 x 256 tiles never.
+static int big_xpath(const BigSched &b, int64_t K, int cus) {
+  if (b.TM * b.TN < 8) return b.G <= cus ? kXLdsDeep : kXLds;
+  if (b.TM * b.TN == 8 && b.full == 0 && b.rem * (K / 64) <= kLdsMaxRange * b.G) return kXLdsDeep;
+  return kXDirect;
+}
+static int64_t big_xmt(const BigSched &b, int64_t K, int cus) {
+  return big_xpath(b, K, cus) == kXDirect ? b.tiles_m * b.tile_rows() / 32 : 0;
+}
+static size_t big_xf_bytes(const BigSched &b, int64_t K, int cus) {
+  return (size_t)big_xmt(b, K, cus) * 32 * (size_t)K * 2;
+}
 
 static size_t workspace_for(const Plan &p, const nvfp4_config &c, int64_t M, int64_t N, int64_t K) {
   if (p.kind == 3)
     return M > kSkinnyDirectMaxM && skinny_shape(M, N, K, c.num_cus).RP == 0 ? skinny_x_bytes(M, K) : 0;
   if (p.kind == 4) {
     const BigSched b = big_sched(M, N, K, c);
-    return big_partials_span(b) + big_xf_bytes(b, K);
+    return big_partials_span(b) + big_xf_bytes(b, K, c.num_cus);
   }
   return 0;
 }
@@ -802,6 +828,7 @@ constexpr int kGroupM = 8;
 // and (8, 3) were no better.
 constexpr int kDeepW = 6;
 constexpr int kDeepX = 2;
+constexpr int kXT = 2;   // the LDS path's x tile: 64 kXT = 128 rows
 
 struct Params {
   const uint16_t *x;
@@ -928,60 +955,62 @@ __device__ __forceinline__ void scales_of(const WFrags<T> &f, f32x2_t (&sc)[T]) 
 // XA chunks ahead) into LDS buffer c & 1 at the end of chunk c - 1. On entry
 // (a, b) are step 0's operands and sc chunk c's scales; on exit, chunk
 // c + 1's.
-template <int P, int T, int DW, int XA>
-__device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uint32_t (&ow)[T],
-                                      const uint32_t (&ows)[T], int64_t c, int64_t nch, WFrags<T> (&f)[DW],
-                                      XRegs<T> (&xr)[XA], f32x2_t (&sc)[T], uint8_t *smem, int wm, bf16x8_t (&a)[T],
-                                      bf16x8_t (&b)[T], f32x16_t (&acc)[T][T]) {
-  constexpr int kValu = 16 / T + 1;                 // dequant instructions per MFMA, rounded up
+template <int P, int TM, int TN, int DW, int XA>
+__device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uint32_t (&ow)[TN],
+                                      const uint32_t (&ows)[TN], int64_t c, int64_t nch, WFrags<TN> (&f)[DW],
+                                      XRegs<kXT> (&xr)[XA], f32x2_t (&sc)[TN], uint8_t *smem, int wm,
+                                      bf16x8_t (&a)[TM], bf16x8_t (&b)[TN], f32x16_t (&acc)[TM][TN]) {
+  constexpr int kValu = 16 / TM + 1;                // dequant instructions per MFMA, rounded up
   constexpr int FW = P % DW, FN = (P + 1) % DW;
-  load_x<T>(tb, ldx, c + XA, nch, xr[P % XA]);      // its previous chunk went into LDS at the end of chunk c - 1
+  constexpr int XBUF = 64 * kXT * 128;              // one chunk of x in LDS
+  load_x<kXT>(tb, ldx, c + XA, nch, xr[P % XA]);    // its previous chunk went into LDS at the end of chunk c - 1
   __builtin_amdgcn_sched_barrier(0);   // x first (see above)
-  load_w<T>(tb, ow, ows, c + DW - 1, nch, f[(P + DW - 1) % DW]);
-  uint8_t *cur = smem + (c & 1) * (64 * T * 128);
-  uint8_t *nxt = smem + ((c + 1) & 1) * (64 * T * 128);
+  load_w<TN>(tb, ow, ows, c + DW - 1, nch, f[(P + DW - 1) % DW]);
+  uint8_t *cur = smem + (c & 1) * XBUF;
+  uint8_t *nxt = smem + ((c + 1) & 1) * XBUF;
 #pragma unroll
   for (int s = 0; s < 4; s++) {
-    bf16x8_t an[T], bn[T];
+    bf16x8_t an[TM], bn[TN];
     if (s < 3) {
-      read_x<T>(cur, s + 1, wm, an);
-      deq_w<T>(f[FW], sc, s + 1, bn);
+      read_x<TM>(cur, s + 1, wm, an);
+      deq_w<TN>(f[FW], sc, s + 1, bn);
     } else {
-      scales_of<T>(f[FN], sc);
-      deq_w<T>(f[FN], sc, 0, bn);
+      scales_of<TN>(f[FN], sc);
+      deq_w<TN>(f[FN], sc, 0, bn);
     }
 #pragma unroll
-    for (int i = 0; i < T; i++)
+    for (int i = 0; i < TM; i++)
 #pragma unroll
-      for (int j = 0; j < T; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < T; i++) {
+    for (int i = 0; i < TM; i++)
       if (s < 3) a[i] = an[i];
-      b[i] = bn[i];
-    }
-    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * T, 0);
 #pragma unroll
-    for (int k = 0; k < T * T; k++) {
+    for (int j = 0; j < TN; j++) b[j] = bn[j];
+    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * kXT, 0);
+#pragma unroll
+    for (int k = 0; k < TM * TN; k++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-      if (s < 3 && k < T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (s < 3 && k < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  store_x<T>(nxt, xr[(P + 1) % XA]);
+  store_x<kXT>(nxt, xr[(P + 1) % XA]);
   lds_barrier();
-  read_x<T>(nxt, 0, wm, a);   // the next chunk's step-0 x, now that it is in LDS
+  read_x<TM>(nxt, 0, wm, a);   // the next chunk's step-0 x, now that it is in LDS
 }
 
 // Chunks c + Q, Q in Qs, while below n (the conditions are uniform over the
 // workgroup, so every wave meets the same barriers).
-template <int T, int DW, int XA, int... Qs>
+template <int TM, int TN, int DW, int XA, int... Qs>
 __device__ __forceinline__ void chunk_run(std::integer_sequence<int, Qs...>, bool all, const TileBase &tb,
-                                          int64_t ldx, const uint32_t (&ow)[T], const uint32_t (&ows)[T], int64_t c,
-                                          int64_t n, WFrags<T> (&f)[DW], XRegs<T> (&xr)[XA], f32x2_t (&sc)[T],
-                                          uint8_t *smem, int wm, bf16x8_t (&a)[T], bf16x8_t (&b)[T],
-                                          f32x16_t (&acc)[T][T]) {
-  ((all || c + Qs < n ? chunk<Qs, T, DW, XA>(tb, ldx, ow, ows, c + Qs, n, f, xr, sc, smem, wm, a, b, acc) : void()),
+                                          int64_t ldx, const uint32_t (&ow)[TN], const uint32_t (&ows)[TN], int64_t c,
+                                          int64_t n, WFrags<TN> (&f)[DW], XRegs<kXT> (&xr)[XA], f32x2_t (&sc)[TN],
+                                          uint8_t *smem, int wm, bf16x8_t (&a)[TM], bf16x8_t (&b)[TN],
+                                          f32x16_t (&acc)[TM][TN]) {
+  ((all || c + Qs < n ? chunk<Qs, TM, TN, DW, XA>(tb, ldx, ow, ows, c + Qs, n, f, xr, sc, smem, wm, a, b, acc)
+                      : void()),
    ...);
 }
 
@@ -1004,16 +1033,16 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // Chunks [c0, c0 + n) of tile `tile` into acc (zeroed first). The tile bases
 // are moved to chunk c0, so chunk c of the loop is chunk c0 + c of the tile and
 // the loads past the range are empty.
-template <int T, int DW, int XA>
+template <int TM, int TN, int WGM, int DW, int XA>
 __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t c0, int64_t n, uint8_t *smem,
-                                              const uint32_t (&ow)[T], const uint32_t (&ows)[T], int wm,
-                                              f32x16_t (&acc)[T][T], int64_t &m0, int64_t &n0) {
-  constexpr int BT = 64 * T;
+                                              const uint32_t (&ow)[TN], const uint32_t (&ows)[TN], int wm,
+                                              f32x16_t (&acc)[TM][TN], int64_t &m0, int64_t &n0) {
+  static_assert(TM * WGM * 32 == 64 * kXT, "the LDS path stages 128 rows of x");
   const int64_t kt = p.K / 64;
   int tm, tn;
   tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
-  m0 = (int64_t)tm * BT;
-  n0 = (int64_t)tn * BT;
+  m0 = (int64_t)tm * 32 * TM * WGM;
+  n0 = (int64_t)tn * 32 * TN * (4 / WGM);
   TileBase tb;
   tb.x = reinterpret_cast<const uint8_t *>(p.x + m0 * p.ldx + c0 * 64);
   tb.x_bytes = (p.M - m0) * p.ldx * 2 - c0 * 128;
@@ -1023,25 +1052,25 @@ __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t
   tb.ws_bytes = (p.N - n0) / 32 * kt * 128 - c0 * 128;
 
 #pragma unroll
-  for (int i = 0; i < T; i++)
+  for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int j = 0; j < T; j++) acc[i][j] = f32x16_t{};
-  WFrags<T> f[DW];
-  XRegs<T> xr[XA];
-  f32x2_t sc[T];
-  bf16x8_t a[T], b[T];
+    for (int j = 0; j < TN; j++) acc[i][j] = f32x16_t{};
+  WFrags<TN> f[DW];
+  XRegs<kXT> xr[XA];
+  f32x2_t sc[TN];
+  bf16x8_t a[TM], b[TN];
   __syncthreads();   // the previous tile's waves are done with the LDS buffers
-  load_x<T>(tb, p.ldx, 0, n, xr[0]);
+  load_x<kXT>(tb, p.ldx, 0, n, xr[0]);
 #pragma unroll
-  for (int q = 1; q < XA; q++) load_x<T>(tb, p.ldx, q, n, xr[q]);
+  for (int q = 1; q < XA; q++) load_x<kXT>(tb, p.ldx, q, n, xr[q]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < DW - 1; q++) load_w<T>(tb, ow, ows, q, n, f[q]);
-  store_x<T>(smem, xr[0]);
+  for (int q = 0; q < DW - 1; q++) load_w<TN>(tb, ow, ows, q, n, f[q]);
+  store_x<kXT>(smem, xr[0]);
   lds_barrier();
-  scales_of<T>(f[0], sc);
-  read_x<T>(smem, 0, wm, a);
-  deq_w<T>(f[0], sc, 0, b);
+  scales_of<TN>(f[0], sc);
+  read_x<TM>(smem, 0, wm, a);
+  deq_w<TN>(f[0], sc, 0, b);
   // chunks in whole periods of the two rings, then the ones left (padding the
   // range to whole periods ran all-zero chunks: a 16-chunk K range took 18
   // with the three-chunk period)
@@ -1049,9 +1078,9 @@ __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t
   using Period = std::make_integer_sequence<int, PER>;
   int64_t c = 0;
   for (; c + PER <= n; c += PER)
-    chunk_run<T, DW, XA>(Period{}, true, tb, p.ldx, ow, ows, c, n, f, xr, sc, smem, wm, a, b, acc);
-  chunk_run<T, DW, XA>(std::make_integer_sequence<int, PER - 1>{}, false, tb, p.ldx, ow, ows, c, n, f, xr, sc, smem,
-                       wm, a, b, acc);
+    chunk_run<TM, TN, DW, XA>(Period{}, true, tb, p.ldx, ow, ows, c, n, f, xr, sc, smem, wm, a, b, acc);
+  chunk_run<TM, TN, DW, XA>(std::make_integer_sequence<int, PER - 1>{}, false, tb, p.ldx, ow, ows, c, n, f, xr, sc,
+                            smem, wm, a, b, acc);
 }
 
 // The main loop with x read straight into registers from its fragment-order
@@ -1231,9 +1260,10 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
 // registers (tile_mainloop_d).
 // COLS: p.alpha_col is set (a separate instantiation, so that the kernel
 // without a per-column scale keeps its registers for the main loop).
-template <int TM, int TN, int WGM, bool COLS, bool DEEP>
-__global__ __launch_bounds__(kThreads, TM * TN >= 8 || DEEP ? 1 : 2) void big_kernel(Params p) {
-  constexpr bool kLds = TM == 2 && TN == 2;
+template <int TM, int TN, int WGM, bool COLS, int XP>
+__global__ __launch_bounds__(kThreads, TM * TN >= 8 || XP == kXLdsDeep ? 1 : 2) void big_kernel(Params p) {
+  constexpr bool kLds = XP != kXDirect;
+  constexpr bool DEEP = XP == kXLdsDeep;
   constexpr int WGN = 4 / WGM;
   // LDS path: two x chunks; direct paths: the epilogue's BF16 staging
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds ? 2 * 128 * 128 : 4 * 32 * 32 * TN * 2];
@@ -1254,7 +1284,8 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 || DEEP ? 1 : 2) void big_ke
   int64_t m0, n0;
   for (int tile = pid; tile < p.full; tile += G) {
     if constexpr (kLds)
-      tile_mainloop<2, DEEP ? kDeepW : 3, DEEP ? kDeepX : 1>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0, n0);
+      tile_mainloop<TM, TN, WGM, DEEP ? kDeepW : 3, DEEP ? kDeepX : 1>(p, tile, 0, nch, smem, ow, ows, wm, acc, m0,
+                                                                      n0);
     else
       tile_mainloop_d<TM, TN, WGM>(p, tile, 0, nch, ow, ows, wm, acc, m0, n0);
     tile_epilogue<TM, TN, COLS>(p, smem, alpha, m0, n0, wave, wm, wn, acc);
@@ -1265,8 +1296,8 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 || DEEP ? 1 : 2) void big_ke
     for (int seg = 0; s < e; seg++) {
       const int64_t rho = s / nch, c0 = s - rho * nch, c1 = min(nch, c0 + (e - s));
       if constexpr (kLds)
-        tile_mainloop<2, DEEP ? kDeepW : 3, DEEP ? kDeepX : 1>(p, p.full + (int)rho, c0, c1 - c0, smem, ow, ows, wm,
-                                                               acc, m0, n0);
+        tile_mainloop<TM, TN, WGM, DEEP ? kDeepW : 3, DEEP ? kDeepX : 1>(p, p.full + (int)rho, c0, c1 - c0, smem, ow,
+                                                                        ows, wm, acc, m0, n0);
       else
         tile_mainloop_d<TM, TN, WGM>(p, p.full + (int)rho, c0, c1 - c0, ow, ows, wm, acc, m0, n0);
       float *dst = p.partials + ((int64_t)pid * 2 + seg) * partial_floats<TM, TN>() +
@@ -1368,23 +1399,31 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
   }
 }
 
-// The tile kernel's instantiations: per-column alpha or not, and for the
-// 128 x 128 LDS path the deep rings when the grid holds one workgroup per CU.
-template <int TM, int TN, int WGM>
-static void launch_big(bool one_per_cu, bool cols, unsigned grid, hipStream_t s, const Params &bp) {
-  if constexpr (TM * TN < 8) {
-    if (one_per_cu) {
-      if (cols)
-        hipLaunchKernelGGL((big_kernel<TM, TN, WGM, true, true>), dim3(grid), dim3(kThreads), 0, s, bp);
-      else
-        hipLaunchKernelGGL((big_kernel<TM, TN, WGM, false, true>), dim3(grid), dim3(kThreads), 0, s, bp);
-      return;
-    }
-  }
+// The tile kernel's instantiations: per-column alpha or not, and the x path
+// (big_xpath): 128 x 128 tiles on LDS (deep rings with one workgroup per CU),
+// 128 x 256 tiles direct or on LDS, 256 x 256 tiles direct.
+template <int TM, int TN, int WGM, int XP>
+static void launch_big_x(bool cols, unsigned grid, hipStream_t s, const Params &bp) {
   if (cols)
-    hipLaunchKernelGGL((big_kernel<TM, TN, WGM, true, false>), dim3(grid), dim3(kThreads), 0, s, bp);
+    hipLaunchKernelGGL((big_kernel<TM, TN, WGM, true, XP>), dim3(grid), dim3(kThreads), 0, s, bp);
   else
-    hipLaunchKernelGGL((big_kernel<TM, TN, WGM, false, false>), dim3(grid), dim3(kThreads), 0, s, bp);
+    hipLaunchKernelGGL((big_kernel<TM, TN, WGM, false, XP>), dim3(grid), dim3(kThreads), 0, s, bp);
+}
+template <int TM, int TN, int WGM>
+static void launch_big(int xpath, bool cols, unsigned grid, hipStream_t s, const Params &bp) {
+  if constexpr (TM * TN < 8) {
+    if (xpath == kXLdsDeep)
+      launch_big_x<TM, TN, WGM, kXLdsDeep>(cols, grid, s, bp);
+    else
+      launch_big_x<TM, TN, WGM, kXLds>(cols, grid, s, bp);
+  } else if constexpr (TM * TN == 8) {
+    if (xpath == kXLdsDeep)
+      launch_big_x<TM, TN, WGM, kXLdsDeep>(cols, grid, s, bp);
+    else
+      launch_big_x<TM, TN, WGM, kXDirect>(cols, grid, s, bp);
+  } else {
+    launch_big_x<TM, TN, WGM, kXDirect>(cols, grid, s, bp);
+  }
 }
 
 }  // namespace big
@@ -1486,9 +1525,11 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   } else if (plan.kind == 4) {
     const w4a16::BigSched b = w4a16::big_sched(M, N, K, cfg);
     // fragment-order x: 32-bit offsets inside it
-    if (b.total > 0x7FFFFFFF || w4a16::big_xf_bytes(b, K) > 0x7FFFFFFFull) return NVFP4_ERR_SHAPE;
-    if (b.TM * b.TN < 8 && (int64_t)128 * ldx * 2 > 0xFFFFFFFFll) return NVFP4_ERR_SHAPE;   // LDS path: 32-bit x offsets
-    const int64_t xmt = w4a16::big_xmt(b);
+    const int xpath = w4a16::big_xpath(b, K, cfg.num_cus);
+    if (b.total > 0x7FFFFFFF || w4a16::big_xf_bytes(b, K, cfg.num_cus) > 0x7FFFFFFFull) return NVFP4_ERR_SHAPE;
+    if (xpath != w4a16::kXDirect && (int64_t)128 * ldx * 2 > 0xFFFFFFFFll)
+      return NVFP4_ERR_SHAPE;   // LDS path: 32-bit x offsets
+    const int64_t xmt = w4a16::big_xmt(b, K, cfg.num_cus);
     uint8_t *xf = xmt > 0 ? static_cast<uint8_t *>(ws) + w4a16::big_partials_span(b) : nullptr;
     if (xmt > 0) {
       hipLaunchKernelGGL(w4a16::tile_x_kernel, dim3((unsigned)(K / 64 * xmt)), dim3(256), 0, s, x, ldx, M, K,
@@ -1500,7 +1541,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
                           (int)b.full, (int)b.rem, static_cast<float *>(ws), xf, (int)xmt};
     const unsigned grid = (unsigned)b.G, fix_grid = (unsigned)(b.rem * b.TM * b.TN);
 #define NVFP4_BIG(TMV, TNV, WGMV)                                                                                \
-  w4a16::big::launch_big<TMV, TNV, WGMV>(b.G <= cfg.num_cus, alpha_col != nullptr, grid, s, bp);                 \
+  w4a16::big::launch_big<TMV, TNV, WGMV>(xpath, alpha_col != nullptr, grid, s, bp);                 \
   if (b.rem > 0) {                                                                                               \
     NVFP4_LAUNCH_CHECK();                                                                                        \
     hipLaunchKernelGGL((w4a16::big::big_fixup_kernel<TMV, TNV, WGMV>), dim3(fix_grid), dim3(w4a16::big::kThreads), \

@@ -187,8 +187,13 @@ def test_workspace_sizes():
     # K past the row kernel's 32-bit weight offsets: the fragment kernel and its copy
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 24, 64, (1 << 27) + 64) == 32 * ((1 << 27) + 64) * 2
     # M = 128 on 34816 x 5120: 136 tiles of 128 x 256, all split over 256 workgroups (two
-    # 128 KiB partial slots each), then x for one 128-row tile in fragment order
-    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 128, 34816, 5120) == 256 * 2 * 128 * 1024 + 128 * 5120 * 2
+    # 128 KiB partial slots each) in ranges of 42-43 chunks, short enough for x to go
+    # through LDS: no copy of x
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 128, 34816, 5120) == 256 * 2 * 128 * 1024
+    # M = 1024 on 5120 x 17408: 160 tiles of 128 x 256, all split, 170 chunks per range:
+    # the partials, then x for eight 128-row tiles in fragment order
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1024, 5120, 17408) == (256 * 2 * 128 * 1024
+                                                                       + 1024 * 17408 * 2)
     # M = 1024: 544 tiles of 256 x 256, 512 in two whole rounds and 32 split (two 256 KiB
     # slots per workgroup), then x for four 256-row tiles
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1024, 34816, 5120) == 256 * 2 * 256 * 1024 + 1024 * 5120 * 2

@@ -633,8 +633,9 @@ def test_w4a16_big_ragged(M, N, K):
     700 x 3008 x 33792 (36 ragged tiles of 528 chunks, 74-75 per workgroup, so ranges
     straddle tiles) and 1024 x 2048 x 49152 (32 tiles, exactly 8 ranges of 96 per tile).
     128 x 256 tiles: 200 x 34816 x 192 (544 tiles of 128 x 128 would do; 272 of 128 x 256
-    fill one round and leave 16 split three chunks over 256 workgroups, most of them empty)
-    and 100 x 8224 x 16064 (33 ragged tiles, all split, about 32 chunks per workgroup)."""
+    fill one round and leave 16 split three chunks over 256 workgroups, most of them empty;
+    x from its fragment-order copy) and 100 x 8224 x 16064 (33 ragged tiles, all split,
+    about 32 chunks per workgroup; x staged through LDS)."""
     x, b, sb, wp, alpha = _w4a16_case(M, N, K, M + N + K)
     out = nv.nvfp4_gemm_w4a16(dev(x).view(torch.bfloat16), wp, N, K, alpha)
     torch.cuda.synchronize()
