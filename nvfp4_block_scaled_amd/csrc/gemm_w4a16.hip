@@ -276,6 +276,8 @@ static size_t big_partials_span(const BigSched &b) {
 // The x path of a schedule: 128 x 128 tiles always stage x through LDS (deep
 // rings when the grid holds one workgroup per CU); 128 x 256 tiles do when
 // every tile is split and the ranges are short; 256 x 256 tiles never.
+// (256 x 256 tiles on the LDS path, with 256 rows of x per chunk, measured
+// slower on whole tiles: 34816 x 5120 at M = 1024 325 -> 384 us.)
 static int big_xpath(const BigSched &b, int64_t K, int cus) {
   if (b.TM * b.TN < 8) return b.G <= cus ? kXLdsDeep : kXLds;
   if (b.TM * b.TN == 8 && b.full == 0 && b.rem * (K / 64) <= kLdsMaxRange * b.G) return kXLdsDeep;
@@ -828,7 +830,6 @@ constexpr int kGroupM = 8;
 // and (8, 3) were no better.
 constexpr int kDeepW = 6;
 constexpr int kDeepX = 2;
-constexpr int kXT = 2;   // the LDS path's x tile: 64 kXT = 128 rows
 
 struct Params {
   const uint16_t *x;
@@ -955,15 +956,15 @@ __device__ __forceinline__ void scales_of(const WFrags<T> &f, f32x2_t (&sc)[T]) 
 // XA chunks ahead) into LDS buffer c & 1 at the end of chunk c - 1. On entry
 // (a, b) are step 0's operands and sc chunk c's scales; on exit, chunk
 // c + 1's.
-template <int P, int TM, int TN, int DW, int XA>
+template <int P, int TM, int TN, int XT, int DW, int XA>
 __device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uint32_t (&ow)[TN],
                                       const uint32_t (&ows)[TN], int64_t c, int64_t nch, WFrags<TN> (&f)[DW],
-                                      XRegs<kXT> (&xr)[XA], f32x2_t (&sc)[TN], uint8_t *smem, int wm,
+                                      XRegs<XT> (&xr)[XA], f32x2_t (&sc)[TN], uint8_t *smem, int wm,
                                       bf16x8_t (&a)[TM], bf16x8_t (&b)[TN], f32x16_t (&acc)[TM][TN]) {
   constexpr int kValu = 16 / TM + 1;                // dequant instructions per MFMA, rounded up
   constexpr int FW = P % DW, FN = (P + 1) % DW;
-  constexpr int XBUF = 64 * kXT * 128;              // one chunk of x in LDS
-  load_x<kXT>(tb, ldx, c + XA, nch, xr[P % XA]);    // its previous chunk went into LDS at the end of chunk c - 1
+  constexpr int XBUF = 64 * XT * 128;               // one chunk of x in LDS
+  load_x<XT>(tb, ldx, c + XA, nch, xr[P % XA]);     // its previous chunk went into LDS at the end of chunk c - 1
   __builtin_amdgcn_sched_barrier(0);   // x first (see above)
   load_w<TN>(tb, ow, ows, c + DW - 1, nch, f[(P + DW - 1) % DW]);
   uint8_t *cur = smem + (c & 1) * XBUF;
@@ -987,7 +988,7 @@ __device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uin
       if (s < 3) a[i] = an[i];
 #pragma unroll
     for (int j = 0; j < TN; j++) b[j] = bn[j];
-    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * kXT, 0);
+    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * XT, 0);
 #pragma unroll
     for (int k = 0; k < TM * TN; k++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -996,20 +997,20 @@ __device__ __forceinline__ void chunk(const TileBase &tb, int64_t ldx, const uin
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  store_x<kXT>(nxt, xr[(P + 1) % XA]);
+  store_x<XT>(nxt, xr[(P + 1) % XA]);
   lds_barrier();
   read_x<TM>(nxt, 0, wm, a);   // the next chunk's step-0 x, now that it is in LDS
 }
 
 // Chunks c + Q, Q in Qs, while below n (the conditions are uniform over the
 // workgroup, so every wave meets the same barriers).
-template <int TM, int TN, int DW, int XA, int... Qs>
+template <int TM, int TN, int XT, int DW, int XA, int... Qs>
 __device__ __forceinline__ void chunk_run(std::integer_sequence<int, Qs...>, bool all, const TileBase &tb,
                                           int64_t ldx, const uint32_t (&ow)[TN], const uint32_t (&ows)[TN], int64_t c,
-                                          int64_t n, WFrags<TN> (&f)[DW], XRegs<kXT> (&xr)[XA], f32x2_t (&sc)[TN],
+                                          int64_t n, WFrags<TN> (&f)[DW], XRegs<XT> (&xr)[XA], f32x2_t (&sc)[TN],
                                           uint8_t *smem, int wm, bf16x8_t (&a)[TM], bf16x8_t (&b)[TN],
                                           f32x16_t (&acc)[TM][TN]) {
-  ((all || c + Qs < n ? chunk<Qs, TM, TN, DW, XA>(tb, ldx, ow, ows, c + Qs, n, f, xr, sc, smem, wm, a, b, acc)
+  ((all || c + Qs < n ? chunk<Qs, TM, TN, XT, DW, XA>(tb, ldx, ow, ows, c + Qs, n, f, xr, sc, smem, wm, a, b, acc)
                       : void()),
    ...);
 }
@@ -1037,7 +1038,7 @@ template <int TM, int TN, int WGM, int DW, int XA>
 __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t c0, int64_t n, uint8_t *smem,
                                               const uint32_t (&ow)[TN], const uint32_t (&ows)[TN], int wm,
                                               f32x16_t (&acc)[TM][TN], int64_t &m0, int64_t &n0) {
-  static_assert(TM * WGM * 32 == 64 * kXT, "the LDS path stages 128 rows of x");
+  constexpr int XT = TM * WGM / 2;   // x rows staged per chunk: 64 XT (the tile's rows)
   const int64_t kt = p.K / 64;
   int tm, tn;
   tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
@@ -1056,17 +1057,17 @@ __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t
 #pragma unroll
     for (int j = 0; j < TN; j++) acc[i][j] = f32x16_t{};
   WFrags<TN> f[DW];
-  XRegs<kXT> xr[XA];
+  XRegs<XT> xr[XA];
   f32x2_t sc[TN];
   bf16x8_t a[TM], b[TN];
   __syncthreads();   // the previous tile's waves are done with the LDS buffers
-  load_x<kXT>(tb, p.ldx, 0, n, xr[0]);
+  load_x<XT>(tb, p.ldx, 0, n, xr[0]);
 #pragma unroll
-  for (int q = 1; q < XA; q++) load_x<kXT>(tb, p.ldx, q, n, xr[q]);
+  for (int q = 1; q < XA; q++) load_x<XT>(tb, p.ldx, q, n, xr[q]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 0; q < DW - 1; q++) load_w<TN>(tb, ow, ows, q, n, f[q]);
-  store_x<kXT>(smem, xr[0]);
+  store_x<XT>(smem, xr[0]);
   lds_barrier();
   scales_of<TN>(f[0], sc);
   read_x<TM>(smem, 0, wm, a);
@@ -1078,9 +1079,9 @@ __device__ __forceinline__ void tile_mainloop(const Params &p, int tile, int64_t
   using Period = std::make_integer_sequence<int, PER>;
   int64_t c = 0;
   for (; c + PER <= n; c += PER)
-    chunk_run<TM, TN, DW, XA>(Period{}, true, tb, p.ldx, ow, ows, c, n, f, xr, sc, smem, wm, a, b, acc);
-  chunk_run<TM, TN, DW, XA>(std::make_integer_sequence<int, PER - 1>{}, false, tb, p.ldx, ow, ows, c, n, f, xr, sc,
-                            smem, wm, a, b, acc);
+    chunk_run<TM, TN, XT, DW, XA>(Period{}, true, tb, p.ldx, ow, ows, c, n, f, xr, sc, smem, wm, a, b, acc);
+  chunk_run<TM, TN, XT, DW, XA>(std::make_integer_sequence<int, PER - 1>{}, false, tb, p.ldx, ow, ows, c, n, f, xr,
+                                sc, smem, wm, a, b, acc);
 }
 
 // The main loop with x read straight into registers from its fragment-order
@@ -1266,7 +1267,7 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 || XP == kXLdsDeep ? 1 : 2) 
   constexpr bool DEEP = XP == kXLdsDeep;
   constexpr int WGN = 4 / WGM;
   // LDS path: two x chunks; direct paths: the epilogue's BF16 staging
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds ? 2 * 128 * 128 : 4 * 32 * 32 * TN * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds ? 2 * (32 * TM * WGM) * 128 : 4 * 32 * 32 * TN * 2];
   const int t = threadIdx.x, wave = t >> 6, wm = wave / WGN, wn = wave % WGN;
   const int lane = t & 63, r = lane & 31;
   const int G = gridDim.x;
@@ -1527,7 +1528,7 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     // fragment-order x: 32-bit offsets inside it
     const int xpath = w4a16::big_xpath(b, K, cfg.num_cus);
     if (b.total > 0x7FFFFFFF || w4a16::big_xf_bytes(b, K, cfg.num_cus) > 0x7FFFFFFFull) return NVFP4_ERR_SHAPE;
-    if (xpath != w4a16::kXDirect && (int64_t)128 * ldx * 2 > 0xFFFFFFFFll)
+    if (xpath != w4a16::kXDirect && b.tile_rows() * ldx * 2 > 0xFFFFFFFFll)
       return NVFP4_ERR_SHAPE;   // LDS path: 32-bit x offsets
     const int64_t xmt = w4a16::big_xmt(b, K, cfg.num_cus);
     uint8_t *xf = xmt > 0 ? static_cast<uint8_t *>(ws) + w4a16::big_partials_span(b) : nullptr;
