@@ -162,9 +162,10 @@ static size_t skinny_x_bytes(int64_t M, int64_t K) { return (size_t)((M + 31) / 
 // and RP > 0 (x rows padded to RP = 8, 16, 32 or 64) for the row kernel, which
 // stages x rows through LDS, or RP = 0 for the fragment kernel, which reads a
 // fragment-order copy of x from the workspace (or, for M <= 16, x directly).
-// The row kernel needs no workspace: rows >= M read whatever in-range bytes
-// their 32-bit offsets reach (or zero) and only feed output rows that are not
-// stored, and rows < M stay below the M ldx 2 bytes the dispatch bounds.
+// The row kernel needs no workspace: rows >= M read zero, or whatever bytes of
+// x their 32-bit offsets wrap to (the buffer range ends with x's last
+// element), and only feed output rows that are not stored; rows < M stay below
+// the M ldx 2 bytes the dispatch bounds.
 // Measured on the 27B-class layer shapes (graph replays, one box), fragment
 // kernel with its copy -> row kernel:
 //   M = 8:  6144 x 5120 9.6 -> 6.5 us, 5120 x 17408 22.7 -> 15.5 us, 34816 x 5120 31.2 -> 23.3 us;
@@ -522,7 +523,9 @@ __global__ __launch_bounds__(W * 64) void skinny_kernel(const uint16_t *__restri
   const uint8_t *cb = wp + ((g0 * T) << 10) + lane * 16;
   const uint8_t *sb = wp + N * K / 2 + ((g0 * T) << 7) + r * 4;
   const uint8_t *xl = XF ? xf + lane * 16 : nullptr;   // this lane's unit of every x fragment
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, XF ? 0 : M * ldx * 2);
+  // x's buffer ends with row M - 1's last element, so an offset of a row >= M
+  // that wraps in 32 bits reads x's own bytes or zero, never past the allocation
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, XF ? 0 : ((M - 1) * ldx + K) * 2);
   uint32_t xo[MT];                                 // direct reads: byte offset of this lane's x row, k = 32h
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) xo[mt] = (uint32_t)(((int64_t)(32 * mt + r) * ldx + 32 * h) * 2);
@@ -659,7 +662,9 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
     rc[q] = make_rsrc16(cb + ((q * T) << 10), T << 10);
     rs[q] = make_rsrc16(sb + ((q * T) << 7), T << 7);
   }
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, M * ldx * 2);   // rows >= M read zero
+  // rows >= M read zero, or (an offset wrapped in 32 bits) some of x's own
+  // bytes: the buffer ends with row M - 1's last element
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc16(x, ((M - 1) * ldx + K) * 2);
   uint8_t *slot = reinterpret_cast<uint8_t *>(lds) + wave * SLOT;
   // Lane piece: row m, 8 columns 8 pc of the tile, pc = 2 b + hh for 16-block b
   // and k-half hh; in fragment order it is unit (b, hh, m). Within each group
