@@ -215,6 +215,10 @@ static SkinnyShape skinny_shape(int64_t M, int64_t N, int64_t K, int cus) {
 // Split ranges write FP32 partials (two slots per workgroup) that a fix-up
 // kernel adds in workgroup order.
 constexpr int kMaxKSplit = 8;
+// 1024-element accumulator parts per fix-up workgroup: 2 for 128 x 128 tiles
+// (twice the workgroups of 4 parts: M = 128 on 6144 x 5120 28.1 -> 27.0 us,
+// 5120 x 17408 46.6 -> 45.3 us; 1 part was no better), else 4.
+constexpr int fixup_parts(int TM, int TN) { return TM * TN == 4 ? 2 : 4; }
 // How a tile kernel's x reaches the MFMAs (XP): a fragment-order copy of x
 // that every wave reads into its own registers (kXDirect), or 128 rows staged
 // once per workgroup through LDS and shared by its four waves (kXLds; kXLdsDeep
@@ -1332,7 +1336,9 @@ __global__ __launch_bounds__(kThreads, TM * TN >= 8 || XP == kXLdsDeep ? 1 : 2) 
 template <int TM, int TN, int WGM>
 __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
   constexpr int WGN = 4 / WGM;
-  const int rho = blockIdx.x / (TM * TN), pg = blockIdx.x % (TM * TN);
+  constexpr int PP = fixup_parts(TM, TN);           // 1024-element parts per workgroup
+  constexpr int WPT = 4 * TM * TN / PP;             // workgroups per tile
+  const int rho = blockIdx.x / WPT, pg = blockIdx.x % WPT;
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6, h = lane >> 5, r = lane & 31;
   const int64_t nch = p.K / 64, units = (int64_t)p.rem * nch;
   const int64_t lo = (int64_t)rho * nch, hi = lo + nch;   // the tile's units
@@ -1363,12 +1369,12 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
   // sum is the same as one over the contributors in order.
   const int64_t pbytes = (int64_t)G * 2 * partial_floats<TM, TN>() * 4;
   const __amdgpu_buffer_rsrc_t rp = rsrc(p.partials, pbytes);
-  const int64_t off = (int64_t)(4 * pg) * 1024 + lane * 16 + 4 * q;
-  f32x4_t v[4];
+  const int64_t off = (int64_t)(PP * pg) * 1024 + lane * 16 + 4 * q;
+  f32x4_t v[PP];
 #pragma unroll
-  for (int u = 0; u < 4; u++) v[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int u = 0; u < PP; u++) v[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t w0 = first; w0 <= last; w0 += 4) {
-    f32x4_t t[4][4];
+    f32x4_t t[4][PP];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       const int64_t w = w0 + k;
@@ -1378,7 +1384,7 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
       const int seg = s >= lo ? 0 : 1;
       const int64_t base = ((w * 2 + seg) * partial_floats<TM, TN>() + off) * 4;
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
+      for (int u = 0; u < PP; u++) {
         const uint32_t o = ok ? (uint32_t)(base + u * 4096) : (uint32_t)pbytes;
         t[k][u] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, o, 0, 0));
       }
@@ -1386,12 +1392,12 @@ __global__ __launch_bounds__(kThreads) void big_fixup_kernel(Params p, int G) {
 #pragma unroll
     for (int k = 0; k < 4; k++)
 #pragma unroll
-      for (int u = 0; u < 4; u++) v[u] += t[k][u];
+      for (int u = 0; u < PP; u++) v[u] += t[k][u];
   }
   const float alpha = load_alpha(p.alpha, p.alpha_dev);
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const int part = 4 * pg + u;   // (wave, i, j)
+  for (int u = 0; u < PP; u++) {
+    const int part = PP * pg + u;   // (wave, i, j)
     const int wave = part / (TM * TN), i = (part / TN) % TM, j = part % TN;
     const int wm = wave / WGN, wn = wave % WGN;
     const int64_t col = n0 + wn * 32 * TN + 32 * j + r;
@@ -1545,7 +1551,8 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
     w4a16::big::Params bp{x,     ldx,           w_prep,        y,           ldy,          M,
                           N,     K,             alpha,         alpha_dev,   alpha_col,   (int)b.tiles_m, (int)b.tiles_n,
                           (int)b.full, (int)b.rem, static_cast<float *>(ws), xf, (int)xmt};
-    const unsigned grid = (unsigned)b.G, fix_grid = (unsigned)(b.rem * b.TM * b.TN);
+    const unsigned grid = (unsigned)b.G,
+                   fix_grid = (unsigned)(b.rem * 4 * b.TM * b.TN / w4a16::fixup_parts(b.TM, b.TN));
 #define NVFP4_BIG(TMV, TNV, WGMV)                                                                                \
   w4a16::big::launch_big<TMV, TNV, WGMV>(xpath, alpha_col != nullptr, grid, s, bp);                 \
   if (b.rem > 0) {                                                                                               \
