@@ -197,8 +197,9 @@ static SkinnyShape skinny_shape(int64_t M, int64_t N, int64_t K, int cus) {
 //    per workgroup took 5120 x 17408 at M = 512 from 155 to 131 us, while 24
 //    made 6144 x 5120 at M = 1024, 30 chunks each, slower: 113 against 100 us;
 //    at M = 384, a quarter of the 256-row tiles empty, it was slower too).
-//  * 128 x 256 tiles (one workgroup per CU, x read directly) follow the same
-//    rules. With 2 x 2 waves of 2 x 4 MFMA tiles, 34816 x 5120 at M = 128 took
+//  * 128 x 256 tiles (one workgroup per CU; x read directly, or through LDS
+//    when every tile is split into short ranges) follow the same rules. With
+//    2 x 2 waves of 2 x 4 MFMA tiles, 34816 x 5120 at M = 128 took
 //    84.5 us against 92.6 with 128 x 128 tiles, but both waves of a column
 //    dequantized the same W fragments: nine vector instructions per MFMA, and
 //    the counters showed the MFMA and vector work barely overlapping.
@@ -806,16 +807,18 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
 // ---------------------------------------------------------------- big MFMA kernel (M > 64)
 
 // The W4A4 kernel's structure with x in BF16. Persistent workgroups of 4 waves
-// (2 x 2) over 64TM x 64TN output tiles, each wave owning TM x TN
-// v_mfma_f32_32x32x16_bf16 tiles: 4 x 4 (256 x 256) and 2 x 4 (128 x 256), one
-// workgroup per CU, read x in fragment order straight into registers
-// (tile_mainloop_d); 2 x 2 (128 x 128, two workgroups per CU) stages x
-// through LDS (tile_mainloop).
+// over 32 TM WGM x 32 TN (4 / WGM) output tiles, each wave owning TM x TN
+// v_mfma_f32_32x32x16_bf16 tiles: 256 x 256 (TM = TN = 4, 2 x 2 waves) and
+// 128 x 256 (TM = 4, TN = 2, 1 x 4 waves), one workgroup per CU, read x in
+// fragment order straight into registers (tile_mainloop_d); 128 x 128 (2 x 2
+// tiles, 2 x 2 waves, up to two workgroups per CU) stages x through LDS
+// (tile_mainloop), and so do 128 x 256 tiles that are all split into short K
+// ranges (big_xpath).
 //  * W: each wave loads its TN column groups' fragments of a 64-wide K chunk
 //    straight into registers (one contiguous 1 KB each plus a scale word), two
 //    chunks ahead in a three-deep ring, and dequantizes them exactly to BF16
 //    (E2M1 -> FP32, times the E4M3 scale, -> BF16) one MFMA step ahead.
-//  * x through LDS: the tile's 128 rows x 64 k BF16 (16 KB) are loaded one chunk ahead with
+//  * x through LDS: the tile's 128 rows x 64 k BF16 (16 KB) are loaded one chunk (or kDeepX chunks) ahead with
 //    coalesced 16-byte loads (rows past M read as zero through the buffer range
 //    check), written into one of two LDS buffers and read back as MFMA
 //    fragments. The 16-byte units of a row are XOR-swizzled by row / 2: an LDS
@@ -1265,9 +1268,10 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
   }
 }
 
-// TM x TN MFMA tiles per wave, the 4 waves WGM x (4 / WGM) over the tile:
-// (2, 2, 2) stages x through LDS; (4, 4, 2) and (4, 2, 1) read x straight into
-// registers (tile_mainloop_d).
+// TM x TN MFMA tiles per wave, the 4 waves WGM x (4 / WGM) over the tile; XP
+// is the x path (big_xpath): the fragment-order copy read straight into
+// registers (tile_mainloop_d), or x staged through LDS (tile_mainloop), with
+// the deeper register rings when the grid holds one workgroup per CU.
 // COLS: p.alpha_col is set (a separate instantiation, so that the kernel
 // without a per-column scale keeps its registers for the main loop).
 template <int TM, int TN, int WGM, bool COLS, int XP>
