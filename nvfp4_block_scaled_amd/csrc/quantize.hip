@@ -1,7 +1,14 @@
-// BF16 -> NVFP4 activation quantizer: a tensor-max pass and a block pass (and,
-// for the two-pass prefill, a residual pass per block inside the block pass).
+// BF16 -> NVFP4 activation quantizer (and, for the two-pass prefill, a
+// residual pass per block). The global scale needs the maximum of |x| over the
+// whole tensor before any block can be encoded. Two forms:
+//  * one read of x (quantize_fused_kernel): when x fits in the vector registers
+//    of a grid of one 1024-thread workgroup per CU (up to 5 tiles of 32 x 64 per
+//    wave, 80 MiB of BF16 on 256 CUs), every workgroup loads its tiles once,
+//    publishes its maximum, waits at a grid-wide barrier and encodes from the
+//    registers;
+//  * two reads (amax_kernel, then a block pass) for anything larger.
 //
-// Both passes are HBM-bound. Every floating-point step is a single IEEE
+// Both forms are HBM-bound. Every floating-point step is a single IEEE
 // binary32 operation with round-to-nearest-even (no contraction, no fast math),
 // in the order stated in nvfp4.h, so the output is bit-identical to any other
 // implementation of that order. The E4M3 scale is rounded with integer logic.
@@ -93,13 +100,20 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red) {
   return red[kThreads / 64];
 }
 
-// Pass 1: per-workgroup maximum of |x| bit patterns over a grid-strided range.
+// Pass 1: per-workgroup maximum of |x| bit patterns over a grid-strided range,
+// four independent 16-byte loads in flight per thread.
 __global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4_t *__restrict__ x, int64_t n16,
                                                         uint32_t *__restrict__ partial) {
   __shared__ uint32_t red[kThreads / 64 + 1];
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kThreads)
-    m = max(m, absmax8(x[i]));
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = __builtin_nontemporal_load(x + i), b = __builtin_nontemporal_load(x + i + stride);
+    const u32x4_t c = __builtin_nontemporal_load(x + i + 2 * stride), d = __builtin_nontemporal_load(x + i + 3 * stride);
+    m = max(m, max(max(absmax8(a), absmax8(b)), max(absmax8(c), absmax8(d))));
+  }
+  for (; i < n16; i += stride) m = max(m, absmax8(x[i]));
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
@@ -308,6 +322,309 @@ __global__ __launch_bounds__(kThreads) void quantize_two_pass_tiled_kernel(
   }
 }
 
+// ---------------------------------------------------------------- one read of x
+//
+// One workgroup of 1024 threads per CU. Workgroup w owns the run of myrun <= 80
+// tiles (32 rows x 64 columns) w run .. w run + myrun - 1 in storage order, that
+// is myrun * 256 16-byte chunks of x: cell (r, t) is row r of the run's tile t
+// (128 contiguous bytes of x), and chunk c of the run is chunk c % 8 of cell
+// e = c / 8, cells ordered tile-major (t = e / 32, r = e % 32). Thread tau holds
+// chunks tau + 1024 i (i < kFusedChunks, 80 VGPRs), i.e. chunk q = tau % 8 of
+// row r = (tau / 8) % 32 of tile t = tau / 256 + 4 i: one load instruction of a
+// wave reads eight whole 128-byte rows of one tile, one code store of a wave
+// writes two whole 128-byte lines of its tile's codes, and threads tau and
+// tau ^ 1 hold the two halves of one 16-element block.
+//
+// Each workgroup stores the maximum of |x| bit patterns over its run in its
+// slot of the workspace and waits until all gridDim.x slots are filled.
+// slots_reset_kernel, launched just before on the same stream, sets the slots
+// to kEmpty (a BF16 magnitude is at most 0x7FFF, so no maximum equals it), so
+// a workspace needs no initialisation and a captured graph replays as it ran.
+// A slot carries its own "filled" mark, so its reader needs no ordering with
+// any other location; slot stores and loads are agent-scope atomics (coherent
+// across the XCDs). The host launches this form only when the whole grid fits
+// on the device at once (the occupancy query), so every workgroup reaches its
+// store; the wait is bounded all the same (kSpinLimit polls, about a second),
+// and a workgroup whose wait runs out encodes its run with g = NaN.
+//
+// With g known, the workgroup tabulates g / scale for the 127 scale bytes
+// (and, for the two-pass form, fl32(code * scale / g) for each scale byte and
+// code) in LDS and encodes and stores its chunks one by one.
+static constexpr int kFusedThreads = 1024;
+static constexpr int kFusedWaves = kFusedThreads / 64;
+static constexpr int kFusedChunks = 20;
+static constexpr int kFusedRun = kFusedChunks * kFusedThreads / 256;   // 80 tiles per workgroup at most
+static constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+static constexpr int kSpinLimit = 1 << 20;
+
+__global__ __launch_bounds__(256) void slots_reset_kernel(uint32_t *slots, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    __hip_atomic_store(slots + i, kEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// n / d for 0 <= n < 2^22 and 1 <= d < 2^22: an FP32 estimate, then one
+// correction each way (the estimate is within one of the quotient).
+__device__ __forceinline__ int div_small(int n, int d, float inv_d) {
+  int q = (int)((float)n * inv_d);
+  if (q * d > n) q--;
+  if ((q + 1) * d <= n) q++;
+  return q;
+}
+
+// E2M1 codes of eight elements (a 16-byte chunk of BF16, element 2i in the low
+// half of word i) times r: four code bytes, element 2i in the low nibble of byte i.
+__device__ __forceinline__ uint32_t codes8(const u32x4_t v, float r) {
+  uint32_t out = 0u;
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(v[0] << 16) * r,
+                                                 __uint_as_float(v[0] & 0xFFFF0000u) * r, 1.0f, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(v[1] << 16) * r,
+                                                 __uint_as_float(v[1] & 0xFFFF0000u) * r, 1.0f, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(v[2] << 16) * r,
+                                                 __uint_as_float(v[2] & 0xFFFF0000u) * r, 1.0f, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(v[3] << 16) * r,
+                                                 __uint_as_float(v[3] & 0xFFFF0000u) * r, 1.0f, 3);
+  return out;
+}
+
+// Scale byte of a block from its |x| maximum under g: E4M3 of amax / 6 * g,
+// 0 for an all-zero block.
+__device__ __forceinline__ uint32_t block_scale_byte(float amax, float g) {
+  if (amax == 0.0f) return 0u;
+  const float t = amax / 6.0f;
+  const float u = t * g;
+  return e4m3_rne_sat(u);
+}
+
+// The value of the neighbouring lane of a pair (lane ^ 1), by a DPP quad
+// permutation (no LDS round trip).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
+}
+
+// The four scale bytes of a cell (blocks 0..3, held by its threads q = 0, 2, 4,
+// 6) as one word, in the thread with q = 0 (DPP row shifts: lane + 2, + 4, + 6
+// stay inside the 16-lane row).
+__device__ __forceinline__ uint32_t cell_scales(uint32_t sb) {
+  const uint32_t s1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x102, 0xF, 0xF, false);   // row_shl:2
+  const uint32_t s2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x104, 0xF, 0xF, false);   // row_shl:4
+  const uint32_t s3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x106, 0xF, 0xF, false);   // row_shl:6
+  return sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+}
+
+// e4m3_rne_sat without branches: both roundings formed, one selected.
+__device__ __forceinline__ uint32_t e4m3_rne_sat_sel(float u) {
+  const uint32_t b = __float_as_uint(u);
+  const uint32_t bn = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;   // 3 mantissa bits, RNE
+  const uint32_t norm = (((bn >> 23) - 120u) << 3) | ((bn >> 20) & 7u);
+  const uint32_t sub = (uint32_t)__builtin_rintf(u * 512.0f);          // below 2^-6: step 2^-9
+  const uint32_t r = (u < 0.015625f) ? sub : norm;
+  return (u < 448.0f) ? r : 0x7Eu;                                       // >= 448, +inf or NaN
+}
+
+// fl32(a / 6) for a BF16 value a >= 0: a * fl32(1/6) corrected by one FMA step,
+// which equals the IEEE division for every BF16 a >= 2^-120 (checked
+// exhaustively); smaller a, whose quotient may be subnormal, divide.
+__device__ __forceinline__ float bf16_div6(float a) {
+  const float c = 1.0f / 6.0f;
+  const float t0 = a * c;
+  const float r = __builtin_fmaf(-t0, 6.0f, a);
+  const float t = __builtin_fmaf(r, c, t0);
+  return (a >= 0x1p-120f) ? t : a / 6.0f;
+}
+
+// MODE 0: row-major codes [rows][K/2] (out) and scales [rows][K/16] (scales_rm);
+// MODE 1: the tile layout (out), as quantize_tiled_kernel;
+// MODE 2: the two-pass tile layout (out), as quantize_two_pass_tiled_kernel.
+// x and the outputs of this form are under 2^31 bytes (x fits in the
+// registers), so 32-bit indices suffice.
+template <int MODE>
+__global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
+    const u32x4_t *__restrict__ x, int rows, int K, int ntiles, int run, float inv_kt, uint32_t *slots,
+    uint8_t *__restrict__ out, uint8_t *__restrict__ scales_rm, float *__restrict__ g_out,
+    float *__restrict__ inv_g_out) {
+  __shared__ uint32_t red[kFusedWaves + 1];
+  __shared__ float rtab[128];                                     // g / scale, per scale byte
+  __shared__ float qtab[MODE == 2 ? 128 * 16 : 1];                // fl32(code * scale / g)
+  const int tau = threadIdx.x, wave = tau >> 6, lane = tau & 63, q = tau & 7;
+  const int kt = K / 64, x_row = K / 8;
+  const int tile0 = (int)blockIdx.x * run;
+  const int myrun = min(run, ntiles - tile0);            // the last run may be shorter
+  const int r = (tau >> 3) & 31, t_base = tau >> 8;      // this thread's row and first tile
+
+  u32x4_t v[kFusedChunks];
+#pragma unroll
+  for (int i = 0; i < kFusedChunks; i++) {
+    const int tile = tile0 + t_base + 4 * i;
+    const int rg = div_small(tile, kt, inv_kt), kk = tile - rg * kt;
+    const int row = rg * 32 + r;
+    v[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (t_base + 4 * i < myrun && row < rows) v[i] = __builtin_nontemporal_load(x + (row * x_row + kk * 8 + q));
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kFusedChunks; i++) m = max(m, absmax8(v[i]));
+  m = wave_max_u32(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t bm = wave_max_u32(lane < kFusedWaves ? red[lane] : 0u);
+    if (lane == 0) __hip_atomic_store(slots + blockIdx.x, bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t tm = kEmpty;
+    for (int it = 0; it < kSpinLimit; it++) {
+      // every slot this lane polls, loaded at once (at most 1024 slots: 16 a lane)
+      uint32_t u[16];
+#pragma unroll
+      for (int k = 0; k < 16; k++)
+        u[k] = (lane + 64 * k < (int)gridDim.x)
+                   ? __hip_atomic_load(slots + lane + 64 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : 0u;
+      uint32_t mm = 0;
+      int full = 1;
+#pragma unroll
+      for (int k = 0; k < 16; k++) {
+        full &= (u[k] != kEmpty);
+        mm = max(mm, u[k]);
+      }
+      if (__all(full)) {
+        tm = wave_max_u32(mm);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) red[kFusedWaves] = tm;
+  }
+  __syncthreads();
+  const uint32_t tmb = red[kFusedWaves];
+  float g;
+  if (tmb == kEmpty) {
+    g = __builtin_nanf("");
+  } else {
+    const float amax_t = __uint_as_float(tmb << 16);
+    g = (amax_t == 0.0f) ? 1.0f : 2688.0f / amax_t;
+  }
+  if (blockIdx.x == 0 && tau == 0) {
+    g_out[0] = g;
+    if (inv_g_out) inv_g_out[0] = 1.0f / g;
+  }
+  if (tau < 128) rtab[tau] = g / e4m3_value(tau);      // entry 0 is only read for zero blocks
+  if (MODE == 2) {
+    for (int k = tau; k < 128 * 16; k += kFusedThreads) {
+      const float code = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((uint32_t)(k & 15), 1.0f, 0)[0];
+      qtab[k] = (code * e4m3_value((uint32_t)(k >> 4))) / g;
+    }
+  }
+  __syncthreads();
+
+  // the indices and block maxima are recomputed below from copies of tau and x
+  // the compiler cannot see through, so it does not keep phase 1's 20 sets of
+  // them live across the wait (they would not fit beside x in the registers)
+  int tau2 = tau;
+  asm volatile("" : "+v"(tau2));
+#pragma unroll
+  for (int i = 0; i < kFusedChunks; i++) asm volatile("" : "+v"(v[i]));
+  const int t2_base = tau2 >> 8;
+  const int code_off = (32 * (q >> 2) + r) * 16 + (q & 3) * 4;   // this thread's word in a tile's codes
+  const int ntiles_out = (MODE == 2) ? 2 * ntiles : ntiles;
+  uint8_t *const scale_base = out + (size_t)ntiles_out * 1024;
+#pragma unroll
+  for (int i = 0; i < kFusedChunks; i++) {
+    const int t = t2_base + 4 * i;
+    const bool have = t < myrun;                                  // the same for the whole wave
+    const int tile = tile0 + t;
+    // the block's maximum from its two halves (both threads run the exchange)
+    const uint32_t mh = absmax8(v[i]);
+    const uint32_t mb = max(mh, pair_swap(mh));
+    const uint32_t sb = e4m3_rne_sat_sel(bf16_div6(__uint_as_float(mb << 16)) * g);   // 0 for a zero block
+    uint32_t w = codes8(v[i], rtab[sb]);
+    w = sb ? w : 0u;
+    if (MODE == 0) {
+      const int rg = div_small(tile, kt, inv_kt), kk = tile - rg * kt;
+      const int row = rg * 32 + r;
+      if (have && row < rows) {
+        *reinterpret_cast<uint32_t *>(out + (row * (K / 2) + kk * 32 + q * 4)) = w;
+        if ((q & 1) == 0) scales_rm[row * (K / 16) + kk * 4 + (q >> 1)] = (uint8_t)sb;
+      }
+    } else {
+      int t1 = tile;
+      if (MODE == 2) {
+        const int rg = div_small(tile, kt, inv_kt), kk = tile - rg * kt;
+        t1 = rg * 2 * kt + kk;
+      }
+      const uint32_t s4 = cell_scales(sb);
+      if (have) {
+        *reinterpret_cast<uint32_t *>(out + (t1 * 1024 + code_off)) = w;
+        if (q == 0) *reinterpret_cast<uint32_t *>(scale_base + (t1 * 128 + 4 * r)) = s4;
+      }
+      if (MODE == 2) {
+        // residual of the eight elements: x - fl32(code * scale / g)
+        const float *qs = qtab + sb * 16;
+        float res[8];
+        float ra = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          res[2 * b] = __uint_as_float(v[i][b] << 16) - qs[(w >> (8 * b)) & 15u];
+          res[2 * b + 1] = __uint_as_float(v[i][b] & 0xFFFF0000u) - qs[(w >> (8 * b + 4)) & 15u];
+          ra = fmaxf(ra, fmaxf(fabsf(res[2 * b]), fabsf(res[2 * b + 1])));
+        }
+        const float rb = fmaxf(ra, __uint_as_float(pair_swap(__float_as_uint(ra))));
+        const uint32_t sb2 = block_scale_byte(rb, g);
+        uint32_t w2 = 0u;
+        if (sb2) {
+          const float rr = rtab[sb2];
+          w2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w2, res[0] * rr, res[1] * rr, 1.0f, 0);
+          w2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w2, res[2] * rr, res[3] * rr, 1.0f, 1);
+          w2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w2, res[4] * rr, res[5] * rr, 1.0f, 2);
+          w2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w2, res[6] * rr, res[7] * rr, 1.0f, 3);
+        }
+        const uint32_t s4b = cell_scales(sb2);
+        if (have) {
+          const int t2 = t1 + kt;
+          *reinterpret_cast<uint32_t *>(out + (t2 * 1024 + code_off)) = w2;
+          if (q == 0) *reinterpret_cast<uint32_t *>(scale_base + (t2 * 128 + 4 * r)) = s4b;
+        }
+      }
+    }
+    // one chunk at a time: interleaving chunks would need registers x holds
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Whether each instantiation fits at least once on every CU (then a grid of up
+// to num_cus workgroups is resident at once), per device.
+static bool g_fused_fits[kMaxDevices][3];
+static std::once_flag g_fused_once[kMaxDevices];
+
+static void query_fused(int dev) {
+  int nb = 0;
+  g_fused_fits[dev][0] = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize_fused_kernel<0>,
+                                                                      kFusedThreads, 0) == hipSuccess && nb >= 1;
+  nb = 0;
+  g_fused_fits[dev][1] = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize_fused_kernel<1>,
+                                                                      kFusedThreads, 0) == hipSuccess && nb >= 1;
+  nb = 0;
+  g_fused_fits[dev][2] = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize_fused_kernel<2>,
+                                                                      kFusedThreads, 0) == hipSuccess && nb >= 1;
+}
+
+// Tiles per workgroup (run) and grid of the one-read form for `ntiles` tiles
+// on `cus` CUs; *grid = 0 when x does not fit.
+static void fused_shape(int64_t ntiles, int cus, int *run, int64_t *grid) {
+  *run = 0;
+  *grid = 0;
+  if (ntiles <= 0 || cus <= 0) return;
+  const int64_t wgs = std::min<int64_t>(cus, kAmaxBlocks);
+  const int64_t r = (ntiles + wgs - 1) / wgs;
+  if (r > kFusedRun) return;
+  *run = (int)r;
+  *grid = (ntiles + r - 1) / r;
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -325,6 +642,32 @@ nvfp4_status quantize_common(const uint16_t *x, int64_t rows, int64_t K, int mod
   DeviceInfo d;
   nvfp4_status st = device_info(&d);
   if (st != NVFP4_OK) return st;
+  std::call_once(g_fused_once[d.device], query_fused, d.device);
+  // one read of x when it fits in the registers of one resident grid
+  if (K % 64 == 0 && g_fused_fits[d.device][mode]) {
+    const int64_t ntiles = (rows + 31) / 32 * (K / 64);
+    int run = 0;
+    int64_t grid = 0;
+    fused_shape(ntiles, d.num_cus, &run, &grid);
+    if (grid > 0) {
+      const float inv_kt = 1.0f / (float)(K / 64);
+      hipLaunchKernelGGL(slots_reset_kernel, dim3(1), dim3(256), 0, s, (uint32_t *)ws, (int)grid);
+      NVFP4_LAUNCH_CHECK();
+#define NVFP4_FUSED(M)                                                                                              \
+  hipLaunchKernelGGL(quantize_fused_kernel<M>, dim3((unsigned)grid), dim3(kFusedThreads), 0, s, (const u32x4_t *)x, \
+                     (int)rows, (int)K, (int)ntiles, run, inv_kt, (uint32_t *)ws, (uint8_t *)codes, scales,  \
+                     g_dev, inv_g_dev)
+      if (mode == 0)
+        NVFP4_FUSED(0);
+      else if (mode == 1)
+        NVFP4_FUSED(1);
+      else
+        NVFP4_FUSED(2);
+#undef NVFP4_FUSED
+      NVFP4_LAUNCH_CHECK();
+      return NVFP4_OK;
+    }
+  }
   const int64_t n16 = rows * K / 8;          // 16-byte chunks of x
   const int64_t nblocks = rows * K / 16;     // 16-element blocks
   hipLaunchKernelGGL(amax_kernel, dim3(kAmaxBlocks), dim3(kThreads), 0, s, (const u32x4_t *)x, n16,

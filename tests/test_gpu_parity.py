@@ -161,6 +161,122 @@ def test_quantize_prefill_activation_full():
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
 
 
+_ORACLE_Q = {}
+
+
+def _oracle_q(rows, K, two):
+    """The oracle's one- or two-pass quantization of the seeded [rows][K] activation, cached."""
+    key = (rows, K, two)
+    if key not in _ORACLE_Q:
+        x = synth.normal_bf16(7000 + rows, rows, K)
+        _ORACLE_Q[key] = (x, quantize.two_pass(x) if two else quantize.quantize(x))
+    return _ORACLE_Q[key]
+
+
+@pytest.mark.parametrize("extra", [0, 1])
+@pytest.mark.parametrize("form", ["row_major", "tiled", "two_pass"])
+def test_quantize_at_and_past_register_capacity(form, extra):
+    """The quantizer reads x once when its 32 x 64 tiles fit in the registers of one resident grid
+    (5 tiles per wave, 16 waves per CU: 32 rows of 5120 columns per CU) and twice otherwise. At
+    exactly that capacity (extra = 0: the one-read form with every register tile in use) and one
+    row past it (extra = 1: the two-read form), every byte and g against the oracle, for the
+    row-major, tiled and two-pass outputs."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    K = 5120
+    rows = min(cus, 1024) * 32 + extra
+    x, ref = _oracle_q(rows, K, form == "two_pass")
+    _progress(f"quantize {form} rows={rows} K={K}")
+    xd = dev(x).view(torch.bfloat16)
+    Mp = -(-rows // 32) * 32
+    if form == "row_major":
+        codes, scales, g, ig = nv.nvfp4_quantize(xd)
+        c_ref, s_ref, g_ref, ig_ref = ref
+        np.testing.assert_array_equal(host(codes), c_ref)
+        np.testing.assert_array_equal(host(scales), s_ref)
+    elif form == "tiled":
+        at, g, ig = nv.nvfp4_quantize_tiled(xd)
+        c_ref, s_ref, g_ref, ig_ref = ref
+        cp = np.zeros((Mp, K // 2), np.uint8)
+        sp = np.zeros((Mp, K // 16), np.uint8)
+        cp[:rows], sp[:rows] = c_ref, s_ref
+        lay, _ = prepared.prepare_weight(cp, sp, "ue4m3")
+        np.testing.assert_array_equal(host(at), lay)
+    else:
+        a2, g, ig = nv.nvfp4_quantize_two_pass_tiled(xd)
+        c1, s1, c2, s2, g_ref, ig_ref = ref
+        cp = np.zeros((Mp, K), np.uint8)
+        sp = np.zeros((Mp, K // 8), np.uint8)
+        cp[:rows], sp[:rows] = np.concatenate([c1, c2], axis=1), np.concatenate([s1, s2], axis=1)
+        lay, _ = prepared.prepare_weight(cp, sp, "ue4m3")
+        np.testing.assert_array_equal(host(a2), lay)
+    assert np.float32(g.item()) == g_ref and np.float32(ig.item()) == ig_ref
+
+
+@pytest.mark.parametrize("rows,K", [(256, 5120), (77, 640), (8192, 5120), (1, 64), (33, 17408)])
+@pytest.mark.parametrize("form", ["row_major", "tiled", "two_pass"])
+def test_quantize_writes_stay_in_bounds(form, rows, K):
+    """Every output of the quantizer sits between guard bytes (one slab, the outputs carved out of
+    it with guards before and after each): the guards are unchanged after the call, and the
+    outputs equal those of a call on separately allocated buffers. Shapes whose tiles split into
+    unequal per-workgroup runs (256 x 5120: 640 tiles as 213 runs of 3 and one of 1)."""
+    G = 4096
+    x = synth.normal_bf16(rows + 3 * K, rows, K)
+    xd = dev(x).view(torch.bfloat16)
+    if form == "row_major":
+        sizes = [rows * K // 2, rows * K // 16]
+    elif form == "tiled":
+        sizes = [int(nv.lib().nvfp4_tiled_activation_bytes(rows, K))]
+    else:
+        sizes = [int(nv.lib().nvfp4_tiled_activation_bytes(rows, 2 * K))]
+    sizes += [4, 4]                                        # g, inv_g
+    total = G + sum(-(-n // 256) * 256 + G for n in sizes)
+    slab = torch.full((total,), 0xA5, dtype=torch.uint8, device="cuda")
+    views, off = [], G
+    for n in sizes:
+        views.append(slab[off:off + n])
+        off += -(-n // 256) * 256 + G
+    g, ig = views[-2].view(torch.float32), views[-1].view(torch.float32)
+    if form == "row_major":
+        nv.nvfp4_quantize(xd, views[0], views[1], g, ig)
+        ref = nv.nvfp4_quantize(xd)
+        outs = [views[0].view(rows, K // 2), views[1].view(rows, K // 16), g, ig]
+    elif form == "tiled":
+        nv.nvfp4_quantize_tiled(xd, views[0], g, ig)
+        ref = nv.nvfp4_quantize_tiled(xd)
+        outs = [views[0], g, ig]
+    else:
+        nv.nvfp4_quantize_two_pass_tiled(xd, views[0], g, ig)
+        ref = nv.nvfp4_quantize_two_pass_tiled(xd)
+        outs = [views[0], g, ig]
+    torch.cuda.synchronize()
+    mask = torch.ones(total, dtype=torch.bool, device="cuda")
+    off = G
+    for n in sizes:
+        mask[off:off + n] = False
+        off += -(-n // 256) * 256 + G
+    assert bool((slab[mask] == 0xA5).all()), "a quantizer write landed outside its output"
+    for a, b in zip(outs, ref):
+        assert torch.equal(a.reshape(-1), b.reshape(-1))
+
+
+def test_quantize_repeat_calls_new_maximum():
+    """Calls in a row on one workspace, each input with a different tensor maximum (larger, then
+    smaller, then zero): no call may see the previous call's per-workgroup maxima."""
+    ws = torch.empty(nv.workspace_bytes(nv.OP_QUANTIZE, 2048, 0, 640), dtype=torch.uint8, device="cuda")
+    for i, scale in enumerate([1.0, 50.0, 0.01, 0.0]):
+        x = synth.normal_bf16(300 + i, 2048, 640, std=max(scale, 1e-3))
+        if scale == 0.0:
+            x[:] = 0
+        xd = dev(x).view(torch.bfloat16)
+        at, g, ig = nv.nvfp4_quantize_tiled(xd, ws=ws)
+        torch.cuda.synchronize()
+        c_ref, s_ref, g_ref, ig_ref = quantize.quantize(x)
+        assert np.float32(g.item()) == g_ref, f"call {i}"
+        cp = c_ref.reshape(2048, 320)
+        lay, _ = prepared.prepare_weight(cp, s_ref, "ue4m3")
+        np.testing.assert_array_equal(host(at), lay)
+
+
 # ------------------------------------------------------------------ W4A4
 
 def _w4a4(a, sa, b, sb, alpha, out_dtype, alpha_dev=None):
