@@ -140,12 +140,19 @@ def sustained_clock(fn, seconds=3.0, settle=1.2):
     return st
 
 
-def time_steps(fn, steps, warmup, sampler=None):
+def time_steps(fn, steps, warmup, sampler=None, warm_s=0.0):
     """Warm-up, then `steps` calls bracketed by synchronisations, with an event before and after
-    each call on the launch stream: (mean ms per call over the whole region, min ms per call)."""
+    each call on the launch stream: (mean ms per call over the whole region, min ms per call).
+    The warm-up is `warmup` calls, continued until at least `warm_s` seconds have passed (short
+    calls need many more than `warmup` to bring the clock to where it settles under load)."""
     import torch
-    for _ in range(warmup):
+    t0 = time.time()
+    n = 0
+    while n < warmup or time.time() - t0 < warm_s:
         fn()
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ctx = sampler if sampler is not None else _Null()
@@ -168,8 +175,13 @@ class _Null:
         pass
 
 
-def time_calls(fn, steps, warmup):
-    return time_steps(fn, steps, warmup)[0]
+def time_calls(fn, steps, warmup, warm_s=0.0):
+    return time_steps(fn, steps, warmup, warm_s=warm_s)[0]
+
+
+# untimed warm-up of the short legs (the 2048^3 and 4096^3 squares, the prefill parts): at
+# least this long, so that they are timed at the clock the chip settles at, as the headline is
+WARM_S_SHORT = 0.3
 
 
 def graph_time(calls, reps=3):
@@ -230,7 +242,7 @@ def square_large_device(S, operand):
     return out
 
 
-def w4a4_square(nv, S, steps, warmup, gen=None, standard_too=False, clock=False):
+def w4a4_square(nv, S, steps, warmup, gen=None, standard_too=False, clock=False, warm_s=0.0):
     """Step = the W4A4 GEMM on A as the quantizer emits it for the GEMM (the tile layout,
     nvfp4_quantize_tiled) and B prepared once: nvfp4_gemm_w4a4_tiled with the library's config.
     Returns dict(ms, ms_min, TFLOPs, ...); with standard_too, also the per-column-alpha call and
@@ -248,10 +260,12 @@ def w4a4_square(nv, S, steps, warmup, gen=None, standard_too=False, clock=False)
     gws = nv.workspace(nv.OP_W4A4_TILED, S, S, S)
     cfg = nv.get_config(nv.OP_W4A4_TILED, S, S, S)
     step = lambda: nv.nvfp4_gemm_w4a4_tiled(at, S, wp, S, S, alpha, None, "bf16", out, ws=gws)
-    ms, ms_min = time_steps(step, steps, warmup)
+    ms, ms_min = time_steps(step, steps, warmup, warm_s=warm_s)
     fl = 2.0 * S ** 3
     r = dict(ms=round(ms, 5), ms_min=round(ms_min, 5), TFLOPs=round(fl / (ms * 1e-3) / 1e12, 1),
              TFLOPs_at_min=round(fl / (ms_min * 1e-3) / 1e12, 1), config=cfg.as_dict())
+    if warm_s:
+        r["warmup_min_s"] = warm_s
     if clock:
         r["sustained_clock"] = sustained_clock(step)
     if standard_too:
@@ -391,13 +405,14 @@ def prefill(nv, steps, warmup):
     def step2():
         quant2()
         gemm2()
-    q_ms, q_min = time_steps(quant, steps, warmup)
-    g_ms, g_min = time_steps(gemm, steps, warmup)
-    t_ms, t_min = time_steps(step, steps, warmup)
-    r_ms = time_calls(step_row_major, steps, warmup)
-    q2_ms = time_calls(quant2, steps, warmup)
-    g2_ms = time_calls(gemm2, steps, warmup)
-    t2_ms = time_calls(step2, steps, warmup)
+    W = WARM_S_SHORT
+    q_ms, q_min = time_steps(quant, steps, warmup, warm_s=W)
+    g_ms, g_min = time_steps(gemm, steps, warmup, warm_s=W)
+    t_ms, t_min = time_steps(step, steps, warmup, warm_s=W)
+    r_ms = time_calls(step_row_major, steps, warmup, warm_s=W)
+    q2_ms = time_calls(quant2, steps, warmup, warm_s=W)
+    g2_ms = time_calls(gemm2, steps, warmup, warm_s=W)
+    t2_ms = time_calls(step2, steps, warmup, warm_s=W)
     sched = {}
     for name, c in (("quadrants", nv.make_config(nv.KERNEL_W4A4_TILES, 256, 256, nv.TAIL_QUADRANTS)),
                     ("split2", nv.make_config(nv.KERNEL_W4A4_TILES, 256, 256, nv.TAIL_SPLIT, 2)),
@@ -409,11 +424,11 @@ def prefill(nv, steps, warmup):
                                                       dynamic=1))):
         ws = nv.workspace(nv.OP_W4A4_TILED, M, N, K, config=c)
         ms = time_calls(lambda: nv.nvfp4_gemm_w4a4_tiled(at, M, wp, N, K, alpha_w, ig, "bf16", out, config=c, ws=ws),
-                        steps, warmup)
+                        steps, warmup, warm_s=W)
         sched[name] = round(ms, 4)
     q_bytes = M * K * 2 + M * K // 2 + M * K // 16
     fl = 2.0 * M * N * K
-    return dict(M=M, N=N, K=K, config=cfg.as_dict(), quantize_us=round(q_ms * 1e3, 1),
+    return dict(M=M, N=N, K=K, config=cfg.as_dict(), warmup_min_s=W, quantize_us=round(q_ms * 1e3, 1),
                 quantize_us_min=round(q_min * 1e3, 1), quantize_GBps=round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                 quantize_hbm_frac=round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
                 gemm_ms=round(g_ms, 4), gemm_ms_min=round(g_min, 4), gemm_TFLOPs=round(fl / (g_ms * 1e-3) / 1e12, 1),
@@ -519,6 +534,7 @@ def cpu_baseline(S=8192, rows=2048, cols=8192):
 
 
 def main():
+    global WARM_S_SHORT
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -531,11 +547,16 @@ def main():
                     help="only the W4A16 M = 1 decode shapes (one JSON line; for profiling the decode kernels)")
     ap.add_argument("--sweep-only", action="store_true",
                     help="only the W4A16 M > 1 layer sweep (one JSON line; for profiling the MFMA kernels)")
+    ap.add_argument("--warm-s", type=float, default=WARM_S_SHORT,
+                    help="least untimed warm-up of the short legs, in seconds (0 under a profiler)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill leg (one JSON line; for profiling the quantizer and its GEMM)")
     ap.add_argument("--square-only", type=int, default=0,
                     help="only the W4A4 square of this size (one JSON line; for profiling at 16k / 32k)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
+    WARM_S_SHORT = args.warm_s
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
@@ -558,6 +579,9 @@ def main():
     if args.sweep_only:
         print(json.dumps({"w4a16_m_sweep": [r for j in range(len(synth.DECODE_SHAPES))
                                             for r in w4a16_m_sweep(nv, j)]}), flush=True)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill_w4a4": prefill(nv, max(10, args.steps // 2), args.warmup)}), flush=True)
         return
     if args.square_only:
         s2 = args.square_only
@@ -620,7 +644,7 @@ def main():
         extras["w4a16_m_sweep"] = [r for j in range(len(synth.DECODE_SHAPES)) for r in w4a16_m_sweep(nv, j)]
         sweep = {}
         for s2 in (2048, 4096):
-            sweep[str(s2)] = w4a4_square(nv, s2, args.steps, args.warmup)
+            sweep[str(s2)] = w4a4_square(nv, s2, args.steps, args.warmup, warm_s=WARM_S_SHORT)
             log(f"[bench] W4A4 {s2}^3: {sweep[str(s2)]}")
         if not args.no_large:
             for s2 in (16384, 32768):

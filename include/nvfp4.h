@@ -116,8 +116,10 @@ size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
  * output tiles: M rounded up to the tile rows, * K * 2 bytes) after the FP32
  * partial tiles of output tiles split along K (M > 64 when the tiles do not
  * fill whole rounds of the CUs; the tile shape and this size depend on the
- * device's CU count); or per-workgroup maxima (quantize). Every call
- * overwrites what it reads. */
+ * device's CU count); or, for the quantizer (12.25 KiB), per-workgroup maxima
+ * and the one-read form's barrier slots with the generation number that tags
+ * them. Every call overwrites what it reads, or (the quantizer's slots) tags
+ * it with a generation it advances, so no workspace needs initialising. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* The configuration a GEMM call with config == NULL uses for (op, M, N, K) on
@@ -301,11 +303,12 @@ nvfp4_status nvfp4_quantize_two_pass_tiled(const uint16_t *x, int64_t rows, int6
 /* nvfp4_quantize_tiled for callers that cannot allocate device memory: code
  * under graph capture, tight serving loops, and harnesses that forbid
  * allocation. It takes no workspace and allocates nothing (no hipMalloc, no
- * hipFree): the 4 KiB the quantizer needs (the tensor-max pass's per-workgroup
- * maxima) live in a static device array of the library, one per GPU, held
+ * hipFree): the 12.25 KiB the quantizer needs (the tensor-max pass's
+ * per-workgroup maxima, or the one-read form's barrier slots and generation
+ * number) live in a static device array of the library, one per GPU, held
  * until the process ends. That size does not depend on rows or K, so no input
- * is too large for it; every call rewrites all of it before reading it, so
- * nothing needs clearing between calls. Calls that overlap on one GPU (on
+ * is too large for it, and nothing needs clearing between calls (each call
+ * writes what it reads, or tags it with a generation number it advances). Calls that overlap on one GPU (on
  * different streams) share that array and race: serialise them. The first
  * call on a device looks up the array's address there; nvfp4_init(device)
  * does it up front. Arguments, outputs and errors as for nvfp4_quantize_tiled. */

@@ -26,20 +26,25 @@ namespace nvfp4 {
 
 static constexpr int kAmaxBlocks = 1024;   // workgroups of the tensor-max pass
 static constexpr int kThreads = 256;
+// The workspace: the tensor-max pass's per-workgroup maxima (kAmaxBlocks
+// words), then the one-read form's barrier state: a generation word (16 bytes
+// reserved) and one 64-bit slot per workgroup (at most kAmaxBlocks).
+static constexpr size_t kFusedStateOff = (size_t)kAmaxBlocks * 4;
+static constexpr size_t kFusedSlotsOff = kFusedStateOff + 16;
+static constexpr size_t kQuantizeWsBytes = (kFusedSlotsOff + (size_t)kAmaxBlocks * 8 + 255) / 256 * 256;
 
 size_t quantize_workspace_bytes(int64_t rows, int64_t K) {
   (void)rows;
   (void)K;
-  return (size_t)kAmaxBlocks * sizeof(uint32_t);
+  return kQuantizeWsBytes;
 }
 
-// The quantizer's workspace for callers that cannot allocate: the tensor-max
-// pass's per-workgroup maxima, kAmaxBlocks words (4 KiB) whatever the input
-// size, in a device array of the library's own. Host code never passes
-// `scratch` itself to a kernel (on the host it names a host-side stand-in):
-// it passes the device address that hipGetSymbolAddress returns for it, looked
-// up once per device with that device current.
-static __device__ __align__(256) uint32_t scratch[kAmaxBlocks];
+// The quantizer's workspace for callers that cannot allocate (kQuantizeWsBytes,
+// 12.25 KiB, whatever the input size), in a device array of the library's own.
+// Host code never passes `scratch` itself to a kernel (on the host it names a
+// host-side stand-in): it passes the device address that hipGetSymbolAddress
+// returns for it, looked up once per device with that device current.
+static __device__ __align__(256) uint32_t scratch[kQuantizeWsBytes / 4];
 static void *g_scratch_ptr[kMaxDevices];
 static nvfp4_status g_scratch_status[kMaxDevices];
 static std::once_flag g_scratch_once[kMaxDevices];
@@ -336,16 +341,25 @@ __global__ __launch_bounds__(kThreads) void quantize_two_pass_tiled_kernel(
 // tau ^ 1 hold the two halves of one 16-element block.
 //
 // Each workgroup stores the maximum of |x| bit patterns over its run in its
-// slot of the workspace and waits until all gridDim.x slots are filled.
-// slots_reset_kernel, launched just before on the same stream, sets the slots
-// to kEmpty (a BF16 magnitude is at most 0x7FFF, so no maximum equals it), so
-// a workspace needs no initialisation and a captured graph replays as it ran.
-// A slot carries its own "filled" mark, so its reader needs no ordering with
-// any other location; slot stores and loads are agent-scope atomics (coherent
-// across the XCDs). The host launches this form only when the whole grid fits
-// on the device at once (the occupancy query), so every workgroup reaches its
-// store; the wait is bounded all the same (kSpinLimit polls, about a second),
-// and a workgroup whose wait runs out encodes its run with g = NaN.
+// slot of the workspace and waits until all gridDim.x slots are filled in this
+// call. The workspace keeps a generation number: every workgroup reads it on
+// entry and tags its slot with tag(gen) = gen ^ kTagMix in the high word of one
+// 64-bit atomic store (the maximum in the low word), then waits until every
+// slot carries that tag, then adds 1 to the generation. A workgroup passes the
+// wait only after every workgroup has stored its slot, and each store uses the
+// generation its workgroup read, so every read comes before every increment;
+// the next call therefore reads gen + gridDim.x and its tag differs from this
+// call's. Nothing needs resetting between calls and a workspace needs no
+// initialisation: a slot of memory filled with any constant c cannot carry the
+// tag of generation c, since c ^ kTagMix != c, and neither can the small
+// maxima the two-read form leaves in the same bytes (their high words are 0).
+// (A slot left untouched while the generation goes all the way round 2^32
+// would match again; random bytes match with probability 2^-32 a slot.) Slot
+// and generation accesses are agent-scope atomics (coherent across the XCDs).
+// The host launches this form only when the whole grid fits on the device at
+// once (the occupancy query), so every workgroup reaches its store; the wait
+// is bounded all the same (kSpinLimit polls, about a second), and a workgroup
+// whose wait runs out encodes its run with g = NaN.
 //
 // With g known, the workgroup tabulates g / scale for the 127 scale bytes
 // (and, for the two-pass form, fl32(code * scale / g) for each scale byte and
@@ -354,13 +368,9 @@ static constexpr int kFusedThreads = 1024;
 static constexpr int kFusedWaves = kFusedThreads / 64;
 static constexpr int kFusedChunks = 20;
 static constexpr int kFusedRun = kFusedChunks * kFusedThreads / 256;   // 80 tiles per workgroup at most
-static constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+static constexpr uint32_t kTagMix = 0x5EED5EEDu;
+static constexpr uint32_t kNoMax = 0xFFFFFFFFu;     // the wait ran out (no BF16 magnitude reaches it)
 static constexpr int kSpinLimit = 1 << 20;
-
-__global__ __launch_bounds__(256) void slots_reset_kernel(uint32_t *slots, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x)
-    __hip_atomic_store(slots + i, kEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -445,10 +455,14 @@ __device__ __forceinline__ float bf16_div6(float a) {
 // registers), so 32-bit indices suffice.
 template <int MODE>
 __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
-    const u32x4_t *__restrict__ x, int rows, int K, int ntiles, int run, float inv_kt, uint32_t *slots,
+    const u32x4_t *__restrict__ x, int rows, int K, int ntiles, int run, float inv_kt, uint8_t *state,
     uint8_t *__restrict__ out, uint8_t *__restrict__ scales_rm, float *__restrict__ g_out,
     float *__restrict__ inv_g_out) {
   __shared__ uint32_t red[kFusedWaves + 1];
+  uint32_t *const gen = reinterpret_cast<uint32_t *>(state);
+  uint64_t *const slots = reinterpret_cast<uint64_t *>(state + 16);
+  // this call's tag, read before this workgroup's slot is stored
+  const uint32_t tag = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ^ kTagMix;
   __shared__ float rtab[128];                                     // g / scale, per scale byte
   __shared__ float qtab[MODE == 2 ? 128 * 16 : 1];                // fl32(code * scale / g)
   const int tau = threadIdx.x, wave = tau >> 6, lane = tau & 63, q = tau & 7;
@@ -474,22 +488,26 @@ __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
   __syncthreads();
   if (wave == 0) {
     const uint32_t bm = wave_max_u32(lane < kFusedWaves ? red[lane] : 0u);
-    if (lane == 0) __hip_atomic_store(slots + blockIdx.x, bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t tm = kEmpty;
+    if (lane == 0)
+      __hip_atomic_store(slots + blockIdx.x, ((uint64_t)tag << 32) | bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t tm = kNoMax;
     for (int it = 0; it < kSpinLimit; it++) {
-      // every slot this lane polls, loaded at once (at most 1024 slots: 16 a lane)
-      uint32_t u[16];
-#pragma unroll
-      for (int k = 0; k < 16; k++)
-        u[k] = (lane + 64 * k < (int)gridDim.x)
-                   ? __hip_atomic_load(slots + lane + 64 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   : 0u;
+      // the slots this lane polls (at most 1024 slots: 16 a lane), four loads at
+      // a time (registers: x holds most of them)
       uint32_t mm = 0;
       int full = 1;
+      for (int k0 = 0; k0 < 16 && 64 * k0 < (int)gridDim.x; k0 += 4) {
+        uint64_t u[4];
 #pragma unroll
-      for (int k = 0; k < 16; k++) {
-        full &= (u[k] != kEmpty);
-        mm = max(mm, u[k]);
+        for (int k = 0; k < 4; k++)
+          u[k] = (lane + 64 * (k0 + k) < (int)gridDim.x)
+                     ? __hip_atomic_load(slots + lane + 64 * (k0 + k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : ((uint64_t)tag << 32);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          full &= ((uint32_t)(u[k] >> 32) == tag);
+          mm = max(mm, (uint32_t)u[k]);
+        }
       }
       if (__all(full)) {
         tm = wave_max_u32(mm);
@@ -497,12 +515,17 @@ __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    if (lane == 0) red[kFusedWaves] = tm;
+    if (lane == 0) {
+      red[kFusedWaves] = tm;
+      // every workgroup has read this call's generation (its slot store used
+      // it): advance it by one per workgroup, gridDim.x in all
+      __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __syncthreads();
   const uint32_t tmb = red[kFusedWaves];
   float g;
-  if (tmb == kEmpty) {
+  if (tmb == kNoMax) {
     g = __builtin_nanf("");
   } else {
     const float amax_t = __uint_as_float(tmb << 16);
@@ -636,7 +659,7 @@ nvfp4_status quantize_common(const uint16_t *x, int64_t rows, int64_t K, int mod
   if (!ws) return NVFP4_ERR_WORKSPACE;
   if (ws_bytes < quantize_workspace_bytes(rows, K)) return NVFP4_ERR_WORKSPACE;
   const bool tiled = mode != 0;
-  if (!aligned(x, 16) || !aligned(codes, tiled ? 16 : 8) || !aligned(ws, 4) || !aligned(g_dev, 4) ||
+  if (!aligned(x, 16) || !aligned(codes, tiled ? 16 : 8) || !aligned(ws, 16) || !aligned(g_dev, 4) ||
       (inv_g_dev && !aligned(inv_g_dev, 4)))
     return NVFP4_ERR_ALIGN;
   DeviceInfo d;
@@ -651,11 +674,9 @@ nvfp4_status quantize_common(const uint16_t *x, int64_t rows, int64_t K, int mod
     fused_shape(ntiles, d.num_cus, &run, &grid);
     if (grid > 0) {
       const float inv_kt = 1.0f / (float)(K / 64);
-      hipLaunchKernelGGL(slots_reset_kernel, dim3(1), dim3(256), 0, s, (uint32_t *)ws, (int)grid);
-      NVFP4_LAUNCH_CHECK();
 #define NVFP4_FUSED(M)                                                                                              \
   hipLaunchKernelGGL(quantize_fused_kernel<M>, dim3((unsigned)grid), dim3(kFusedThreads), 0, s, (const u32x4_t *)x, \
-                     (int)rows, (int)K, (int)ntiles, run, inv_kt, (uint32_t *)ws, (uint8_t *)codes, scales,  \
+                     (int)rows, (int)K, (int)ntiles, run, inv_kt, (uint8_t *)ws + kFusedStateOff, (uint8_t *)codes, scales,  \
                      g_dev, inv_g_dev)
       if (mode == 0)
         NVFP4_FUSED(0);

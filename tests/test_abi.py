@@ -44,6 +44,7 @@ def test_prepared_size():
 
 
 FAKE = ctypes.c_void_p(0x10000)       # a non-null, 64 KiB-aligned value; never dereferenced
+QWS = 12544        # bytes of the quantizer workspace (nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, ...))
 ODD = ctypes.c_void_p(0x10001)
 
 
@@ -106,21 +107,21 @@ def test_tile_activation_and_tiled_gemm_argument_checks():
 
 def test_quantize_tiled_argument_checks():
     q = nv.lib().nvfp4_quantize_tiled
-    assert q(FAKE, 64, 128, FAKE, None, None, FAKE, 4096, None) == nv.ERR_NULL      # g_dev
-    assert q(FAKE, 64, 96, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_SHAPE      # K % 64
-    assert q(FAKE, -1, 128, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_SHAPE
-    assert q(None, 64, 128, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_NULL
+    assert q(FAKE, 64, 128, FAKE, None, None, FAKE, QWS, None) == nv.ERR_NULL      # g_dev
+    assert q(FAKE, 64, 96, FAKE, FAKE, None, FAKE, QWS, None) == nv.ERR_SHAPE      # K % 64
+    assert q(FAKE, -1, 128, FAKE, FAKE, None, FAKE, QWS, None) == nv.ERR_SHAPE
+    assert q(None, 64, 128, FAKE, FAKE, None, FAKE, QWS, None) == nv.ERR_NULL
     assert q(FAKE, 64, 128, FAKE, FAKE, None, None, 0, None) == nv.ERR_WORKSPACE
-    assert q(FAKE, 64, 128, ODD, FAKE, None, FAKE, 4096, None) == nv.ERR_ALIGN
+    assert q(FAKE, 64, 128, ODD, FAKE, None, FAKE, QWS, None) == nv.ERR_ALIGN
 
 
 def test_two_pass_argument_checks():
     L = nv.lib()
     q = L.nvfp4_quantize_two_pass_tiled
-    assert q(FAKE, 64, 128, FAKE, None, None, FAKE, 4096, None) == nv.ERR_NULL      # g_dev
-    assert q(FAKE, 64, 96, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_SHAPE      # K % 64
+    assert q(FAKE, 64, 128, FAKE, None, None, FAKE, QWS, None) == nv.ERR_NULL      # g_dev
+    assert q(FAKE, 64, 96, FAKE, FAKE, None, FAKE, QWS, None) == nv.ERR_SHAPE      # K % 64
     assert q(FAKE, 64, 128, FAKE, FAKE, None, None, 0, None) == nv.ERR_WORKSPACE
-    assert q(FAKE, 64, 128, ODD, FAKE, None, FAKE, 4096, None) == nv.ERR_ALIGN
+    assert q(FAKE, 64, 128, ODD, FAKE, None, FAKE, QWS, None) == nv.ERR_ALIGN
     g = L.nvfp4_gemm_w4a4_two_pass_tiled
 
     def call(at=FAKE, w=FAKE, M=64, N=64, K=128, alpha=1.0, ac=None, d=FAKE, dt=nv.OUT_BF16, ldd=64):
@@ -159,11 +160,11 @@ def test_prepare_and_quantize_argument_checks():
     assert p(FAKE, FAKE, nv.SCALE_E4M3, 32, 96, FAKE, None, None) == nv.ERR_SHAPE
     assert p(ODD, FAKE, nv.SCALE_E4M3, 32, 64, FAKE, None, None) == nv.ERR_ALIGN
     q = L.nvfp4_quantize
-    assert q(FAKE, 4, 32, FAKE, FAKE, None, None, FAKE, 4096, None) == nv.ERR_NULL
-    assert q(FAKE, 4, 24, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_SHAPE
+    assert q(FAKE, 4, 32, FAKE, FAKE, None, None, FAKE, QWS, None) == nv.ERR_NULL
+    assert q(FAKE, 4, 24, FAKE, FAKE, FAKE, None, FAKE, QWS, None) == nv.ERR_SHAPE
     assert q(FAKE, 4, 32, FAKE, FAKE, FAKE, None, None, 0, None) == nv.ERR_WORKSPACE
     assert q(FAKE, 4, 32, FAKE, FAKE, FAKE, None, FAKE, 16, None) == nv.ERR_WORKSPACE
-    assert q(ODD, 4, 32, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == nv.ERR_ALIGN
+    assert q(ODD, 4, 32, FAKE, FAKE, FAKE, None, FAKE, QWS, None) == nv.ERR_ALIGN
 
 
 def test_workspace_sizes():
@@ -172,7 +173,7 @@ def test_workspace_sizes():
     assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 8192, 8192, 8192) == 8192 * 8192 * 9 // 16
     assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 33, 64, 128) == 64 * 128 * 9 // 16
     assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 0, 64, 128) == 0
-    assert L.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 0, 5120) >= 4
+    assert L.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 0, 5120) == QWS   # any size: 12.25 KiB
     # W4A16 (no device here: the plan assumes 256 CUs). Decode (M <= 4) and the row kernel
     # (M <= 64, M <= 48 on weights of >= 256 row groups) need none; the fragment kernel's x
     # copy is roundup32(M) rows x K BF16.

@@ -277,6 +277,35 @@ def test_quantize_repeat_calls_new_maximum():
         np.testing.assert_array_equal(host(at), lay)
 
 
+@pytest.mark.parametrize("fill", ["zeros", "ones", "a5", "after_two_read", "random"])
+def test_quantize_workspace_any_initial_state(fill):
+    """The one-read quantizer's barrier needs no workspace initialisation: whatever the workspace
+    holds (zeros as nvfp4_workspace_init leaves it, all-ones bytes, a constant byte, what the
+    two-read form leaves there, random bytes), several calls in a row give the oracle's bytes,
+    with the tensor maximum changing from call to call."""
+    n = nv.workspace_bytes(nv.OP_QUANTIZE, 256, 0, 5120)
+    if fill == "zeros":
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    elif fill == "ones":
+        ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    elif fill == "a5":
+        ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    elif fill == "random":
+        ws = torch.from_numpy(np.random.default_rng(3).integers(0, 256, n, dtype=np.uint8)).cuda()
+    else:
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        big = synth.normal_bf16(5, 8256, 5120)             # past the register capacity: two reads
+        nv.nvfp4_quantize_tiled(dev(big).view(torch.bfloat16), ws=ws)
+    for i, std in enumerate([1.0, 3.0, 0.25]):
+        x = synth.normal_bf16(400 + i, 256, 5120, std=std)
+        at, g, ig = nv.nvfp4_quantize_tiled(dev(x).view(torch.bfloat16), ws=ws)
+        torch.cuda.synchronize()
+        c_ref, s_ref, g_ref, _ = quantize.quantize(x)
+        assert np.float32(g.item()) == g_ref, f"{fill}: call {i}"
+        lay, _ = prepared.prepare_weight(c_ref, s_ref, "ue4m3")
+        np.testing.assert_array_equal(host(at), lay)
+
+
 # ------------------------------------------------------------------ W4A4
 
 def _w4a4(a, sa, b, sb, alpha, out_dtype, alpha_dev=None):
