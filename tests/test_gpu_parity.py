@@ -360,6 +360,27 @@ def test_w4a4_big_tiles_ragged_strided_out(out_dtype, pad):
     assert_close(host(out), D, S, bf16=out_dtype == "bf16", what=f"strided {out_dtype} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(4000, 4192, 256), (8192, 8192, 128), (300, 8704, 192)])
+def test_w4a4_bf16_aligned_padded_rows_ragged(M, N, K):
+    """BF16 out on 256 x 256 tiles into rows 8 elements longer than N (16-byte aligned rows, the
+    16-byte store path): every element inside D against the oracle, the padding columns
+    untouched. Ragged M and N (last tiles part-filled), several tiles per workgroup (8192 x 8192:
+    four rounds), and fewer tiles than CUs (300 x 8704)."""
+    a, sa = _random_nvfp4(M + 31, M, K)
+    b, sb = _random_nvfp4(N + 37, N, K)
+    wp, bad = _prep(b, sb)
+    assert bad == 0
+    big = torch.full((M, N + 8), -3.0, dtype=torch.bfloat16, device="cuda")
+    cfg = nv.make_config(nv.KERNEL_W4A4_TILES, 256, 256)
+    out = nv.nvfp4_gemm_w4a4(dev(a), dev(sa), wp, N, K, 0.59, None, "bf16", out=big[:, :N], config=cfg)
+    again = nv.nvfp4_gemm_w4a4(dev(a), dev(sa), wp, N, K, 0.59, None, "bf16", config=cfg)
+    torch.cuda.synchronize()
+    assert torch.all(big[:, N:] == -3.0), "columns past N were written"
+    assert torch.equal(out, again)
+    D, S = oracle_w4a4_exact_blocked(a, sa, b, sb, 0.59)
+    assert_close(host(out), D, S, bf16=True, what=f"bf16 padded rows {M}x{N}x{K}")
+
+
 def test_w4a4_last_round_quadrants_same_bits():
     """16 x 17 = 272 tiles of 256 x 256 on 256 CUs: the last 16 (at most half a round) run as
     128 x 128 quadrants on two workgroups per CU. Ragged both ways: the last tile row holds 160
