@@ -141,10 +141,13 @@ def sustained_clock(fn, seconds=3.0, settle=1.2):
 
 
 def time_steps(fn, steps, warmup, sampler=None, warm_s=0.0):
-    """Warm-up, then `steps` calls bracketed by synchronisations, with an event before and after
-    each call on the launch stream: (mean ms per call over the whole region, min ms per call).
-    The warm-up is `warmup` calls, continued until at least `warm_s` seconds have passed (short
-    calls need many more than `warmup` to bring the clock to where it settles under load)."""
+    """Warm-up, then `steps` calls bracketed by synchronisations and by one HIP event before and
+    one after, on the launch stream: the mean ms per call over that region. Then a second run of
+    up to `steps` calls with an event between consecutive calls, for the fastest single call (an
+    event between calls costs a few microseconds, which would inflate the mean of short calls).
+    Returns (mean ms, min ms). The warm-up is `warmup` calls, continued until at least `warm_s`
+    seconds have passed (short calls need many more than `warmup` to bring the clock to where it
+    settles under load)."""
     import torch
     t0 = time.time()
     n = 0
@@ -154,17 +157,25 @@ def time_steps(fn, steps, warmup, sampler=None, warm_s=0.0):
         if n % 64 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ctx = sampler if sampler is not None else _Null()
     with ctx:
-        ev[0].record()
-        for i in range(steps):
+        e0.record()
+        for _ in range(steps):
             fn()
-            ev[i + 1].record()
-        ev[-1].synchronize()
+        e1.record()
+        e1.synchronize()
     torch.cuda.synchronize()
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return ev[0].elapsed_time(ev[-1]) / steps, min(per)
+    mean = e0.elapsed_time(e1) / steps
+    k = min(steps, 50)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+    ev[0].record()
+    for i in range(k):
+        fn()
+        ev[i + 1].record()
+    ev[-1].synchronize()
+    torch.cuda.synchronize()
+    return mean, min(ev[i].elapsed_time(ev[i + 1]) for i in range(k))
 
 
 class _Null:
