@@ -143,11 +143,12 @@ def sustained_clock(fn, seconds=3.0, settle=1.2):
 def time_steps(fn, steps, warmup, sampler=None, warm_s=0.0):
     """Warm-up, then `steps` calls bracketed by synchronisations and by one HIP event before and
     one after, on the launch stream: the mean ms per call over that region. Then a second run of
-    up to `steps` calls with an event between consecutive calls, for the fastest single call (an
-    event between calls costs a few microseconds, which would inflate the mean of short calls).
-    Returns (mean ms, min ms). The warm-up is `warmup` calls, continued until at least `warm_s`
-    seconds have passed (short calls need many more than `warmup` to bring the clock to where it
-    settles under load)."""
+    up to 10 groups of g = max(1, min(10, steps // 10)) consecutive calls, with an event between
+    groups only, for the fastest group's ms per call (an event between every two calls costs a
+    few microseconds, which would inflate short calls). Returns (mean ms, fastest group's ms per
+    call). The warm-up is `warmup` calls, continued until at least `warm_s` seconds have passed
+    (short calls need many more than `warmup` to bring the clock to where it settles under
+    load)."""
     import torch
     t0 = time.time()
     n = 0
@@ -167,15 +168,17 @@ def time_steps(fn, steps, warmup, sampler=None, warm_s=0.0):
         e1.synchronize()
     torch.cuda.synchronize()
     mean = e0.elapsed_time(e1) / steps
-    k = min(steps, 50)
+    g = max(1, min(10, steps // 10))
+    k = min(10, max(1, steps // g))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
     ev[0].record()
     for i in range(k):
-        fn()
+        for _ in range(g):
+            fn()
         ev[i + 1].record()
     ev[-1].synchronize()
     torch.cuda.synchronize()
-    return mean, min(ev[i].elapsed_time(ev[i + 1]) for i in range(k))
+    return mean, min(ev[i].elapsed_time(ev[i + 1]) for i in range(k)) / g
 
 
 class _Null:

@@ -80,7 +80,13 @@ constexpr int kDecodeLdsBytes = 64 * 1024;  // x staged in LDS: M * K * 2 bytes 
 //  * else 128 x 256 when those fill the CUs or split that way, as 4 x 2 MFMA
 //    tiles per wave with the 4 waves side by side along N (each wave
 //    dequantizes W fragments for all four of its row tiles);
-//  * else 2 x 2 (128 x 128).
+//  * else 128 x 128, as 4 x 1 MFMA tiles per wave with the 4 waves side by
+//    side along N: each wave dequantizes one W fragment per step for four
+//    MFMAs. (With 2 x 2 waves of 2 x 2 tiles, each W fragment was dequantized
+//    by both waves of its column, nine vector instructions per MFMA against
+//    five; the same bits, back to back on one box: M = 128 on 5120 x 5120
+//    25.8 -> 24.4 us, 5120 x 17408 43.0 -> 39.0 us, M = 768 on 5120 x 5120
+//    52.9 -> 46.2 us.)
 // WGM is the number of waves along M (2 x 2 waves, or 1 x 4).
 constexpr int64_t kBigSplitMinChunks = 32;
 static void big_tile_shape(int64_t M, int64_t N, int64_t K, int cus, int &TM, int &TN, int &WGM) {
@@ -98,7 +104,9 @@ static void big_tile_shape(int64_t M, int64_t N, int64_t K, int cus, int &TM, in
     WGM = 1;
     return;
   }
-  TM = TN = WGM = 2;
+  TM = 4;
+  TN = 1;
+  WGM = 1;
 }
 
 // One 32-row group per workgroup. Eight waves once there are two groups per
@@ -117,7 +125,9 @@ static void tiles_of(const nvfp4_config &c, int &TM, int &TN, int &WGM) {
     TN = 2;
     WGM = 1;
   } else {
-    TM = TN = WGM = 2;
+    TM = 4;
+    TN = 1;
+    WGM = 1;
   }
 }
 
@@ -810,8 +820,8 @@ __global__ __launch_bounds__(W * 64) void skinny_rows_kernel(const uint16_t *__r
 // over 32 TM WGM x 32 TN (4 / WGM) output tiles, each wave owning TM x TN
 // v_mfma_f32_32x32x16_bf16 tiles: 256 x 256 (TM = TN = 4, 2 x 2 waves) and
 // 128 x 256 (TM = 4, TN = 2, 1 x 4 waves), one workgroup per CU, read x in
-// fragment order straight into registers (tile_mainloop_d); 128 x 128 (2 x 2
-// tiles, 2 x 2 waves, up to two workgroups per CU) stages x through LDS
+// fragment order straight into registers (tile_mainloop_d); 128 x 128 (4 x 1
+// tiles, 1 x 4 waves, up to two workgroups per CU) stages x through LDS
 // (tile_mainloop), and so do 128 x 256 tiles that are all split into short K
 // ranges (big_xpath).
 //  * W: each wave loads its TN column groups' fragments of a 64-wide K chunk
@@ -1566,10 +1576,10 @@ extern "C" nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const u
   }
     if (b.TN == 4) {
       NVFP4_BIG(4, 4, 2)
-    } else if (b.TM == 4) {
+    } else if (b.TN == 2) {
       NVFP4_BIG(4, 2, 1)
     } else {
-      NVFP4_BIG(2, 2, 2)
+      NVFP4_BIG(4, 1, 1)
     }
 #undef NVFP4_BIG
   } else if (plan.kind == 3) {
