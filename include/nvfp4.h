@@ -272,7 +272,14 @@ nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_p
  *  codes   [rows][K/2] bytes out, 8-byte aligned.  scales [rows][K/16] UE4M3 bytes out.
  *  g_dev   device float out: g.  inv_g_dev  device float out (may be NULL): 1/g in FP32.
  *  ws      nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, 0, K) bytes (no init needed).
- * Inputs must be finite. rows == 0 writes g = 1. */
+ * Inputs must be finite. rows == 0 writes g = 1.
+ * When K % 64 == 0 and x fits in the vector registers of one grid that is
+ * resident all at once (up to 80 tiles of 32 x 64 per workgroup, one
+ * workgroup per CU: 80 MiB of BF16 on 256 CUs), x is read once: the
+ * workgroups exchange their maxima through the workspace and wait for each
+ * other there once. The wait is bounded (about a second); kernels on other
+ * streams that hold CUs longer than that make the late workgroups' outputs
+ * NaN. Larger inputs, and other K, read x twice with no wait. */
 nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales,
                             float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes, void *stream);
 
