@@ -277,9 +277,11 @@ nvfp4_status nvfp4_gemm_w4a16(const uint16_t *x, int64_t ldx, const uint8_t *w_p
  * resident all at once (up to 80 tiles of 32 x 64 per workgroup, one
  * workgroup per CU: 80 MiB of BF16 on 256 CUs), x is read once: the
  * workgroups exchange their maxima through the workspace and wait for each
- * other there once. The wait is bounded (about a second); kernels on other
- * streams that hold CUs longer than that make the late workgroups' outputs
- * NaN. Larger inputs, and other K, read x twice with no wait. */
+ * other there once. The wait is bounded (about a second): if kernels on other
+ * streams keep some of its workgroups off the CUs for longer than that, the
+ * workgroups whose wait ran out encode their rows with g = NaN, which leaves
+ * those rows' scales and codes meaningless (and g_dev NaN when workgroup 0 is
+ * among them). Larger inputs, and other K, read x twice with no wait. */
 nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales,
                             float *g_dev, float *inv_g_dev, void *ws, size_t ws_bytes, void *stream);
 
