@@ -168,6 +168,10 @@ def test_prepare_and_quantize_argument_checks():
 
 
 def test_workspace_sizes():
+    def heur_ws(op, M, N, K):   # the heuristic's config, whatever the tuned table holds
+        c = nv.get_config(op, M, N, K, -256)
+        return nv.lib().nvfp4_config_workspace_bytes(op, M, N, K, ctypes.byref(c))
+
     L = nv.lib()
     # W4A4: A in the prepared tile layout, rows rounded up to 32
     assert L.nvfp4_workspace_bytes(nv.OP_W4A4, 8192, 8192, 8192) == 8192 * 8192 * 9 // 16
@@ -182,7 +186,10 @@ def test_workspace_sizes():
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 16, 34816, 5120) == 0
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 24, 17408, 4160) == 0
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 48, 34816, 5120) == 0
-    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 64, 5120, 17408) == 0       # 160 row groups
+    assert heur_ws(nv.OP_W4A16, 64, 5120, 17408) == 0       # 160 row groups
+    # the tuned table's 128 x 128 tiles there: 40 tiles split 6 ways, two 64 KiB slots per
+    # workgroup, x through LDS
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 64, 5120, 17408) == 240 * 2 * 64 * 1024
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 49, 34816, 5120) == 64 * 5120 * 2
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 64, 8192, 5120) == 64 * 5120 * 2   # 256 row groups
     # K past the row kernel's 32-bit weight offsets: the fragment kernel and its copy
@@ -193,11 +200,16 @@ def test_workspace_sizes():
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 128, 34816, 5120) == 256 * 2 * 128 * 1024
     # M = 1024 on 5120 x 17408: 80 tiles of 256 x 256, all split over 256 workgroups (two
     # 256 KiB slots each), then x for four 256-row tiles in fragment order
-    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1024, 5120, 17408) == (256 * 2 * 256 * 1024
+    assert heur_ws(nv.OP_W4A16, 1024, 5120, 17408) == 256 * 2 * 256 * 1024 + 1024 * 17408 * 2
+    # the tuned table's 128 x 256 tiles there: 160 tiles all split over 256 workgroups (two
+    # 128 KiB slots each) in 170-chunk ranges, x read from its fragment-order copy
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1024, 5120, 17408) == (256 * 2 * 128 * 1024
                                                                        + 1024 * 17408 * 2)
     # M = 1024 on 5120 x 5120 (128 x 256 tiles, 160 of them, all split into 50-chunk ranges):
     # x through LDS, the partials only
-    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1024, 5120, 5120) == 256 * 2 * 128 * 1024
+    assert heur_ws(nv.OP_W4A16, 1024, 5120, 5120) == 256 * 2 * 128 * 1024
+    # the tuned table's 128 x 128 tiles there: 320 whole tiles, no split, x through LDS
+    assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1024, 5120, 5120) == 0
     # M = 1024: 544 tiles of 256 x 256, 512 in two whole rounds and 32 split (two 256 KiB
     # slots per workgroup), then x for four 256-row tiles
     assert L.nvfp4_workspace_bytes(nv.OP_W4A16, 1024, 34816, 5120) == 256 * 2 * 256 * 1024 + 1024 * 5120 * 2
