@@ -465,6 +465,7 @@ __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
   const uint32_t tag = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ^ kTagMix;
   __shared__ float rtab[128];                                     // g / scale, per scale byte
   __shared__ float qtab[MODE == 2 ? 128 * 16 : 1];                // fl32(code * scale / g)
+  __shared__ float dtab[kFusedChunks * kFusedThreads];            // amax_b / 6 of each thread's chunks
   const int tau = threadIdx.x, wave = tau >> 6, lane = tau & 63, q = tau & 7;
   const int kt = K / 64, x_row = K / 8;
   const int tile0 = (int)blockIdx.x * run;
@@ -480,9 +481,18 @@ __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
     v[i] = u32x4_t{0u, 0u, 0u, 0u};
     if (t_base + 4 * i < myrun && row < rows) v[i] = __builtin_nontemporal_load(x + (row * x_row + kk * 8 + q));
   }
+  // The tensor maximum, and each chunk's block maximum over the block's two
+  // halves (threads tau and tau ^ 1) divided by 6, kept in LDS for the encode:
+  // this work overlaps the loads still in flight, where after the wait it would
+  // hold up the encode (the registers have no room for it: x fills them).
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < kFusedChunks; i++) m = max(m, absmax8(v[i]));
+  for (int i = 0; i < kFusedChunks; i++) {
+    const uint32_t mh = absmax8(v[i]);
+    m = max(m, mh);
+    const uint32_t mb = max(mh, pair_swap(mh));
+    dtab[i * kFusedThreads + tau] = bf16_div6(__uint_as_float(mb << 16));
+  }
   m = wave_max_u32(m);
   if (lane == 0) red[wave] = m;
   __syncthreads();
@@ -544,9 +554,9 @@ __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
   }
   __syncthreads();
 
-  // the indices and block maxima are recomputed below from copies of tau and x
-  // the compiler cannot see through, so it does not keep phase 1's 20 sets of
-  // them live across the wait (they would not fit beside x in the registers)
+  // the indices are recomputed below from copies of tau and x the compiler
+  // cannot see through, so it does not keep phase 1's 20 sets of them live
+  // across the wait (they would not fit beside x in the registers)
   int tau2 = tau;
   asm volatile("" : "+v"(tau2));
 #pragma unroll
@@ -560,10 +570,8 @@ __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
     const int t = t2_base + 4 * i;
     const bool have = t < myrun;                                  // the same for the whole wave
     const int tile = tile0 + t;
-    // the block's maximum from its two halves (both threads run the exchange)
-    const uint32_t mh = absmax8(v[i]);
-    const uint32_t mb = max(mh, pair_swap(mh));
-    const uint32_t sb = e4m3_rne_sat_sel(bf16_div6(__uint_as_float(mb << 16)) * g);   // 0 for a zero block
+    // the block's maximum / 6, from phase 1 (this thread's own entry)
+    const uint32_t sb = e4m3_rne_sat_sel(dtab[i * kFusedThreads + tau2] * g);   // 0 for a zero block
     uint32_t w = codes8(v[i], rtab[sb]);
     w = sb ? w : 0u;
     if (MODE == 0) {
