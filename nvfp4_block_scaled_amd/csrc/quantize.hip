@@ -340,9 +340,11 @@ __global__ __launch_bounds__(kThreads) void quantize_two_pass_tiled_kernel(
 // writes two whole 128-byte lines of its tile's codes, and threads tau and
 // tau ^ 1 hold the two halves of one 16-element block.
 //
-// Each workgroup stores the maximum of |x| bit patterns over its run in its
-// slot of the workspace and waits until all gridDim.x slots are filled in this
-// call. The workspace keeps a generation number: every workgroup reads it on
+// While the loads arrive, each thread also forms every chunk's 16-element block
+// maximum (its half and its partner's) divided by 6, and keeps it in LDS for
+// the encode. Each workgroup stores the maximum of |x| bit patterns over its
+// run in its slot of the workspace and waits until all gridDim.x slots are
+// filled in this call. The workspace keeps a generation number: every workgroup reads it on
 // entry and tags its slot with tag(gen) = gen ^ kTagMix in the high word of one
 // 64-bit atomic store (the maximum in the low word), then waits until every
 // slot carries that tag, then adds 1 to the generation. A workgroup passes the
