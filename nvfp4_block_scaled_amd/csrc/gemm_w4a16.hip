@@ -1267,7 +1267,7 @@ __device__ __forceinline__ void tile_epilogue(const Params &p, uint8_t *smem, fl
         const u32x4_t v = *reinterpret_cast<const u32x4_t *>(reg + row * ROW_BYTES + pc * 16);
         uint16_t *dst = p.y + m * p.ldy + col0 + cc;
         if (vec_ok) {
-          *reinterpret_cast<u32x4_t *>(dst) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));   // written once: stream it
         } else {
           const uint16_t *src = reinterpret_cast<const uint16_t *>(&v);
           for (int e2 = 0; e2 < 8; e2++) dst[e2] = src[e2];

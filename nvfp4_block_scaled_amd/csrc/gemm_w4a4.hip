@@ -333,7 +333,7 @@ __device__ __forceinline__ void epilogue(uint8_t *smem, const Params &p, int64_t
         const u32x4_t v = *reinterpret_cast<const u32x4_t *>(reg + row * ROW_BYTES + pc * 16);
         uint8_t *dst = reinterpret_cast<uint8_t *>(p.d) + (m * p.ldd + col0 + c) * ESZ;
         if (vec_ok) {
-          *reinterpret_cast<u32x4_t *>(dst) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));   // written once: stream it
         } else {
           // unaligned output rows: element stores
           const uint8_t *src = reinterpret_cast<const uint8_t *>(&v);

@@ -591,8 +591,8 @@ __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
       }
       const uint32_t s4 = cell_scales(sb);
       if (have) {
-        *reinterpret_cast<uint32_t *>(out + (t1 * 1024 + code_off)) = w;
-        if (q == 0) *reinterpret_cast<uint32_t *>(scale_base + (t1 * 128 + 4 * r)) = s4;
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t *>(out + (t1 * 1024 + code_off)));
+        if (q == 0) __builtin_nontemporal_store(s4, reinterpret_cast<uint32_t *>(scale_base + (t1 * 128 + 4 * r)));
       }
       if (MODE == 2) {
         // residual of the eight elements: x - fl32(code * scale / g)
@@ -618,12 +618,18 @@ __global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(
         const uint32_t s4b = cell_scales(sb2);
         if (have) {
           const int t2 = t1 + kt;
-          *reinterpret_cast<uint32_t *>(out + (t2 * 1024 + code_off)) = w2;
-          if (q == 0) *reinterpret_cast<uint32_t *>(scale_base + (t2 * 128 + 4 * r)) = s4b;
+          __builtin_nontemporal_store(w2, reinterpret_cast<uint32_t *>(out + (t2 * 1024 + code_off)));
+          if (q == 0) __builtin_nontemporal_store(s4b, reinterpret_cast<uint32_t *>(scale_base + (t2 * 128 + 4 * r)));
         }
       }
     }
-    // one chunk at a time: interleaving chunks would need registers x holds
+    // one chunk at a time: interleaving chunks would need registers x holds.
+    // The tile-layout stores are non-temporal: each wave store fills whole
+    // 128-byte lines that are written once, and streaming them past the cache
+    // took [8192][5120] from 27.7 to 24.3 us (tiled) and from 43.4 to 38.5 us
+    // (two-pass). The row-major form's 4-byte code and 1-byte scale stores
+    // leave lines partly written, and as non-temporal stores they took it from
+    // 30.3 to 58.7 us, so they stay ordinary stores.
     __builtin_amdgcn_sched_barrier(0);
   }
 }
